@@ -1,0 +1,170 @@
+"""CPU oracle for C = ReLU(A @ B) (fp16 in, fp16 out) -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, the package smoke check in ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. The product path
+(the HIP library and its Python binding) never imports it and shares no code
+with it.
+
+The arithmetic lives in ``gemm_relu_oracle.c`` (plain C, built with gcc); this
+module builds it on demand and marshals numpy arrays of fp16 bit patterns
+(``uint16``) through ctypes. What each function computes, and the passage of
+the TileLang pages it follows, is stated in the C source.
+
+Parity is pinned by ``tests/test_oracle.py``: exhaustive fp16 decode/encode
+checks, exact rational brute force on tiny shapes, identity / zero / K=1 closed
+forms, integer-exact sums and the C >= 0 invariant.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gemm_relu_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_gemm_relu.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math). Returns the .so path."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + f".tmp{os.getpid()}"
+    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        build()
+        lib = ctypes.CDLL(_LIB)
+        i64, p = ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_to_f64.restype = ctypes.c_double
+        lib.oracle_f64_to_f16_rne.argtypes = [ctypes.c_double]
+        lib.oracle_f64_to_f16_rne.restype = ctypes.c_uint16
+        lib.oracle_decode_f16.argtypes = [p, p, i64]
+        lib.oracle_decode_f16.restype = None
+        lib.oracle_encode_f16.argtypes = [p, p, i64]
+        lib.oracle_encode_f16.restype = None
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_gemm_relu_f16.argtypes = [i64, i64, i64, p, p, p, p, p]
+        lib.oracle_gemm_relu_f16.restype = ctypes.c_int
+        lib.oracle_gemm_relu_f16_rows.argtypes = [i64, i64, i64, p, p, p, p, p, i64, i64]
+        lib.oracle_gemm_relu_f16_rows.restype = ctypes.c_int
+        lib.oracle_gemm_relu_f16_points.argtypes = [i64, i64, i64, p, p, i64, p, p, p, p, p]
+        lib.oracle_gemm_relu_f16_points.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(x: np.ndarray, shape) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint16:
+        raise TypeError("oracle inputs are fp16 bit patterns (numpy uint16)")
+    if x.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {x.shape}")
+    return x
+
+
+def f16_to_f64(bits) -> np.ndarray:
+    """Decode fp16 bit patterns (uint16 array) to float64."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_decode_f16(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def f64_to_f16(x) -> np.ndarray:
+    """Encode float64 values to fp16 bit patterns, round to nearest even."""
+    v = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().oracle_encode_f16(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def gemm_relu_f16(A: np.ndarray, B: np.ndarray, *, want_pre: bool = False,
+                  want_absdot: bool = False, rows: tuple[int, int] | None = None):
+    """C = ReLU(A @ B) as fp16 bit patterns.
+
+    A: uint16 [M, K], B: uint16 [K, N]. With ``rows=(r0, r1)`` only those rows
+    are computed and returned (shape [r1-r0, N]). Optionally also returns the
+    float64 pre-activation sums and sum_k |a||b| for the same rows.
+    """
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    A = _u16(A, (M, K))
+    B = _u16(B, (K, N))
+    r0, r1 = (0, M) if rows is None else rows
+    # the C routine indexes C, pre and absdot as full [M, N] arrays; only the
+    # requested rows are touched, so offset the base pointers accordingly
+    nr = r1 - r0
+    C = np.zeros((nr, N), dtype=np.uint16)
+    pre = np.zeros((nr, N), dtype=np.float64) if want_pre else None
+    sab = np.zeros((nr, N), dtype=np.float64) if want_absdot else None
+
+    def base(arr, itemsize):
+        if arr is None:
+            return None
+        return ctypes.c_void_p(arr.ctypes.data - r0 * N * itemsize)
+
+    rc = _load().oracle_gemm_relu_f16_rows(M, N, K, _ptr(A), _ptr(B), base(C, 2),
+                                           base(pre, 8), base(sab, 8), r0, r1)
+    if rc != 0:
+        raise RuntimeError("oracle_gemm_relu_f16_rows failed")
+    out = [C]
+    if want_pre:
+        out.append(pre)
+    if want_absdot:
+        out.append(sab)
+    return out[0] if len(out) == 1 else tuple(out)
+
+
+def gemm_relu_f16_points(A: np.ndarray, B: np.ndarray, ii, jj, *, want_pre: bool = False,
+                         want_absdot: bool = False):
+    """Elements C[ii[t], jj[t]] of ReLU(A @ B) as fp16 bit patterns."""
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    A = _u16(A, (M, K))
+    B = _u16(B, (K, N))
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    if ii.shape != jj.shape or ii.ndim != 1:
+        raise ValueError("ii and jj must be 1-D of equal length")
+    out = np.zeros(ii.shape, dtype=np.uint16)
+    pre = np.zeros(ii.shape, dtype=np.float64) if want_pre else None
+    sab = np.zeros(ii.shape, dtype=np.float64) if want_absdot else None
+    rc = _load().oracle_gemm_relu_f16_points(M, N, K, _ptr(A), _ptr(B), ii.size, _ptr(ii),
+                                             _ptr(jj), _ptr(out), _ptr(pre), _ptr(sab))
+    if rc != 0:
+        raise RuntimeError("oracle_gemm_relu_f16_points failed")
+    res = [out]
+    if want_pre:
+        res.append(pre)
+    if want_absdot:
+        res.append(sab)
+    return res[0] if len(res) == 1 else tuple(res)

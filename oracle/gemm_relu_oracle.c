@@ -1,0 +1,205 @@
+/*
+ * CPU oracle for C = ReLU(A @ B), fp16 A[M,K], B[K,N], fp16 C[M,N].
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the package's smoke check and the
+ * benchmark's CPU-baseline leg load this library. The product path never
+ * calls it and shares no code with it.
+ *
+ * What it computes follows the TileLang GEMM example ("Writing
+ * high-performance kernels in TileLang", section "Escribamos un GEMM"): the
+ * kernel there takes fp16 A (M x K) and B (K x N), accumulates the tile
+ * products in a wider accumulator, applies max(x, 0) to the accumulator and
+ * only then writes the result into an fp16 C (M x N); the example checks the
+ * result against relu(a @ b). That result has a plain definition, so the
+ * oracle is that definition written out:
+ *
+ *   1. decode every fp16 bit pattern to a double (IEEE binary16 definition);
+ *   2. pre[i][j] = sum over k = 0, 1, ..., K-1 (in that order) of
+ *      a[i][k] * b[k][j] in double precision -- each product of two fp16
+ *      values is exact in double (11 + 11 significant bits);
+ *   3. y = pre > 0 ? pre : +0 (the ReLU);
+ *   4. encode y to fp16 with round to nearest, ties to even.
+ *
+ * Readings where the pages are silent: the final rounding is IEEE
+ * round-to-nearest-even (what an ordinary fp32 -> fp16 conversion does);
+ * overflow past the largest finite fp16 becomes +inf; fp16 subnormals are
+ * honoured on input and output; the sum over an empty K is 0.
+ *
+ * Each output element's summation order is fixed (k ascending), so results do
+ * not depend on how many threads run the row loop.
+ *
+ * Plain C11, no fp16 compiler types, built with gcc -O2 (no fast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- IEEE binary16 decode: sign, 5-bit exponent (bias 15), 10-bit fraction ---- */
+double oracle_f16_to_f64(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int e = (h >> 10) & 0x1f;
+    const int m = h & 0x3ff;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)m, -24);                 /* subnormal: m * 2^-24 */
+    } else if (e == 31) {
+        v = (m == 0) ? INFINITY : NAN;             /* inf / NaN */
+    } else {
+        v = ldexp((double)(1024 + m), e - 25);     /* (1 + m/1024) * 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+/* Round a non-negative double q to the nearest integer, ties to even. */
+static double round_half_even(double q)
+{
+    const double fl = floor(q);
+    const double r = q - fl;                       /* exact for q < 2^52 */
+    if (r > 0.5) return fl + 1.0;
+    if (r < 0.5) return fl;
+    return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+}
+
+/* ---- IEEE binary16 encode, round to nearest, ties to even ---- */
+uint16_t oracle_f64_to_f16_rne(double x)
+{
+    if (isnan(x)) return 0x7e00;
+    const uint16_t sign = signbit(x) ? 0x8000 : 0;
+    const double a = fabs(x);
+    /* 65504 is the largest finite value, its spacing is 32; half of it past
+       65504 is 65520, which ties to the even neighbour 65536 = overflow. */
+    if (a >= 65520.0) return sign | 0x7c00;
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: quantum 2^-24; n == 1024 is the smallest normal */
+        const double n = round_half_even(ldexp(a, 24));
+        return sign | (uint16_t)n;
+    }
+    int E;
+    (void)frexp(a, &E);                            /* a = f * 2^E, f in [0.5, 1) */
+    int ex = E - 1;                                /* a in [2^ex, 2^(ex+1)) */
+    double n = round_half_even(ldexp(a, 10 - ex)); /* in [1024, 2048] */
+    if (n == 2048.0) { n = 1024.0; ex += 1; }
+    if (ex + 15 >= 31) return sign | 0x7c00;
+    return sign | (uint16_t)(((ex + 15) << 10) | ((int)n - 1024));
+}
+
+void oracle_decode_f16(const uint16_t* h, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_to_f64(h[i]);
+}
+
+void oracle_encode_f16(const double* x, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_f16_rne(x[i]);
+}
+
+static uint16_t relu_to_f16(double pre)
+{
+    return oracle_f64_to_f16_rne(pre > 0.0 ? pre : 0.0);
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Rows [row0, row1) of C = ReLU(A @ B). C points at row 0 of the full C
+ * (leading dimension N). pre, if not NULL, receives the double pre-activation
+ * sums (same indexing as C); absdot, if not NULL, receives sum_k |a||b|.
+ * Returns 0, or -1 on a bad argument or allocation failure.
+ */
+int oracle_gemm_relu_f16_rows(int64_t M, int64_t N, int64_t K,
+                              const uint16_t* A, const uint16_t* B, uint16_t* C,
+                              double* pre, double* absdot,
+                              int64_t row0, int64_t row1)
+{
+    if (M < 0 || N < 0 || K < 0 || row0 < 0 || row1 > M || row0 > row1) return -1;
+    if (N == 0 || row0 == row1) return 0;
+    double* bd = NULL;
+    if (K > 0) {
+        bd = (double*)malloc((size_t)K * (size_t)N * sizeof(double));
+        if (!bd) return -1;
+        oracle_decode_f16(B, bd, K * N);
+    }
+    int err = 0;
+#pragma omp parallel
+    {
+        double* acc = (double*)malloc((size_t)N * sizeof(double));
+        double* sab = absdot ? (double*)malloc((size_t)N * sizeof(double)) : NULL;
+        if (!acc || (absdot && !sab)) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t i = row0; i < row1; ++i) {
+                for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
+                if (sab) for (int64_t j = 0; j < N; ++j) sab[j] = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    const double a = oracle_f16_to_f64(A[i * K + k]);
+                    const double* brow = bd + k * N;
+                    for (int64_t j = 0; j < N; ++j) acc[j] += a * brow[j];
+                    if (sab) {
+                        const double aa = fabs(a);
+                        for (int64_t j = 0; j < N; ++j) sab[j] += aa * fabs(brow[j]);
+                    }
+                }
+                for (int64_t j = 0; j < N; ++j) {
+                    C[i * N + j] = relu_to_f16(acc[j]);
+                    if (pre) pre[i * N + j] = acc[j];
+                    if (sab) absdot[i * N + j] = sab[j];
+                }
+            }
+        }
+        free(acc);
+        free(sab);
+    }
+    free(bd);
+    return err ? -1 : 0;
+}
+
+/* The whole of C = ReLU(A @ B). */
+int oracle_gemm_relu_f16(int64_t M, int64_t N, int64_t K,
+                         const uint16_t* A, const uint16_t* B, uint16_t* C,
+                         double* pre, double* absdot)
+{
+    return oracle_gemm_relu_f16_rows(M, N, K, A, B, C, pre, absdot, 0, M);
+}
+
+/*
+ * Selected elements (ii[t], jj[t]) of C = ReLU(A @ B), each summed in the same
+ * k-ascending order as the full routine, so it gives the same values there.
+ */
+int oracle_gemm_relu_f16_points(int64_t M, int64_t N, int64_t K,
+                                const uint16_t* A, const uint16_t* B,
+                                int64_t npts, const int64_t* ii, const int64_t* jj,
+                                uint16_t* out, double* pre, double* absdot)
+{
+    if (M < 0 || N < 0 || K < 0 || npts < 0) return -1;
+    for (int64_t t = 0; t < npts; ++t)
+        if (ii[t] < 0 || ii[t] >= M || jj[t] < 0 || jj[t] >= N) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < npts; ++t) {
+        const int64_t i = ii[t], j = jj[t];
+        double acc = 0.0, s = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = oracle_f16_to_f64(A[i * K + k]);
+            const double b = oracle_f16_to_f64(B[k * N + j]);
+            acc += a * b;
+            s += fabs(a) * fabs(b);
+        }
+        out[t] = relu_to_f16(acc);
+        if (pre) pre[t] = acc;
+        if (absdot) absdot[t] = s;
+    }
+    return 0;
+}
