@@ -1,0 +1,210 @@
+"""Throughput of C = ReLU(A @ B) (fp16 in, fp32 accumulate, fp16 out) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one call of gemm_relu_f16 on one batch of synthetic input that is
+already resident in HBM: the whole hot path (tile loads, MFMA main loop, ReLU,
+fp16 store) in one kernel. W untimed steps are followed by K timed ones,
+bracketed by stream synchronisation; the line printed on stdout is one JSON
+object. Extra per-workload lines (``--all``) go to stderr.
+
+The CPU baseline leg times the oracle (plain C, all host threads) on a bounded
+slice of the same workload -- leading rows of C -- and scales it to TFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "TFLOP/s and % of MI355X dense FP16 MFMA peak, fp16 GEMM+ReLU 4096³"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_relu.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "tiled_dense_gemm_f16_amd", "csrc", "gemm_relu.hip"),
+                  os.path.join(ROOT, "include", "gemm_relu.h")]
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str) -> float | None:
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    cur = source_hash()
+    entries, entry = [], {}
+    for line in open(TRAFFIC_FILE):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        k, _, v = line.partition(":")
+        k, v = k.strip(), v.strip()
+        if k == "workload" and entry:
+            entries.append(entry)
+            entry = {}
+        entry[k] = v
+    if entry:
+        entries.append(entry)
+    for e in entries:
+        if e.get("workload") == workload and e.get("source_sha256") == cur:
+            try:
+                return float(e["traffic_bytes_per_launch"])
+            except (KeyError, ValueError):
+                return None
+    return None
+
+
+def time_gpu(w, steps: int, warmup: int, tile=None):
+    import torch
+    import tiled_dense_gemm_f16_amd as gr
+
+    a, b = workloads.workload_inputs(w)
+    ad, bd = a.cuda(), b.cuda()
+    c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+    opts = gr.make_opts(tile)
+    args = (w.M, w.N, w.K, ad.data_ptr(), bd.data_ptr(), c.data_ptr(), stream.cuda_stream, opts)
+    for _ in range(warmup):
+        st = gr.gemm_relu_f16_ex(*args)
+        if st != gr.OK:
+            raise RuntimeError(gr.strerror(st))
+    torch.cuda.synchronize()
+    # the whole timed region between two events on the launch stream
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        gr.gemm_relu_f16_ex(*args)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    # per-launch event pairs (same stream) for the kernel's own duration
+    nper = min(steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nper)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        gr.gemm_relu_f16_ex(*args)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    tile_id = gr.select_tile(w.M, w.N, w.K, ad.data_ptr(), bd.data_ptr(), c.data_ptr()) if tile is None else tile
+    return {"total_ms": total_ms, "ms_per_step": total_ms / steps,
+            "launch_ms_mean": float(per.mean()), "launch_ms_median": float(np.median(per)),
+            "launch_ms_min": float(per.min()), "tile": gr.tile_name(tile_id) if tile_id >= 0 else "generic",
+            "c": c, "a": a, "b": b}
+
+
+def cpu_baseline(w, gpu_c, target_s: float = 12.0):
+    """The oracle as it stands, on leading rows of the same workload."""
+    import oracle
+    A, B = workloads.as_u16(gpu_c["a"]), workloads.as_u16(gpu_c["b"])
+    threads = oracle.num_threads()
+    r_cal = min(w.M, max(threads, 8))
+    t = time.perf_counter()
+    oracle.gemm_relu_f16(A, B, rows=(0, r_cal))
+    t_cal = time.perf_counter() - t
+    rows = int(min(w.M, max(r_cal, round(r_cal * target_s / max(t_cal, 1e-6)))))
+    t = time.perf_counter()
+    ora = oracle.gemm_relu_f16(A, B, rows=(0, rows))
+    secs = time.perf_counter() - t
+    flops = 2.0 * rows * w.N * w.K
+    g = workloads.as_u16(gpu_c["c"][:rows].cpu()).view(np.float16).astype(np.float64)
+    o = ora.view(np.float16).astype(np.float64)
+    err = np.abs(g - o)
+    viol = int((~(err <= 1e-2 + 1e-2 * np.abs(o))).sum())
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of C for {w.name} ({rows}x{w.N}x{w.K} multiply-adds, "
+                      f"{secs:.1f} s on {threads} threads)",
+            "seconds": secs, "parity_of_sample": {"max_abs_err": float(err.max()), "violations": viol}}
+
+
+def result_line(w, r, steps, warmup, cpu=None):
+    bound = "hbm" if 2 * w.M * w.N * w.K / w.min_bytes < 315 and w.M <= 64 else "mfma"
+    value = w.flops / (r["ms_per_step"] * 1e-3) / 1e12
+    launch_s = r["launch_ms_mean"] * 1e-3
+    if bound == "mfma":
+        achieved = w.flops / launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4)}
+    else:
+        achieved = w.min_bytes / launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = measured_traffic(w.name)
+    line = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16 (fp32 accumulate)", "data": "synthetic",
+            "pct_of_fp16_peak": round(100 * value / PEAK_FP16_TFLOPS, 2),
+            "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dist": w.dist,
+                       "scale": w.scale, "seed": w.seed, "tile": r["tile"], "parallelism": "single GPU"},
+            "roofline": roof,
+            "kernel_ms": {"mean": round(r["launch_ms_mean"], 5), "median": round(r["launch_ms_median"], 5),
+                          "min": round(r["launch_ms_min"], 5)},
+            "hbm_gbs_at_min_bytes": round(w.min_bytes / (r["ms_per_step"] * 1e-3) / 1e9, 1),
+            "source_sha256": source_hash()}
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    return line
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default=workloads.SQUARE_4096.name, choices=sorted(workloads.BY_NAME))
+    ap.add_argument("--tile", type=int, default=None, help="pin a tile id (default: library's choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--all", action="store_true", help="also time every workload (lines on stderr)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards along M or N without communication, but no multi-GPU run is made.",
+              file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    import tiled_dense_gemm_f16_amd as gr
+    gr.load()
+
+    w = workloads.BY_NAME[args.workload]
+    r = time_gpu(w, args.steps, args.warmup, args.tile)
+    print(f"[bench] {w.name}: {r['ms_per_step'] * 1e3:.2f} us/step, kernel mean "
+          f"{r['launch_ms_mean'] * 1e3:.2f} us, tile {r['tile']}", file=sys.stderr, flush=True)
+    if args.all:
+        for ow in workloads.ALL:
+            if ow is w:
+                continue
+            orr = time_gpu(ow, max(args.steps // 4, 50), max(args.warmup // 4, 10))
+            print(json.dumps(result_line(ow, orr, max(args.steps // 4, 50), max(args.warmup // 4, 10))),
+                  file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, r, args.cpu_seconds)
+    print(json.dumps(result_line(w, r, args.steps, args.warmup, cpu)), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,112 @@
+/*
+ * gemm_relu.h -- C ABI of the MI355X (gfx950) fp16 GEMM with a fused ReLU.
+ *
+ * Operation (the GEMM + ReLU example of "Writing high-performance kernels in
+ * TileLang", section "Escribamos un GEMM"): for fp16 matrices A (M x K) and
+ * B (K x N),
+ *
+ *     C[i][j] = fp16( max( sum_k A[i][k] * B[k][j], 0 ) )
+ *
+ * The products are accumulated in fp32 (the example's accumulator type), the
+ * ReLU is applied to the fp32 accumulator, and the result is rounded once to
+ * fp16, to nearest with ties to even (a sum past the fp16 range becomes +inf).
+ * The order of the fp32 additions is unspecified. An empty sum (K = 0) gives
+ * C = 0. Inputs are expected to be finite.
+ *
+ * Layout: A, B and C are dense row-major device buffers of IEEE binary16
+ * values with leading dimensions K, N and N. No torch or HIP types appear in
+ * this header; a stream is passed as an opaque pointer (a hipStream_t, or
+ * NULL for the null stream).
+ *
+ * Ownership: the caller owns A, B and C and keeps them alive until the work
+ * enqueued on `stream` has finished. The library neither frees nor retains
+ * them. C must not overlap A or B.
+ *
+ * Execution: the call validates its arguments on the host, enqueues one kernel
+ * on `stream` and returns without waiting. Faults during execution surface at
+ * the caller's next synchronisation of that stream. Calls on different streams
+ * may run concurrently.
+ *
+ * Errors: every entry point returns a gemm_relu_status. All argument checks
+ * happen before any HIP runtime call, so a rejected call has no side effects.
+ */
+#ifndef GEMM_RELU_H
+#define GEMM_RELU_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gemm_relu_status {
+    GEMM_RELU_OK = 0,
+    /* a dimension is negative, a pointer is NULL while its matrix is not
+       empty, or C overlaps A or B */
+    GEMM_RELU_EINVAL = 1,
+    /* a dimension exceeds INT32_MAX, a pointer is not 2-byte aligned, the
+       current device is not gfx950, or opts names an unknown tile */
+    GEMM_RELU_EUNSUPPORTED = 2,
+    /* the HIP runtime reported an error (no device, launch failure) */
+    GEMM_RELU_EHIP = 3,
+    /* a library-owned workspace could not be allocated */
+    GEMM_RELU_ENOMEM = 4
+} gemm_relu_status;
+
+/* Pass as gemm_relu_opts.tile to let the library choose. */
+#define GEMM_RELU_TILE_AUTO (-1)
+
+/* Block orders for gemm_relu_opts.block_order. */
+#define GEMM_RELU_ORDER_DEFAULT 0   /* XCD-aware grouped order */
+#define GEMM_RELU_ORDER_ROW_MAJOR 1 /* plain row-major tile order (ablation) */
+
+/*
+ * Optional launch choices. They change speed, never the set of admissible
+ * results. Zero-initialise and set only what you need; tile = -1 means auto.
+ */
+typedef struct gemm_relu_opts {
+    int32_t tile;        /* GEMM_RELU_TILE_AUTO or an id < gemm_relu_tile_count() */
+    int32_t block_order; /* GEMM_RELU_ORDER_* */
+    int32_t group_m;     /* tile-rows per group of the grouped order; 0 = default */
+    int32_t reserved[5]; /* must be zero */
+} gemm_relu_opts;
+
+/*
+ * C = ReLU(A @ B) in fp16, as described at the top of this header.
+ *   M, N, K : matrix sizes, each in [0, INT32_MAX]
+ *   A       : device pointer to M*K fp16 values (row-major, leading dim K)
+ *   B       : device pointer to K*N fp16 values (row-major, leading dim N)
+ *   C       : device pointer to M*N fp16 values (row-major, leading dim N),
+ *             fully overwritten
+ *   stream  : hipStream_t to enqueue on, or NULL
+ * M == 0 or N == 0 is a successful no-op (no launch).
+ */
+int gemm_relu_f16(int64_t M, int64_t N, int64_t K,
+                  const void* A, const void* B, void* C, void* stream);
+
+/* Same as gemm_relu_f16; opts (may be NULL) pins the tile and block order. */
+int gemm_relu_f16_ex(int64_t M, int64_t N, int64_t K,
+                     const void* A, const void* B, void* C, void* stream,
+                     const gemm_relu_opts* opts);
+
+/* A static, human-readable message for a status code. */
+const char* gemm_relu_strerror(int status);
+
+/* Number of compiled tile configurations, and the name of one ("" if out of range). */
+int gemm_relu_tile_count(void);
+const char* gemm_relu_tile_name(int tile);
+
+/*
+ * The tile the library would use for this problem without opts, or -1 for the
+ * generic element-wise path that serves shapes whose K or N is not a multiple
+ * of 8 or whose pointers are not 16-byte aligned (pass NULL pointers to ask
+ * about shapes alone). Host-only; makes no HIP call.
+ */
+int gemm_relu_select_tile(int64_t M, int64_t N, int64_t K,
+                          const void* A, const void* B, const void* C);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_RELU_H */

@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute call).
+
+The library must load, export every entry point that include/gemm_relu.h
+declares, and reject bad arguments before it makes any HIP runtime call.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import tiled_dense_gemm_f16_amd as gr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_relu.h")
+
+
+def declared_functions() -> list[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gemm_relu_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert "gemm_relu_f16" in names and "gemm_relu_f16_ex" in names
+    assert set(names) == set(gr.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gr.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", gr.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+
+
+def test_library_targets_gfx950_only(tmp_path):
+    fatbin = tmp_path / "fatbin.bin"
+    subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", gr.LIB_PATH, str(fatbin)],
+                   check=True)
+    out = subprocess.run(["/opt/rocm/llvm/bin/clang-offload-bundler", "--list", "--type=o",
+                          f"--input={fatbin}"], capture_output=True, text=True, check=True)
+    targets = [t for t in out.stdout.split() if "amdgcn" in t]
+    assert targets and all("gfx950" in t for t in targets), targets
+
+
+def test_strerror_and_tiles():
+    assert gr.strerror(gr.OK) == "success"
+    for s in (gr.EINVAL, gr.EUNSUPPORTED, gr.EHIP, gr.ENOMEM):
+        assert gr.strerror(s) and gr.strerror(s) != "success"
+    assert gr.strerror(999) == "unknown status"
+    n = gr.tile_count()
+    assert n >= 4
+    names = [gr.tile_name(i) for i in range(n)]
+    assert all(names) and len(set(names)) == n
+    assert "128x128x64" in names[1]  # the pages' tile is kept as a named entry
+    assert gr.tile_name(-1) == "" and gr.tile_name(n) == ""
+
+
+def test_tile_selection_is_host_only():
+    # large square -> the 256x256 tile; few rows -> the skinny tile
+    assert gr.select_tile(4096, 4096, 4096) == 0
+    assert gr.select_tile(16, 8192, 8192) == 3
+    # K or N not a multiple of 8 -> the generic element-wise path
+    assert gr.select_tile(64, 64, 7) == -1
+    assert gr.select_tile(64, 9, 64) == -1
+    # misaligned pointers -> generic path
+    assert gr.select_tile(64, 64, 64, 0x1000, 0x2002, 0x3000) == -1
+    assert gr.select_tile(64, 64, 64, 0x1000, 0x2000, 0x3000) >= 0
+
+
+FAKE = 0x10000  # never dereferenced: these calls must fail validation first
+
+
+@pytest.mark.parametrize("M,N,K", [(-1, 4, 4), (4, -1, 4), (4, 4, -1)])
+def test_negative_sizes_rejected(M, N, K):
+    assert gr.gemm_relu_f16(M, N, K, FAKE, FAKE * 2, FAKE * 3) == gr.EINVAL
+
+
+def test_null_pointers_rejected():
+    assert gr.gemm_relu_f16(4, 4, 4, 0, FAKE, FAKE * 3) == gr.EINVAL
+    assert gr.gemm_relu_f16(4, 4, 4, FAKE, 0, FAKE * 3) == gr.EINVAL
+    assert gr.gemm_relu_f16(4, 4, 4, FAKE, FAKE * 2, 0) == gr.EINVAL
+
+
+def test_oversized_and_misaligned_rejected():
+    assert gr.gemm_relu_f16(2 ** 31, 4, 4, FAKE, FAKE * 2, FAKE * 3) == gr.EUNSUPPORTED
+    assert gr.gemm_relu_f16(4, 4, 4, FAKE + 1, FAKE * 2, FAKE * 3) == gr.EUNSUPPORTED
+
+
+def test_overlap_rejected():
+    # C overlapping A (4x4 fp16 = 32 bytes)
+    assert gr.gemm_relu_f16(4, 4, 4, FAKE, FAKE * 2, FAKE + 16) == gr.EINVAL
+    assert gr.gemm_relu_f16(4, 4, 4, FAKE, FAKE * 2, FAKE * 2 - 16) == gr.EINVAL
+
+
+def test_bad_opts_rejected():
+    o = gr.make_opts(tile=gr.tile_count())
+    assert gr.gemm_relu_f16_ex(4, 4, 4, FAKE, FAKE * 2, FAKE * 3, 0, o) == gr.EUNSUPPORTED
+    o = gr.make_opts(block_order=7)
+    assert gr.gemm_relu_f16_ex(4, 4, 4, FAKE, FAKE * 2, FAKE * 3, 0, o) == gr.EINVAL
+    o = gr.make_opts()
+    o.reserved[2] = 1
+    assert gr.gemm_relu_f16_ex(4, 4, 4, FAKE, FAKE * 2, FAKE * 3, 0, o) == gr.EINVAL
+
+
+def test_empty_output_is_a_no_op():
+    # M == 0 or N == 0: success without touching the device (NULL is fine then)
+    assert gr.gemm_relu_f16(0, 5, 5, 0, FAKE, 0) == gr.OK
+    assert gr.gemm_relu_f16(5, 0, 5, FAKE, 0, 0) == gr.OK
+
+
+def test_python_wrapper_rejects_bad_tensors():
+    import torch
+    a = torch.zeros(4, 4, dtype=torch.float16)
+    with pytest.raises((TypeError, ValueError)):
+        gr.gemm_relu(a.float(), a)
+    with pytest.raises(ValueError):
+        gr.gemm_relu(a, torch.zeros(5, 4, dtype=torch.float16))
+    with pytest.raises(ValueError):  # CPU tensors are not device memory
+        gr.gemm_relu(a, a)
+
+
+def test_product_path_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "tiled_dense_gemm_f16_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".hpp", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f

@@ -1,0 +1,225 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Every case draws seeded inputs on the CPU, runs gemm_relu_f16 on cuda:0 and
+compares with the oracle element by element: within rtol = atol = 1e-2 for
+floating-point inputs (plus the tighter fp32-accumulation bound), bit for bit
+for integer-valued inputs, whose fp32 sums are exact in any order.
+"""
+from __future__ import annotations
+
+import itertools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import tiled_dense_gemm_f16_amd as gr  # noqa: E402
+
+
+def say(*msg):
+    print(*msg, file=sys.stderr, flush=True)
+
+
+def run(a_cpu, b_cpu, **kw) -> np.ndarray:
+    a = a_cpu.cuda()
+    b = b_cpu.cuda()
+    c = gr.gemm_relu(a, b, **kw)
+    torch.cuda.synchronize()
+    return workloads.as_u16(c.cpu())
+
+
+def neg(t):
+    return (-t).contiguous()
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("w", [workloads.SQUARE_256, workloads.SQUARE_1024, workloads.RAGGED,
+                               workloads.SKINNY], ids=lambda w: w.name)
+def test_workload_full_parity(w):
+    say(f"[parity] {w.name} M={w.M} N={w.N} K={w.K} seed={w.seed} tile={gr.select_tile(w.M, w.N, w.K)}")
+    a, b = workloads.workload_inputs(w)
+    A, B = workloads.as_u16(a), workloads.as_u16(b)
+    for sign, aa, AA in ((+1, a, A), (-1, neg(a), workloads.as_u16(neg(a)))):
+        got = run(aa, b)
+        want, absdot = oracle.gemm_relu_f16(AA, B, want_absdot=True)
+        st = parity.check(got, want, absdot=absdot, K=w.K, label=f"{w.name} sign={sign}")
+        say(f"  sign={sign:+d} {st}")
+
+
+def test_workload_4096_sampled():
+    w = workloads.SQUARE_4096
+    say(f"[parity] {w.name} sampled, tile={gr.select_tile(w.M, w.N, w.K)}")
+    a, b = workloads.workload_inputs(w)
+    A, B = workloads.as_u16(a), workloads.as_u16(b)
+    got = run(a, b)
+    got_neg = run(neg(a), b)
+    # properties at full size: finite, non-negative, never both signs positive
+    g = parity.f16_values(got)
+    gn = parity.f16_values(got_neg)
+    assert np.isfinite(g).all() and (g >= 0).all()
+    assert not ((g > 0) & (gn > 0)).any()
+    # whole rows at the start, middle and end (every column tile, every lane)
+    for r0, r1 in ((0, 8), (2044, 2052), (4088, 4096)):
+        want, absdot = oracle.gemm_relu_f16(A, B, rows=(r0, r1), want_absdot=True)
+        parity.check(got[r0:r1], want, absdot=absdot, K=w.K, label=f"rows {r0}:{r1}")
+    # random elements, both signs
+    rng = np.random.default_rng(4096)
+    ii = rng.integers(0, w.M, 4096)
+    jj = rng.integers(0, w.N, 4096)
+    want, absdot = oracle.gemm_relu_f16_points(A, B, ii, jj, want_absdot=True)
+    parity.check(got[ii, jj], want, absdot=absdot, K=w.K, label="points")
+    AN = workloads.as_u16(neg(a))
+    want_n, absdot_n = oracle.gemm_relu_f16_points(AN, B, ii, jj, want_absdot=True)
+    parity.check(got_neg[ii, jj], want_n, absdot=absdot_n, K=w.K, label="points, -A")
+
+
+# ---------------------------------------------------------------------------
+# bit-exact cases: integer-valued inputs make every fp32 partial sum exact
+# ---------------------------------------------------------------------------
+
+INT_SHAPES = [(256, 256, 256), (1000, 1016, 1000), (16, 8192, 8192), (512, 512, 4096),
+              (33, 47, 129), (100, 77, 333), (1, 1, 1), (300, 260, 64)]
+
+
+@pytest.mark.parametrize("M,N,K", INT_SHAPES)
+def test_integer_inputs_bit_exact(M, N, K):
+    say(f"[exact] M={M} N={N} K={K} tile={gr.select_tile(M, N, K)}")
+    a, b = workloads.make_inputs(M, N, K, dist="intsmall", seed=M + N + K)
+    want = oracle.gemm_relu_f16(workloads.as_u16(a), workloads.as_u16(b))
+    got = run(a, b)
+    assert np.array_equal(got, want), f"{np.sum(got != want)} mismatches"
+
+
+EDGE = [1, 7, 8, 9, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 257]
+
+
+def edge_triples():
+    # every value in every position, paired with a spread of partners
+    out = set()
+    for i, v in enumerate(EDGE):
+        p = EDGE[(i * 5 + 3) % len(EDGE)]
+        q = EDGE[(i * 7 + 11) % len(EDGE)]
+        out.update({(v, p, q), (p, v, q), (q, p, v)})
+    return sorted(out)
+
+
+@pytest.mark.parametrize("M,N,K", edge_triples())
+def test_edge_shapes_every_tile(M, N, K):
+    a, b = workloads.make_inputs(M, N, K, dist="intsmall", seed=M * 7 + N * 3 + K)
+    want = oracle.gemm_relu_f16(workloads.as_u16(a), workloads.as_u16(b))
+    for tile in [None] + list(range(gr.tile_count())):
+        say(f"[edge] M={M} N={N} K={K} tile={tile}")
+        got = run(a, b, tile=tile)
+        assert np.array_equal(got, want), f"tile {tile}: {np.sum(got != want)} mismatches"
+
+
+@pytest.mark.parametrize("tile", range(4))
+@pytest.mark.parametrize("w", [workloads.SQUARE_1024, workloads.RAGGED], ids=lambda w: w.name)
+def test_each_tile_on_workloads(w, tile):
+    say(f"[tile] {w.name} tile={tile} {gr.tile_name(tile)}")
+    a, b = workloads.workload_inputs(w)
+    A, B = workloads.as_u16(a), workloads.as_u16(b)
+    want, absdot = oracle.gemm_relu_f16(A, B, want_absdot=True)
+    parity.check(run(a, b, tile=tile), want, absdot=absdot, K=w.K, label=f"tile {tile}")
+
+
+# ---------------------------------------------------------------------------
+# memory safety: NaN guard bands after the inputs, sentinels around C
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,off", [(1000, 1016, 1000, 0), (129, 65, 257, 0), (16, 8192, 1000, 0),
+                                       (100, 96, 200, 1), (77, 40, 24, 3)])
+def test_guard_bands(M, N, K, off):
+    say(f"[guard] M={M} N={N} K={K} elem offset={off}")
+    a, b = workloads.make_inputs(M, N, K, dist="intsmall", seed=5)
+    want = oracle.gemm_relu_f16(workloads.as_u16(a), workloads.as_u16(b))
+    G = 4096  # guard elements
+    nan = float("nan")
+    abuf = torch.full((off + M * K + G,), nan, dtype=torch.float16, device="cuda")
+    bbuf = torch.full((off + K * N + G,), nan, dtype=torch.float16, device="cuda")
+    abuf[off:off + M * K] = a.reshape(-1).cuda()
+    bbuf[off:off + K * N] = b.reshape(-1).cuda()
+    sentinel = torch.tensor([0x7777], dtype=torch.int16).view(torch.float16).item()
+    cbuf = torch.full((G + off + M * N + G,), sentinel, dtype=torch.float16, device="cuda")
+    av = abuf[off:off + M * K].view(M, K)
+    bv = bbuf[off:off + K * N].view(K, N)
+    cv = cbuf[G + off:G + off + M * N].view(M, N)
+    gr.gemm_relu(av, bv, out=cv)
+    torch.cuda.synchronize()
+    cb = workloads.as_u16(cbuf.cpu())
+    assert (cb[:G + off] == 0x7777).all(), "write before C"
+    assert (cb[G + off + M * N:] == 0x7777).all(), "write after C"
+    assert np.array_equal(cb[G + off:G + off + M * N].reshape(M, N), want)
+
+
+# ---------------------------------------------------------------------------
+# invariance and hygiene
+# ---------------------------------------------------------------------------
+
+def test_block_order_does_not_change_results():
+    w = workloads.RAGGED
+    a, b = workloads.workload_inputs(w)
+    ref = run(a, b)
+    for order, gm in ((gr.ORDER_ROW_MAJOR, 0), (gr.ORDER_DEFAULT, 1), (gr.ORDER_DEFAULT, 2),
+                      (gr.ORDER_DEFAULT, 8), (gr.ORDER_DEFAULT, 64)):
+        say(f"[order] order={order} group_m={gm}")
+        assert np.array_equal(run(a, b, block_order=order, group_m=gm), ref)
+
+
+@pytest.mark.parametrize("w", [workloads.SQUARE_1024, workloads.RAGGED, workloads.SKINNY], ids=lambda w: w.name)
+def test_deterministic_over_repeats(w):
+    say(f"[determinism] {w.name}")
+    a, b = workloads.workload_inputs(w)
+    a, b = a.cuda(), b.cuda()
+    ref = gr.gemm_relu(a, b).clone()
+    out = torch.empty_like(ref)
+    for _ in range(50):
+        out.fill_(1.0)
+        gr.gemm_relu(a, b, out=out)
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    torch.cuda.synchronize()
+
+
+def test_nondefault_stream():
+    w = workloads.SQUARE_1024
+    a, b = workloads.workload_inputs(w)
+    ref = run(a, b)
+    s = torch.cuda.Stream()
+    ad, bd = a.cuda(), b.cuda()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        c = gr.gemm_relu(ad, bd)
+    s.synchronize()
+    assert np.array_equal(workloads.as_u16(c.cpu()), ref)
+
+
+def test_k_zero_gives_zero():
+    a = torch.empty((33, 0), dtype=torch.float16, device="cuda")
+    b = torch.empty((0, 40), dtype=torch.float16, device="cuda")
+    c = torch.full((33, 40), 3.0, dtype=torch.float16, device="cuda")
+    gr.gemm_relu(a, b, out=c)
+    torch.cuda.synchronize()
+    assert not c.float().abs().sum().item()
+
+
+def test_raw_abi_call_and_empty_shapes():
+    a, b = workloads.make_inputs(64, 64, 64, seed=1)
+    ad, bd = a.cuda(), b.cuda()
+    c = torch.zeros((64, 64), dtype=torch.float16, device="cuda")
+    st = gr.gemm_relu_f16(64, 64, 64, ad.data_ptr(), bd.data_ptr(), c.data_ptr(),
+                          torch.cuda.current_stream().cuda_stream)
+    assert st == gr.OK
+    torch.cuda.synchronize()
+    want = oracle.gemm_relu_f16(workloads.as_u16(a), workloads.as_u16(b))
+    parity.check(workloads.as_u16(c.cpu()), want, label="raw call")
+    assert gr.gemm_relu_f16(0, 64, 64, ad.data_ptr(), bd.data_ptr(), c.data_ptr(), 0) == gr.OK

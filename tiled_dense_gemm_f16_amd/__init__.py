@@ -1,0 +1,12 @@
+"""MI355X (gfx950) fp16 GEMM with a fused ReLU: C = ReLU(A @ B).
+
+The computation is the GEMM + ReLU example of "Writing high-performance
+kernels in TileLang" (section "Escribamos un GEMM"), implemented as
+hand-written HIP for CDNA4 behind the C ABI in ``include/gemm_relu.h``.
+This package is the thin Python binding of that ABI.
+"""
+from ._binding import (  # noqa: F401
+    EHIP, EINVAL, ENOMEM, EUNSUPPORTED, EXPORTED, LIB_PATH, OK, ORDER_DEFAULT, ORDER_ROW_MAJOR,
+    TILE_AUTO, GemmReluError, Opts, gemm_relu, gemm_relu_f16, gemm_relu_f16_ex, load, make_opts,
+    select_tile, strerror, tile_count, tile_name,
+)

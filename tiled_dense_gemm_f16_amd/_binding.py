@@ -1,0 +1,137 @@
+"""ctypes binding of libgemm_relu.so (the C ABI in include/gemm_relu.h).
+
+Argument marshalling only: every step of C = ReLU(A @ B) runs in the HIP
+library. Torch is used for device memory and streams. There is no fallback: if
+the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgemm_relu.so")
+
+OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, 1, 2, 3, 4
+TILE_AUTO = -1
+ORDER_DEFAULT, ORDER_ROW_MAJOR = 0, 1
+
+
+class GemmReluError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"gemm_relu status {status}: {msg}")
+        self.status = status
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("tile", ctypes.c_int32), ("block_order", ctypes.c_int32),
+                ("group_m", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+EXPORTED = ("gemm_relu_f16", "gemm_relu_f16_ex", "gemm_relu_strerror", "gemm_relu_tile_count",
+            "gemm_relu_tile_name", "gemm_relu_select_tile")
+
+
+def load():
+    """Load the library, building it first only if it has never been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            from . import build as _build
+            _build.build()
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib.gemm_relu_f16.argtypes = [i64, i64, i64, p, p, p, p]
+        lib.gemm_relu_f16.restype = i32
+        lib.gemm_relu_f16_ex.argtypes = [i64, i64, i64, p, p, p, p, ctypes.POINTER(Opts)]
+        lib.gemm_relu_f16_ex.restype = i32
+        lib.gemm_relu_strerror.argtypes = [i32]
+        lib.gemm_relu_strerror.restype = ctypes.c_char_p
+        lib.gemm_relu_tile_count.argtypes = []
+        lib.gemm_relu_tile_count.restype = i32
+        lib.gemm_relu_tile_name.argtypes = [i32]
+        lib.gemm_relu_tile_name.restype = ctypes.c_char_p
+        lib.gemm_relu_select_tile.argtypes = [i64, i64, i64, p, p, p]
+        lib.gemm_relu_select_tile.restype = i32
+        _lib = lib
+        return lib
+
+
+def strerror(status: int) -> str:
+    return load().gemm_relu_strerror(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise GemmReluError(status, strerror(status))
+
+
+def make_opts(tile: int | None = None, block_order: int = ORDER_DEFAULT, group_m: int = 0) -> Opts:
+    o = Opts()
+    o.tile = TILE_AUTO if tile is None else int(tile)
+    o.block_order = int(block_order)
+    o.group_m = int(group_m)
+    return o
+
+
+def gemm_relu_f16(M: int, N: int, K: int, A: int, B: int, C: int, stream: int = 0) -> int:
+    """Raw C-ABI call with integer device pointers; returns the status code."""
+    return load().gemm_relu_f16(M, N, K, A or None, B or None, C or None, stream or None)
+
+
+def gemm_relu_f16_ex(M: int, N: int, K: int, A: int, B: int, C: int, stream: int = 0,
+                     opts: Opts | None = None) -> int:
+    """Raw C-ABI call with launch options; returns the status code."""
+    return load().gemm_relu_f16_ex(M, N, K, A or None, B or None, C or None, stream or None,
+                                   ctypes.byref(opts) if opts is not None else None)
+
+
+def tile_count() -> int:
+    return int(load().gemm_relu_tile_count())
+
+
+def tile_name(tile: int) -> str:
+    return load().gemm_relu_tile_name(int(tile)).decode()
+
+
+def select_tile(M: int, N: int, K: int, A: int = 0, B: int = 0, C: int = 0) -> int:
+    return int(load().gemm_relu_select_tile(M, N, K, A or None, B or None, C or None))
+
+
+def gemm_relu(a, b, out=None, *, tile: int | None = None, block_order: int = ORDER_DEFAULT,
+              group_m: int = 0, stream=None):
+    """C = ReLU(a @ b) for fp16 CUDA(HIP) tensors a[M,K], b[K,N]; returns out[M,N].
+
+    Enqueued on torch's current stream (or ``stream``); does not synchronise.
+    """
+    import torch
+
+    if a.dtype != torch.float16 or b.dtype != torch.float16:
+        raise TypeError("a and b must be float16")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not chain")
+    if not (a.is_cuda and b.is_cuda) or a.device != b.device:
+        raise ValueError("a and b must be on the same GPU")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous row-major")
+    M, K = a.shape
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=a.device)
+    else:
+        if out.dtype != torch.float16 or tuple(out.shape) != (M, N) or out.device != a.device:
+            raise ValueError("out must be float16 [M, N] on the inputs' device")
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+    s = stream if stream is not None else torch.cuda.current_stream(a.device)
+    opts = make_opts(tile, block_order, group_m)
+    with torch.cuda.device(a.device):
+        _check(gemm_relu_f16_ex(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(),
+                                s.cuda_stream, opts))
+    return out
