@@ -31,7 +31,7 @@ PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA: 256 CU x 4096 FLOP/clk x 2
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "TFLOP/s and % of MI355X dense FP16 MFMA peak, fp16 GEMM+ReLU 4096³"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_relu.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "tiled_dense_gemm_f16_amd", "csrc", "gemm_relu.hip"),
+KERNEL_SOURCES = [os.path.join(ROOT, "tiled_dense_gemm_f16_amd", "csrc", f) for f in ("gemm_relu.hip", "common.hpp", "pipelined.hpp", "staged.hpp")] + [
                   os.path.join(ROOT, "include", "gemm_relu.h")]
 
 

@@ -1,0 +1,301 @@
+// Pipelined kernel for large tiles: the hot path at big problem sizes.
+//
+// Same computation as the TileLang GEMM + ReLU example ("Writing
+// high-performance kernels in TileLang", section "Escribamos un GEMM"):
+// a BM x BN tile of C per workgroup, K walked in BK-wide steps staged through
+// shared memory, fp32 accumulators in registers, max(x, 0), fp16 store. The
+// gfx950 design:
+//
+//  * Direct-to-LDS loads. Each `buffer_load_dwordx4 ... lds` moves 1 KiB (64
+//    lanes x 16 B) from global memory straight into LDS without passing
+//    through registers. A lane whose element lies outside the matrix is given
+//    an offset past the buffer's end and the hardware writes zeros: that is
+//    the masking of ragged edge tiles (M, N and the K tail).
+//  * A four-stage LDS ring of BK = 32 steps (4 x 32 KiB at 256 x 256).
+//    While step k is multiplied, steps k+1 and k+2 are in flight and step
+//    k+3 is issued. Each stage is its own LDS array, so the compiler can tell
+//    the stages apart and never drains the whole ring.
+//  * One barrier per step, placed between the two 16-deep halves of the step:
+//    after it, the next step's first fragments are read while the current
+//    step's second half runs on the matrix cores.
+//  * Tile products on v_mfma_f32_32x32x16_f16 (one 64-lane wave per TM x TN
+//    sub-tile). The B fragment is the first operand, so each lane of the
+//    32x32 result holds runs of four consecutive columns of one row of C.
+//  * A is stored k-contiguous ([BM][32]) and read with ds_read_b128. B is
+//    stored as it lies in memory, n-contiguous ([32][BN]), and read with the
+//    gfx950 transposing LDS load ds_read_b64_tr_b16, which hands each lane
+//    four k-values of one column: no register transpose.
+//  * XOR swizzles of the 16-byte chunk index (applied when choosing which
+//    global chunk each lane fetches) keep both fragment reads free of LDS
+//    bank conflicts; the direct loads themselves write 1 KiB linearly.
+//  * Epilogue: ReLU on the fp32 accumulators, v_cvt_f16_f32 (round to
+//    nearest even), 8-byte stores.
+//
+// Requirements (checked on the host): K % 8 == 0, N % 8 == 0, A, B and C
+// 16-byte aligned, BM * K * 2 and 32 * N * 2 below 2^31.
+#pragma once
+
+#include "common.hpp"
+
+namespace gemm_relu {
+namespace pipelined {
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = 4;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int NW = WAVES_M * WAVES_N, NT = kWave * NW;
+    static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;  // wave sub-tile
+    static constexpr int FM = TM / 32, FN = TN / 32;              // 32x32 MFMA blocks
+    static constexpr int A_HALVES = BM * BK, B_HALVES = BK * BN;  // per stage
+    static constexpr int A_LOADS = A_HALVES * 2 / 1024;            // 1 KiB loads per stage
+    static constexpr int B_LOADS = B_HALVES * 2 / 1024;
+    static constexpr int A_LOADS_W = A_LOADS / NW, B_LOADS_W = B_LOADS / NW;
+    static constexpr int LPT = A_LOADS_W + B_LOADS_W;              // loads per wave per step
+    static constexpr int B_ROW_BYTES = BN * 2;
+    static_assert(A_LOADS % NW == 0 && B_LOADS % NW == 0, "loads must split evenly over waves");
+    static_assert(TM % 32 == 0 && TN % 128 == 0, "wave sub-tile: 32-row blocks, 128-column units");
+    static_assert(2 * LPT < 64, "vmcnt range");
+};
+
+// A: row r of a stage holds 32 halves = four 16-byte chunks; logical chunk c
+// sits at physical chunk c ^ a_swz(r). Sixteen consecutive rows read at one
+// logical chunk then cover 16 distinct 16-byte slots of a 256-byte span,
+// and any 8 consecutive rows 8 distinct slots of a 128-byte span.
+__device__ __forceinline__ int a_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// B: row kr of a stage holds BN halves; logical chunk c sits at physical chunk
+// c ^ b_swz(kr). A transposing read touches four consecutive rows (kr % 4 =
+// 0..3) at one 32-byte column pair; XOR-ing the pair index with kr % 4 spreads
+// them over four pairs.
+__device__ __forceinline__ int b_swz(int kr) { return 2 * (kr & 3); }
+
+template <class T>
+__global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
+{
+    // One LDS array per stage (A tile, then B tile): the compiler tracks
+    // direct-to-LDS writes per array, so distinct arrays keep the reads of
+    // one stage from waiting on the loads into another.
+    __shared__ __attribute__((aligned(1024))) uint16_t st0[T::A_HALVES + T::B_HALVES];
+    __shared__ __attribute__((aligned(1024))) uint16_t st1[T::A_HALVES + T::B_HALVES];
+    __shared__ __attribute__((aligned(1024))) uint16_t st2[T::A_HALVES + T::B_HALVES];
+    __shared__ __attribute__((aligned(1024))) uint16_t st3[T::A_HALVES + T::B_HALVES];
+    auto stage_a = [&]<int S>() -> uint16_t* {
+        if constexpr (S == 0) return st0;
+        else if constexpr (S == 1) return st1;
+        else if constexpr (S == 2) return st2;
+        else return st3;
+    };
+    auto stage_b = [&]<int S>() -> uint16_t* { return stage_a.template operator()<S>() + T::A_HALVES; };
+
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+    const int M = p.M, N = p.N, K = p.K;
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+    const int nk = (K + T::BK - 1) / T::BK;
+
+    // ---- per-lane global offsets of this wave's direct loads (bytes, relative
+    // to the step's descriptor base: A + m0*K + k0 and B + k0*N) ----
+    uint32_t a_off[T::A_LOADS_W];
+    int a_kc[T::A_LOADS_W];  // logical k-chunk of the lane, for the K tail
+#pragma unroll
+    for (int i = 0; i < T::A_LOADS_W; ++i) {
+        const int gi = wave * T::A_LOADS_W + i;
+        const int row = gi * 16 + lane / 4;
+        const int c = (lane % 4) ^ a_swz(row);
+        a_kc[i] = c;
+        a_off[i] = (m0 + row < M) ? (uint32_t)(row * K + c * 8) * 2u : kOOB;
+    }
+    uint32_t b_off[T::B_LOADS_W];
+    int b_kr[T::B_LOADS_W];
+#pragma unroll
+    for (int i = 0; i < T::B_LOADS_W; ++i) {
+        const int gi = wave * T::B_LOADS_W + i;
+        const int kr = gi * 2 + lane / 32;
+        const int c = (lane % 32) ^ b_swz(kr);
+        b_kr[i] = kr;
+        b_off[i] = (n0 + c * 8 < N) ? (uint32_t)(kr * N + n0 + c * 8) * 2u : kOOB;
+    }
+
+    // Issue step kt's loads into stage S. Steps past the end of K get empty
+    // descriptors: every lane is out of range and the stage is filled with
+    // zeros.
+    auto issue = [&]<int S>(int kt) {
+        // Branch-free on purpose (see the step below): byte counts are clamped
+        // at zero arithmetically and the K mask is applied on every step.
+        const int k0 = kt * T::BK;
+        int64_t arem = ((int64_t)(M - m0) * K - k0) * 2;
+        int64_t brem = ((int64_t)K - k0) * N * 2;
+        arem &= ~(arem >> 63);
+        brem &= ~(brem >> 63);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * K + k0, (uint64_t)arem);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)k0 * N, (uint64_t)brem);
+        uint16_t* sa = stage_a.template operator()<S>();
+        uint16_t* sb = stage_b.template operator()<S>();
+#pragma unroll
+        for (int i = 0; i < T::A_LOADS_W; ++i) {
+            const uint32_t off = (k0 + a_kc[i] * 8 < K) ? a_off[i] : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (GR_LDS void*)(sa + (wave * T::A_LOADS_W + i) * 512), 16, (int)off, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < T::B_LOADS_W; ++i) {
+            const uint32_t off = (k0 + b_kr[i] < K) ? b_off[i] : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (GR_LDS void*)(sb + (wave * T::B_LOADS_W + i) * 512), 16, (int)off, 0, 0, 0);
+        }
+    };
+
+    // ---- per-lane LDS byte offsets of the fragment reads ----
+    // A block i, half h of a step: row wm*TM + 32i + lane%32, chunk 2h + lane/32.
+    const int ar = wm * T::TM + lane % 32;
+    uint32_t a_rd[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) a_rd[h] = ar * 64 + (((2 * h + lane / 32) ^ a_swz(lane % 32)) * 16);
+    // B block j: the 16-lane group g reads rows 8*(g/2) + 4*t + (lane%16)/4
+    // (t = 0, 1 for the two transposing reads) and columns
+    //   wn*TN + 128*(j/4) + 16*(j%4) + 64*(g%2) + 4*(lane%4) .. +3,
+    // so result row d of the 32x32 block is column 16*(j%4) + 64*(d/16) + d%16
+    // of the 128-column unit.
+    const int g = lane / 16, q16 = lane % 16;
+    uint32_t b_rd[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int kr = 8 * (g / 2) + q16 / 4;
+        const int col = wn * T::TN + 16 * j + 64 * (g % 2) + 4 * (q16 % 4);
+        const int c = col / 8;
+        b_rd[j] = kr * T::B_ROW_BYTES + ((c ^ b_swz(kr)) * 16) + 8 * ((col / 4) % 2);
+    }
+
+    // fragments of one 16-deep half-step
+    struct Frag {
+        f16x8 a[T::FM];
+        f16x8 b[T::FN];
+    };
+    auto read_frag = [&]<int S>(int half, Frag& f) {
+        const char* sa = reinterpret_cast<const char*>(stage_a.template operator()<S>());
+        const char* sb = reinterpret_cast<const char*>(stage_b.template operator()<S>());
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+            f.a[i] = *reinterpret_cast<const f16x8*>(sa + a_rd[half] + i * 32 * 64);
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+            const char* base = sb + b_rd[j % 4] + (j / 4) * 256 + half * 16 * T::B_ROW_BYTES;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GR_LDS i16x4*)(base));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GR_LDS i16x4*)(base + 4 * T::B_ROW_BYTES));
+            const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            f.b[j] = __builtin_bit_cast(f16x8, v);
+        }
+    };
+
+    f32x16 acc[T::FM][T::FN];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // The matrix operations of one half-step. The fragment reads of the next
+    // half-step were issued just before in the same basic block; the
+    // scheduling groups below interleave them, two at a time, between the
+    // first matrix operations, so they are in flight while the matrix cores
+    // work instead of being sunk to the point of use.
+    auto mma = [&](const Frag& f) {
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+        constexpr int kReads = T::FM + 2 * T::FN, kMfma = T::FM * T::FN;
+        constexpr int kPaired = (kReads + 1) / 2;
+        static_assert(kPaired <= kMfma, "more read pairs than matrix operations");
+#pragma unroll
+        for (int i = 0; i < kPaired; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kPaired, 0);
+    };
+
+    // Wait until this wave's loads older than the newest `N` are in LDS and its
+    // LDS reads are done, then meet the other waves.
+    auto sync = [&]<int N>() {
+        static_assert(N >= 0 && N < 64, "vmcnt range");
+        __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));  // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    // The ring runs for nk4 = nk rounded up to a multiple of 4 steps, so that
+    // the 4-way unrolled loop has no exits and no branch around the matrix
+    // operations (such branches make the register allocator copy the whole
+    // accumulator). The extra steps multiply zero tiles.
+    const int nk4 = (nk + 3) & ~3;
+    Frag x, y;
+    if (nk4 > 0) {
+        // prologue: steps 0..2 in flight, wait for step 0
+        issue.template operator()<0>(0);
+        issue.template operator()<1>(1);
+        issue.template operator()<2>(2);
+        sync.template operator()<2 * T::LPT>();
+        read_frag.template operator()<0>(0, x);
+    }
+
+    // One pipeline step on stage S = kt % 4. The body has no branches: the
+    // loads of step kt+3 are issued even past the end (they are all out of
+    // range and only write zeros into a stage nobody reads any more), so
+    // exactly LPT loads are always younger than step kt+1's, and the compiler
+    // keeps its per-stage tracking of the direct-to-LDS loads.
+    auto step = [&]<int S>(int kt) {
+        read_frag.template operator()<S>(1, y);
+        mma(x);
+        // step kt+1 has landed (kt+2 may still be in flight); after the
+        // barrier every wave is done with stage (kt-1) % 4
+        sync.template operator()<T::LPT>();
+        issue.template operator()<(S + 3) % 4>(kt + 3);
+        read_frag.template operator()<(S + 1) % 4>(0, x);
+        mma(y);
+    };
+
+    for (int kt = 0; kt < nk4; kt += 4) {
+        step.template operator()<0>(kt);
+        step.template operator()<1>(kt + 1);
+        step.template operator()<2>(kt + 2);
+        step.template operator()<3>(kt + 3);
+    }
+    // the zero-filling loads past the end must land before the workgroup's
+    // LDS is released
+    wait_vmcnt<0>();
+
+    // ---- epilogue: ReLU, fp16 (nearest even), 8-byte stores ----
+    // Lane holds, for result rows d = 8q + 4*(lane/32) + r (r = 0..3), the
+    // column 16*(j%4) + 64*(q/2) + 8*(q%2) + 4*(lane/32) + r of unit j/4.
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+        const int m = m0 + wm * T::TM + 32 * i + lane % 32;
+        if (m >= M) continue;
+        uint16_t* crow = p.C + (int64_t)m * N;
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * T::TN + 128 * (j / 4) + 16 * (j % 4) + 64 * (q / 2) + 8 * (q % 2) +
+                              4 * (lane / 32);
+                if (n < N) {
+                    u32x2 w;
+                    w[0] = relu_pack2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+                    w[1] = relu_pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                    *reinterpret_cast<u32x2*>(crow + n) = w;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace pipelined
+}  // namespace gemm_relu

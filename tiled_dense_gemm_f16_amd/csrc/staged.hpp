@@ -1,0 +1,267 @@
+// Register-staged kernel: the first, general-purpose instance of the tiled
+// GEMM + ReLU. It serves small tiles and the generic element-wise path.
+//
+// Each workgroup owns one BM x BN tile of C and walks K in BK = 64 steps:
+//  * 16-byte buffer loads bring the next A and B tiles into registers while
+//    the current tile is multiplied (out-of-range lanes read zeros);
+//  * A is stored k-contiguous ([BM][BK]); B arrives n-contiguous and is
+//    transposed in registers (8x8 blocks of halves) so it is also stored
+//    k-contiguous ([BN][BK]); both use an XOR swizzle of the 16-byte chunk
+//    index, so fragment reads hit distinct LDS banks;
+//  * two LDS stages plus the register prefetch form a three-deep pipeline;
+//  * tile products run on v_mfma_f32_16x16x32_f16 with the B fragment as the
+//    first operand, so the result block is C^T and each lane holds four
+//    consecutive columns of one row -- the epilogue stores 8 bytes per lane.
+// With VEC = false every global access is an element-wise, bounds-checked
+// load or store: any K, N and pointer alignment.
+#pragma once
+
+#include "common.hpp"
+
+namespace gemm_relu {
+namespace staged {
+
+// 16-byte chunk swizzle for a row of 8 chunks (BK = 64 halves): XOR with the
+// row's low three bits, so 8 consecutive rows read at one logical chunk land
+// on 8 different physical chunks (all 32 four-byte banks of a 128-byte span).
+__device__ __forceinline__ int swz(int row) { return row & 7; }
+
+// Transpose an 8x8 block of halves held as 8 rows of 16 bytes: out[c] holds
+// column c (8 values, one per input row).
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8])
+{
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // low half from row 2j, high half from row 2j+1, both at column c
+            out[c][j] = __builtin_amdgcn_perm(in[2 * j + 1][c >> 1], in[2 * j][c >> 1], sel);
+        }
+    }
+}
+
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MIN_WAVES_ = 1>
+struct Tile {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int NT = kWave * WAVES_M * WAVES_N;
+    static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;  // per-wave sub-tile
+    static constexpr int FM = TM / 16, FN = TN / 16;              // 16x16 MFMA blocks
+    static constexpr int KC = BK / 8;                             // 16-byte chunks per row
+    static constexpr int A_CHUNKS = BM * KC;                      // per stage
+    static constexpr int B_UNITS = KC * (BN / 8);                 // 8x8 blocks per stage
+    static constexpr int A_PER_T = (A_CHUNKS + NT - 1) / NT;
+    static constexpr int B_PER_T = (B_UNITS + NT - 1) / NT;
+    static constexpr int STAGE_HALVES = (BM + BN) * BK;
+    static constexpr int LDS_BYTES = 2 * STAGE_HALVES * 2;
+    static constexpr int MIN_WAVES = MIN_WAVES_;
+    static_assert(BK == 64, "the swizzle assumes 8 chunks per row");
+    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole MFMA blocks");
+    static_assert(BM % WAVES_M == 0 && BN % WAVES_N == 0, "waves must divide the tile");
+};
+
+// Registers holding one k-step of the block's operands on their way to LDS.
+template <class T>
+struct Staging {
+    u32x4 a[T::A_PER_T];
+    u32x4 b[T::B_PER_T][8];
+};
+
+template <class T, bool VEC>
+__device__ __forceinline__ void load_tile(const Args& p, int m0, int n0, int k0, Staging<T>& st)
+{
+    const int t = threadIdx.x;
+    const int K = p.K, N = p.N, M = p.M;
+    if constexpr (VEC) {
+        // A: BM rows x KC chunks, block base at row m0, column k0
+        const uint16_t* abase = p.A + (int64_t)m0 * K + k0;
+        const uint64_t arem = ((uint64_t)(M - m0) * (uint64_t)K - (uint64_t)k0) * 2u;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, arem);
+        const bool ktail = (k0 + T::BK > K);
+#pragma unroll
+        for (int i = 0; i < T::A_PER_T; ++i) {
+            const int c = t + i * T::NT;
+            const int row = c / T::KC, kc = c % T::KC;
+            bool ok = (c < T::A_CHUNKS) && (m0 + row < M);
+            if (ktail) ok = ok && (k0 + kc * 8 < K);
+            const uint32_t off = ok ? (uint32_t)(row * K + kc * 8) * 2u : kOOB;
+            st.a[i] = load16(ra, off);
+        }
+        // B: BK rows x BN columns as 8x8 units; unit u -> k-block u % KC,
+        // n-block u / KC (8 consecutive lanes cover one n-block's 8 k-blocks,
+        // so the transposed LDS writes below hit 8 different chunks)
+        const uint16_t* bbase = p.B + (int64_t)k0 * N;
+        const uint64_t brem = (uint64_t)(K - k0) * (uint64_t)N * 2u;
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bbase, brem);
+#pragma unroll
+        for (int i = 0; i < T::B_PER_T; ++i) {
+            const int u = t + i * T::NT;
+            const int kb = u % T::KC, nb = u / T::KC;
+            const bool uok = (u < T::B_UNITS) && (n0 + nb * 8 < N);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int kr = kb * 8 + r;
+                const bool ok = uok && (!ktail || k0 + kr < K);
+                const uint32_t off = ok ? (uint32_t)(kr * N + n0 + nb * 8) * 2u : kOOB;
+                st.b[i][r] = load16(rb, off);
+            }
+        }
+    } else {
+        // element-wise loads with full bounds checks (any K, N, alignment)
+#pragma unroll
+        for (int i = 0; i < T::A_PER_T; ++i) {
+            const int c = t + i * T::NT;
+            const int row = c / T::KC, kc = c % T::KC;
+            uint16_t h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int gm = m0 + row, gk = k0 + kc * 8 + e;
+                h[e] = (c < T::A_CHUNKS && gm < M && gk < K) ? p.A[(int64_t)gm * K + gk] : (uint16_t)0;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st.a[i][j] = (uint32_t)h[2 * j] | ((uint32_t)h[2 * j + 1] << 16);
+        }
+#pragma unroll
+        for (int i = 0; i < T::B_PER_T; ++i) {
+            const int u = t + i * T::NT;
+            const int kb = u % T::KC, nb = u / T::KC;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                uint16_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int gk = k0 + kb * 8 + r, gn = n0 + nb * 8 + e;
+                    h[e] = (u < T::B_UNITS && gk < K && gn < N) ? p.B[(int64_t)gk * N + gn] : (uint16_t)0;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) st.b[i][r][j] = (uint32_t)h[2 * j] | ((uint32_t)h[2 * j + 1] << 16);
+            }
+        }
+    }
+}
+
+template <class T>
+__device__ __forceinline__ void store_tile(uint16_t* As, uint16_t* Bs, const Staging<T>& st)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < T::A_PER_T; ++i) {
+        const int c = t + i * T::NT;
+        if (c < T::A_CHUNKS) {
+            const int row = c / T::KC, kc = c % T::KC;
+            *reinterpret_cast<u32x4*>(As + row * T::BK + ((kc ^ swz(row)) * 8)) = st.a[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_PER_T; ++i) {
+        const int u = t + i * T::NT;
+        if (u < T::B_UNITS) {
+            const int kb = u % T::KC, nb = u / T::KC;
+            u32x4 cols[8];
+            transpose8x8(st.b[i], cols);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int n = nb * 8 + c;
+                *reinterpret_cast<u32x4*>(Bs + n * T::BK + ((kb ^ swz(n)) * 8)) = cols[c];
+            }
+        }
+    }
+}
+
+template <class T>
+__device__ __forceinline__ void compute_tile(const uint16_t* As, const uint16_t* Bs,
+                                             f32x4 (&acc)[T::FM][T::FN], int wm, int wn, int lane)
+{
+    const int lr = lane & 15;  // row (A) / column (B) of the 16-wide fragment
+    const int lg = lane >> 4;  // which 8-wide k-slice of the 32-deep step
+#pragma unroll
+    for (int kk = 0; kk < T::BK / 32; ++kk) {
+        const int c = kk * 4 + lg;
+        f16x8 af[T::FM], bf[T::FN];
+#pragma unroll
+        for (int fm = 0; fm < T::FM; ++fm) {
+            const int r = wm * T::TM + fm * 16 + lr;
+            af[fm] = *reinterpret_cast<const f16x8*>(As + r * T::BK + ((c ^ swz(r)) * 8));
+        }
+#pragma unroll
+        for (int fn = 0; fn < T::FN; ++fn) {
+            const int n = wn * T::TN + fn * 16 + lr;
+            bf[fn] = *reinterpret_cast<const f16x8*>(Bs + n * T::BK + ((c ^ swz(n)) * 8));
+        }
+        // B fragment as the first operand: the result block is C^T, so each
+        // lane ends up holding 4 consecutive columns of one row of C.
+#pragma unroll
+        for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < T::FN; ++fn)
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[fn], af[fm], acc[fm][fn], 0, 0, 0);
+    }
+}
+
+template <class T, bool VEC>
+__global__ void __launch_bounds__(T::NT, T::MIN_WAVES) staged_kernel(Args p)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE_HALVES];
+
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+
+    f32x4 acc[T::FM][T::FN];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = (p.K + T::BK - 1) / T::BK;
+    Staging<T> st;
+    if (nk > 0) {
+        load_tile<T, VEC>(p, m0, n0, 0, st);
+        store_tile<T>(smem, smem + T::BM * T::BK, st);
+        __syncthreads();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        uint16_t* cur = smem + (kt & 1) * T::STAGE_HALVES;
+        uint16_t* nxt = smem + ((kt + 1) & 1) * T::STAGE_HALVES;
+        const bool more = kt + 1 < nk;
+        if (more) load_tile<T, VEC>(p, m0, n0, (kt + 1) * T::BK, st);
+        compute_tile<T>(cur, cur + T::BM * T::BK, acc, wm, wn, lane);
+        if (more) store_tile<T>(nxt, nxt + T::BM * T::BK, st);
+        __syncthreads();
+    }
+
+    // Epilogue: ReLU on the fp32 accumulator, round to fp16 (nearest even),
+    // store. Lane holds rows m, columns n .. n+3 of each 16x16 block.
+    const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int fm = 0; fm < T::FM; ++fm) {
+        const int m = m0 + wm * T::TM + fm * 16 + lr;
+#pragma unroll
+        for (int fn = 0; fn < T::FN; ++fn) {
+            const int n = n0 + wn * T::TN + fn * 16 + lg * 4;
+            const f32x4 v = acc[fm][fn];
+            if (m < p.M) {
+                uint16_t* dst = p.C + (int64_t)m * p.N + n;
+                if constexpr (VEC) {
+                    if (n < p.N) {
+                        u32x2 w;
+                        w[0] = relu_pack2(v[0], v[1]);
+                        w[1] = relu_pack2(v[2], v[3]);
+                        *reinterpret_cast<u32x2*>(dst) = w;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < p.N) dst[r] = relu_f16(v[r]);
+                }
+            }
+        }
+    }
+}
+
+}  // namespace staged
+}  // namespace gemm_relu
