@@ -116,11 +116,17 @@ def cpu_baseline(w, gpu_c, target_s: float = 12.0):
     import oracle
     A, B = workloads.as_u16(gpu_c["a"]), workloads.as_u16(gpu_c["b"])
     threads = oracle.num_threads()
+    # calibrate on a growing slice until one call takes at least 0.5 s (the
+    # first call also pays for starting the thread pool)
     r_cal = min(w.M, max(threads, 8))
-    t = time.perf_counter()
-    oracle.gemm_relu_f16(A, B, rows=(0, r_cal))
-    t_cal = time.perf_counter() - t
-    rows = int(min(w.M, max(r_cal, round(r_cal * target_s / max(t_cal, 1e-6)))))
+    while True:
+        t = time.perf_counter()
+        oracle.gemm_relu_f16(A, B, rows=(0, r_cal))
+        t_cal = time.perf_counter() - t
+        if t_cal >= 0.5 or r_cal >= w.M:
+            break
+        r_cal = min(w.M, r_cal * 4)
+    rows = int(min(w.M, max(1, round(r_cal * target_s / max(t_cal, 1e-6)))))
     t = time.perf_counter()
     ora = oracle.gemm_relu_f16(A, B, rows=(0, rows))
     secs = time.perf_counter() - t
@@ -150,7 +156,7 @@ def result_line(w, r, steps, warmup, cpu=None):
     roof["traffic"] = measured_traffic(w.name)
     line = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
             "warmup": warmup, "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "f16 (fp32 accumulate)", "data": "synthetic",
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16", "accum_dtype": "f32", "data": "synthetic",
             "pct_of_fp16_peak": round(100 * value / PEAK_FP16_TFLOPS, 2),
             "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dist": w.dist,
                        "scale": w.scale, "seed": w.seed, "tile": r["tile"], "parallelism": "single GPU"},
@@ -174,6 +180,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--all", action="store_true", help="also time every workload (lines on stderr)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run an element-wise copy (negation) of MIB MiB, 20 times: a kernel of known "
+                         "traffic, used to scale the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -185,6 +194,17 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        # an element-wise kernel that reads n bytes and writes n bytes (a plain
+        # copy may be served by a DMA engine instead of a kernel)
+        src = torch.ones(n // 2, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 20}), flush=True)
+        return 0
     import tiled_dense_gemm_f16_amd as gr
     gr.load()
 
