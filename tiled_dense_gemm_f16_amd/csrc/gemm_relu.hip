@@ -49,7 +49,10 @@ template <class T>
 hipError_t launch_pipelined(const Args& a, hipStream_t s)
 {
     const int blocks = a.tiles_m * a.tiles_n;
-    hipLaunchKernelGGL((gemm_relu::pipelined::pipelined_kernel<T>), dim3(blocks), dim3(T::NT), 0, s, a);
+    if (a.K % T::BK == 0)
+        hipLaunchKernelGGL((gemm_relu::pipelined::pipelined_kernel<T, true>), dim3(blocks), dim3(T::NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((gemm_relu::pipelined::pipelined_kernel<T, false>), dim3(blocks), dim3(T::NT), 0, s, a);
     return hipGetLastError();
 }
 

@@ -11,13 +11,16 @@
 //    through registers. A lane whose element lies outside the matrix is given
 //    an offset past the buffer's end and the hardware writes zeros: that is
 //    the masking of ragged edge tiles (M, N and the K tail).
-//  * A four-stage LDS ring of BK = 32 steps (4 x 32 KiB at 256 x 256).
-//    While step k is multiplied, steps k+1 and k+2 are in flight and step
-//    k+3 is issued. Each stage is its own LDS array, so the compiler can tell
-//    the stages apart and never drains the whole ring.
-//  * One barrier per step, placed between the two 16-deep halves of the step:
-//    after it, the next step's first fragments are read while the current
-//    step's second half runs on the matrix cores.
+//  * A four-slot LDS ring of BK = 32 steps (4 x 32 KiB at 256 x 256): while
+//    step k is multiplied, steps k+1 and k+2 are in flight and step k+3 is
+//    issued. Each slot is its own LDS array, so the compiler can tell the
+//    slots apart and never drains the whole ring.
+//  * One barrier per step. Between two barriers a wave runs 32 matrix
+//    operations: the second half of one step and the first half of the next.
+//    The loads of a later step and the fragment reads of the next two halves
+//    are issued one or two at a time between the first matrix operations, in
+//    an order fixed in the source, so the matrix cores are never left waiting
+//    behind a cluster of memory instructions.
 //  * Tile products on v_mfma_f32_32x32x16_f16 (one 64-lane wave per TM x TN
 //    sub-tile). The B fragment is the first operand, so each lane of the
 //    32x32 result holds runs of four consecutive columns of one row of C.
@@ -26,10 +29,14 @@
 //    gfx950 transposing LDS load ds_read_b64_tr_b16, which hands each lane
 //    four k-values of one column: no register transpose.
 //  * XOR swizzles of the 16-byte chunk index (applied when choosing which
-//    global chunk each lane fetches) keep both fragment reads free of LDS
-//    bank conflicts; the direct loads themselves write 1 KiB linearly.
-//  * Epilogue: ReLU on the fp32 accumulators, v_cvt_f16_f32 (round to
-//    nearest even), 8-byte stores.
+//    global chunk each lane fetches) spread the fragment reads over the LDS
+//    banks; the direct loads themselves write 1 KiB linearly.
+//  * When K is a multiple of 32 (KALIGNED) no step is partial: the loads carry
+//    no per-lane K test and each step only moves two buffer descriptors.
+//  * Epilogue: ReLU on the fp32 accumulators and v_cvt_f16_f32 (round to
+//    nearest even) into the now idle LDS ring, which holds the whole 256 x 256
+//    fp16 tile; then every lane stores 16 consecutive bytes of a row, so each
+//    store instruction writes two full 512-byte rows of C.
 //
 // Requirements (checked on the host): K % 8 == 0, N % 8 == 0, A, B and C
 // 16-byte aligned, BM * K * 2 and 32 * N * 2 below 2^31.
@@ -48,14 +55,22 @@ struct Cfg {
     static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;  // wave sub-tile
     static constexpr int FM = TM / 32, FN = TN / 32;              // 32x32 MFMA blocks
     static constexpr int A_HALVES = BM * BK, B_HALVES = BK * BN;  // per stage
+    static constexpr int STAGE_BYTES = (A_HALVES + B_HALVES) * 2;
     static constexpr int A_LOADS = A_HALVES * 2 / 1024;            // 1 KiB loads per stage
     static constexpr int B_LOADS = B_HALVES * 2 / 1024;
     static constexpr int A_LOADS_W = A_LOADS / NW, B_LOADS_W = B_LOADS / NW;
     static constexpr int LPT = A_LOADS_W + B_LOADS_W;              // loads per wave per step
     static constexpr int B_ROW_BYTES = BN * 2;
+    static constexpr int NMMA = FM * FN;                           // matrix ops per half-step
+    static constexpr int NSLOT = FM + FN;                          // fragment-read slots per half-step
+    // epilogue: the fp16 C tile, BN * 2 bytes per row, fills the ring exactly
+    static constexpr int C_ROWS_PER_STAGE = STAGE_BYTES / (BN * 2);
     static_assert(A_LOADS % NW == 0 && B_LOADS % NW == 0, "loads must split evenly over waves");
     static_assert(TM % 32 == 0 && TN % 128 == 0, "wave sub-tile: 32-row blocks, 128-column units");
     static_assert(2 * LPT < 64, "vmcnt range");
+    static_assert(LPT <= NMMA && NSLOT <= NMMA, "every load and read slot needs a matrix op to hide behind");
+    static_assert(STAGES * STAGE_BYTES == BM * BN * 2, "the C tile must fill the LDS ring exactly");
+    static_assert(BN == 256, "the epilogue maps 32 lanes x 16 B onto one row of C");
 };
 
 // A: row r of a stage holds 32 halves = four 16-byte chunks; logical chunk c
@@ -70,7 +85,12 @@ __device__ __forceinline__ int a_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; 
 // them over four pairs.
 __device__ __forceinline__ int b_swz(int kr) { return 2 * (kr & 3); }
 
-template <class T>
+// Epilogue C tile in LDS: row r (BN halves = 32 chunks of 16 B), logical chunk
+// c at physical chunk c ^ (r % 32), so the 32 rows that one store of the
+// accumulator layout touches land on 32 different chunks.
+__device__ __forceinline__ int c_swz(int r) { return r & 31; }
+
+template <class T, bool KALIGNED>
 __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
 {
     // One LDS array per stage (A tile, then B tile): the compiler tracks
@@ -110,42 +130,47 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         a_off[i] = (m0 + row < M) ? (uint32_t)(row * K + c * 8) * 2u : kOOB;
     }
     uint32_t b_off[T::B_LOADS_W];
-    int b_kr[T::B_LOADS_W];
 #pragma unroll
     for (int i = 0; i < T::B_LOADS_W; ++i) {
         const int gi = wave * T::B_LOADS_W + i;
         const int kr = gi * 2 + lane / 32;
         const int c = (lane % 32) ^ b_swz(kr);
-        b_kr[i] = kr;
+        // rows past K are cut off by the descriptor's byte count
         b_off[i] = (n0 + c * 8 < N) ? (uint32_t)(kr * N + n0 + c * 8) * 2u : kOOB;
     }
 
-    // Issue step kt's loads into stage S. Steps past the end of K get empty
-    // descriptors: every lane is out of range and the stage is filled with
-    // zeros.
-    auto issue = [&]<int S>(int kt) {
-        // Branch-free on purpose (see the step below): byte counts are clamped
-        // at zero arithmetically and the K mask is applied on every step.
+    // Buffer descriptors of step kt. Steps past the end of K get empty
+    // descriptors: every lane is out of range and the stage fills with zeros.
+    struct Rsrc {
+        __amdgpu_buffer_rsrc_t a, b;
+    };
+    auto descriptors = [&](int kt) -> Rsrc {
         const int k0 = kt * T::BK;
+        const bool live = kt < nk;
         int64_t arem = ((int64_t)(M - m0) * K - k0) * 2;
         int64_t brem = ((int64_t)K - k0) * N * 2;
-        arem &= ~(arem >> 63);
-        brem &= ~(brem >> 63);
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * K + k0, (uint64_t)arem);
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)k0 * N, (uint64_t)brem);
+        arem = live ? arem : 0;
+        brem = live ? brem : 0;
+        return {make_rsrc(p.A + (int64_t)m0 * K + k0, (uint64_t)arem),
+                make_rsrc(p.B + (int64_t)k0 * N, (uint64_t)brem)};
+    };
+    // Load number i (A loads first, then B loads) of step kt into stage S.
+    // (The descriptor is copied into a local first: handing the builtin a
+    // member of a reference keeps the host side from emitting the kernel.)
+    auto load_one = [&]<int S>(int i, const Rsrc& r, int kt) {
         uint16_t* sa = stage_a.template operator()<S>();
         uint16_t* sb = stage_b.template operator()<S>();
-#pragma unroll
-        for (int i = 0; i < T::A_LOADS_W; ++i) {
-            const uint32_t off = (k0 + a_kc[i] * 8 < K) ? a_off[i] : kOOB;
+        if (i < T::A_LOADS_W) {
+            const __amdgpu_buffer_rsrc_t ra = r.a;
+            uint32_t off = a_off[i];
+            if constexpr (!KALIGNED) off = (kt * T::BK + a_kc[i] * 8 < K) ? off : kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (GR_LDS void*)(sa + (wave * T::A_LOADS_W + i) * 512), 16, (int)off, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < T::B_LOADS_W; ++i) {
-            const uint32_t off = (k0 + b_kr[i] < K) ? b_off[i] : kOOB;
+        } else {
+            const __amdgpu_buffer_rsrc_t rb = r.b;
+            const int j = i - T::A_LOADS_W;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (GR_LDS void*)(sb + (wave * T::B_LOADS_W + i) * 512), 16, (int)off, 0, 0, 0);
+                rb, (GR_LDS void*)(sb + (wave * T::B_LOADS_W + j) * 512), 16, (int)b_off[j], 0, 0, 0);
         }
     };
 
@@ -175,14 +200,17 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         f16x8 a[T::FM];
         f16x8 b[T::FN];
     };
-    auto read_frag = [&]<int S>(int half, Frag& f) {
+    // Read slot s of half-step `half` of stage S: slot 0 is A block 0, slots
+    // 1..FN are the B blocks (two transposing reads each), the rest the other
+    // A blocks -- the first matrix operation needs only slots 0 and 1.
+    auto read_slot = [&]<int S>(int half, int s, Frag& f) {
         const char* sa = reinterpret_cast<const char*>(stage_a.template operator()<S>());
         const char* sb = reinterpret_cast<const char*>(stage_b.template operator()<S>());
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i)
+        if (s == 0 || s > T::FN) {
+            const int i = (s == 0) ? 0 : s - T::FN;
             f.a[i] = *reinterpret_cast<const f16x8*>(sa + a_rd[half] + i * 32 * 64);
-#pragma unroll
-        for (int j = 0; j < T::FN; ++j) {
+        } else {
+            const int j = s - 1;
             const char* base = sb + b_rd[j % 4] + (j / 4) * 256 + half * 16 * T::B_ROW_BYTES;
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GR_LDS i16x4*)(base));
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GR_LDS i16x4*)(base + 4 * T::B_ROW_BYTES));
@@ -199,26 +227,9 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // The matrix operations of one half-step. The fragment reads of the next
-    // half-step were issued just before in the same basic block; the
-    // scheduling groups below interleave them, two at a time, between the
-    // first matrix operations, so they are in flight while the matrix cores
-    // work instead of being sunk to the point of use.
-    auto mma = [&](const Frag& f) {
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < T::FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
-        constexpr int kReads = T::FM + 2 * T::FN, kMfma = T::FM * T::FN;
-        constexpr int kPaired = (kReads + 1) / 2;
-        static_assert(kPaired <= kMfma, "more read pairs than matrix operations");
-#pragma unroll
-        for (int i = 0; i < kPaired; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kPaired, 0);
+    auto mma_one = [&](const Frag& f, int u) {
+        const int i = u / T::FN, j = u % T::FN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
     };
 
     // Wait until this wave's loads older than the newest `N` are in LDS and its
@@ -237,63 +248,110 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     // accumulator). The extra steps multiply zero tiles.
     const int nk4 = (nk + 3) & ~3;
     Frag x, y;
-    if (nk4 > 0) {
-        // prologue: steps 0..2 in flight, wait for step 0
-        issue.template operator()<0>(0);
-        issue.template operator()<1>(1);
-        issue.template operator()<2>(2);
-        sync.template operator()<2 * T::LPT>();
-        read_frag.template operator()<0>(0, x);
-    }
 
-    // One pipeline step on stage S = kt % 4. The body has no branches: the
-    // loads of step kt+3 are issued even past the end (they are all out of
-    // range and only write zeros into a stage nobody reads any more), so
-    // exactly LPT loads are always younger than step kt+1's, and the compiler
-    // keeps its per-stage tracking of the direct-to-LDS loads.
-    auto step = [&]<int S>(int kt) {
-        read_frag.template operator()<S>(1, y);
-        mma(x);
-        // step kt+1 has landed (kt+2 may still be in flight); after the
-        // barrier every wave is done with stage (kt-1) % 4
+    // The code between the barriers of steps kt and kt+1 (S = kt % 4):
+    //  block A: the 16 matrix ops of step kt, second half (fragments y), with
+    //           the loads of step kt+3 and the reads of step kt+1's first half
+    //           (into x) issued one by one between them;
+    //  block B: the 16 matrix ops of step kt+1, first half (fragments x), with
+    //           the reads of step kt+1's second half (into y) between them.
+    // Step kt+1's data is in LDS: the barrier of step kt waited for it. The
+    // loads of step kt+3 overwrite the stage of step kt-1, which every wave
+    // finished reading before the barrier of step kt-1.
+    auto region = [&]<int S>(int kt) {
+        constexpr int S1 = (S + 1) % 4, S3 = (S + 3) % 4;
+        const Rsrc r = descriptors(kt + 3);
+#pragma unroll
+        for (int u = 0; u < T::NMMA; ++u) {
+            mma_one(y, u);
+            if (u < T::LPT) load_one.template operator()<S3>(u, r, kt + 3);
+            if (u < T::NSLOT) read_slot.template operator()<S1>(0, u, x);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int u = 0; u < T::NMMA; ++u) {
+            mma_one(x, u);
+            if (u < T::NSLOT) read_slot.template operator()<S1>(1, u, y);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // step kt+2 has landed (kt+3 may still be in flight)
         sync.template operator()<T::LPT>();
-        issue.template operator()<(S + 3) % 4>(kt + 3);
-        read_frag.template operator()<(S + 1) % 4>(0, x);
-        mma(y);
     };
 
-    for (int kt = 0; kt < nk4; kt += 4) {
-        step.template operator()<0>(kt);
-        step.template operator()<1>(kt + 1);
-        step.template operator()<2>(kt + 2);
-        step.template operator()<3>(kt + 3);
+    if (nk4 > 0) {
+        // prologue: steps 0..2 in flight; wait for step 0, read both of its
+        // halves and run its first half
+        {
+            const Rsrc r0 = descriptors(0), r1 = descriptors(1), r2 = descriptors(2);
+#pragma unroll
+            for (int i = 0; i < T::LPT; ++i) load_one.template operator()<0>(i, r0, 0);
+#pragma unroll
+            for (int i = 0; i < T::LPT; ++i) load_one.template operator()<1>(i, r1, 1);
+#pragma unroll
+            for (int i = 0; i < T::LPT; ++i) load_one.template operator()<2>(i, r2, 2);
+        }
+        sync.template operator()<2 * T::LPT>();
+#pragma unroll
+        for (int s = 0; s < T::NSLOT; ++s) read_slot.template operator()<0>(0, s, x);
+#pragma unroll
+        for (int u = 0; u < T::NMMA; ++u) {
+            mma_one(x, u);
+            if (u < T::NSLOT) read_slot.template operator()<0>(1, u, y);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // step 1 has landed
+        sync.template operator()<T::LPT>();
     }
-    // the zero-filling loads past the end must land before the workgroup's
-    // LDS is released
-    wait_vmcnt<0>();
 
-    // ---- epilogue: ReLU, fp16 (nearest even), 8-byte stores ----
+    // Each pass of this loop runs four regions; the last region of the last
+    // pass multiplies the first half of step nk4, a zero tile.
+    for (int kt = 0; kt < nk4; kt += 4) {
+        region.template operator()<0>(kt);
+        region.template operator()<1>(kt + 1);
+        region.template operator()<2>(kt + 2);
+        region.template operator()<3>(kt + 3);
+    }
+    // the zero-filling loads past the end must land before the ring is reused
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+
+    // ---- epilogue: ReLU, fp16 (nearest even) into LDS, then row stores ----
     // Lane holds, for result rows d = 8q + 4*(lane/32) + r (r = 0..3), the
     // column 16*(j%4) + 64*(q/2) + 8*(q%2) + 4*(lane/32) + r of unit j/4.
+    auto c_stage = [&](int s) -> char* {
+        return reinterpret_cast<char*>(s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3);
+    };
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
-        const int m = m0 + wm * T::TM + 32 * i + lane % 32;
-        if (m >= M) continue;
-        uint16_t* crow = p.C + (int64_t)m * N;
+        const int rl = wm * T::TM + 32 * i + lane % 32;  // row in the tile
+        // the 32 rows of block i lie in one stage array
+        char* cs = c_stage(__builtin_amdgcn_readfirstlane((wm * T::TM + 32 * i) / T::C_ROWS_PER_STAGE));
+        char* crow = cs + (rl % T::C_ROWS_PER_STAGE) * (T::BN * 2);
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * T::TN + 128 * (j / 4) + 16 * (j % 4) + 64 * (q / 2) + 8 * (q % 2) +
-                              4 * (lane / 32);
-                if (n < N) {
-                    u32x2 w;
-                    w[0] = relu_pack2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-                    w[1] = relu_pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                    *reinterpret_cast<u32x2*>(crow + n) = w;
-                }
+                const int cl = wn * T::TN + 128 * (j / 4) + 16 * (j % 4) + 64 * (q / 2) + 8 * (q % 2) +
+                               4 * (lane / 32);
+                u32x2 w;
+                w[0] = relu_pack2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+                w[1] = relu_pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                *reinterpret_cast<u32x2*>(crow + (((cl / 8) ^ c_swz(rl)) * 16) + (cl % 8) * 2) = w;
             }
         }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    constexpr int kRowsPerPass = T::NT / 32;  // 32 lanes x 16 B per row
+#pragma unroll
+    for (int it = 0; it < T::BM / kRowsPerPass; ++it) {
+        const int rl = it * kRowsPerPass + (int)threadIdx.x / 32;
+        const int c = threadIdx.x % 32;
+        const char* cs = c_stage((it * kRowsPerPass) / T::C_ROWS_PER_STAGE);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(cs + (rl % T::C_ROWS_PER_STAGE) * (T::BN * 2) +
+                                                        ((c ^ c_swz(rl)) * 16));
+        const int m = m0 + rl, n = n0 + c * 8;
+        if (m < M && n < N) *reinterpret_cast<u32x4*>(p.C + (int64_t)m * N + n) = v;
     }
 }
 
