@@ -17,10 +17,13 @@
 //    slots apart and never drains the whole ring.
 //  * One barrier per step. Between two barriers a wave runs 32 matrix
 //    operations: the second half of one step and the first half of the next.
-//    The loads of a later step and the fragment reads of the next two halves
-//    are issued one or two at a time between the first matrix operations, in
-//    an order fixed in the source, so the matrix cores are never left waiting
-//    behind a cluster of memory instructions.
+//    The first two of them do not depend on the barrier and are issued before
+//    it, so the matrix cores have work while the waves meet. The loads of a
+//    later step are spread evenly over the region and the fragment reads of
+//    the next two halves are issued one slot at a time between the matrix
+//    operations, in an order fixed in the source: a burst of loads would
+//    hold the matrix operations queued behind it until the address unit had
+//    taken them all.
 //  * Tile products on v_mfma_f32_32x32x16_f16 (one 64-lane wave per TM x TN
 //    sub-tile). The B fragment is the first operand, so each lane of the
 //    32x32 result holds runs of four consecutive columns of one row of C.
@@ -68,7 +71,7 @@ struct Cfg {
     static_assert(A_LOADS % NW == 0 && B_LOADS % NW == 0, "loads must split evenly over waves");
     static_assert(TM % 32 == 0 && TN % 128 == 0, "wave sub-tile: 32-row blocks, 128-column units");
     static_assert(2 * LPT < 64, "vmcnt range");
-    static_assert(LPT <= NMMA && NSLOT <= NMMA, "every load and read slot needs a matrix op to hide behind");
+    static_assert(NSLOT + 3 <= NMMA, "the reads of x must be issued before block x starts");
     static_assert(STAGES * STAGE_BYTES == BM * BN * 2, "the C tile must fill the LDS ring exactly");
     static_assert(BN == 256, "the epilogue maps 32 lanes x 16 B onto one row of C");
 };
@@ -89,6 +92,48 @@ __device__ __forceinline__ int b_swz(int kr) { return 2 * (kr & 3); }
 // c at physical chunk c ^ (r % 32), so the 32 rows that one store of the
 // accumulator layout touches land on 32 different chunks.
 __device__ __forceinline__ int c_swz(int r) { return r & 31; }
+
+// Which memory item follows the matrix op at each position of a region of
+// 2 * NMMA ops (positions 0..NMMA-1 use fragments y, the rest x). After
+// position kPre (the barrier and the descriptors), the read slots of x
+// alternate two-to-one with loads until block x begins, then the read slots
+// of y do the same; leftover loads fill the next free positions. Every
+// position holds at most one item.
+template <int NMMA, int NSLOT, int LPT>
+struct RegionPlan {
+    static constexpr int kNone = 0, kReadX = 1, kReadY = 2, kLoad = 3;
+    int kind[2 * NMMA];
+    int index[2 * NMMA];
+    constexpr explicit RegionPlan(int pre) : kind{}, index{}
+    {
+        int xi = 0, yi = 0, li = 0;
+        for (int q = pre + 1, run = 0; q < 2 * NMMA; ++q) {
+            const bool block_x = q >= NMMA;
+            int& ri = block_x ? yi : xi;
+            if (!block_x && q == NMMA - 1 && xi < NSLOT) run = 0;  // never leave x reads behind
+            if (ri < NSLOT && (run < 2 || li >= LPT)) {
+                kind[q] = block_x ? kReadY : kReadX;
+                index[q] = ri++;
+                ++run;
+            } else if (li < LPT) {
+                kind[q] = kLoad;
+                index[q] = li++;
+                run = 0;
+            }
+        }
+    }
+    constexpr bool complete(int pre) const
+    {
+        int nx = 0, ny = 0, nl = 0, last_x = -1;
+        for (int q = 0; q < 2 * NMMA; ++q) {
+            if (q <= pre && kind[q] != kNone) return false;
+            if (kind[q] == kReadX) { ++nx; last_x = q; }
+            if (kind[q] == kReadY) ++ny;
+            if (kind[q] == kLoad) ++nl;
+        }
+        return nx == NSLOT && ny == NSLOT && nl == LPT && last_x < NMMA;
+    }
+};
 
 template <class T, bool KALIGNED>
 __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
@@ -249,33 +294,43 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     const int nk4 = (nk + 3) & ~3;
     Frag x, y;
 
-    // The code between the barriers of steps kt and kt+1 (S = kt % 4):
-    //  block A: the 16 matrix ops of step kt, second half (fragments y), with
-    //           the loads of step kt+3 and the reads of step kt+1's first half
-    //           (into x) issued one by one between them;
-    //  block B: the 16 matrix ops of step kt+1, first half (fragments x), with
-    //           the reads of step kt+1's second half (into y) between them.
-    // Step kt+1's data is in LDS: the barrier of step kt waited for it. The
-    // loads of step kt+3 overwrite the stage of step kt-1, which every wave
-    // finished reading before the barrier of step kt-1.
+    // The code of region kt (S = kt % 4): 2 * NMMA matrix ops, those of step
+    // kt, second half (fragments y), then those of step kt+1, first half
+    // (fragments x). Position q of the region is one matrix op followed by at
+    // most one memory item (see RegionPlan):
+    //  * before position kPre: the barrier. This wave's loads of step kt+1
+    //    have landed and its fragment reads are done, and after it every
+    //    wave's have. The first kPre ops of y do not depend on it and are
+    //    issued first, so the matrix cores have work while the waves meet.
+    //  * at position kPre: the descriptors of step kt+3;
+    //  * then, one item per position: the read slots of step kt+1's first
+    //    half (into x, needed by block x), the loads of step kt+3, and from the
+    //    start of block x the read slots of step kt+1's second half (into y).
+    // A wave issues instructions in order, so whatever sits between two
+    // matrix ops must issue within one op's 32 cycles or the matrix core
+    // idles: a one-kilobyte direct-to-LDS load and a fragment read never
+    // share a gap.
+    // The loads of step kt+3 overwrite the stage of step kt-1, which every
+    // wave finished reading before this barrier.
+    constexpr int kPre = 2;
+    constexpr RegionPlan<T::NMMA, T::NSLOT, T::LPT> plan(kPre);
+    static_assert(plan.complete(kPre), "every read slot and load must be placed, the x reads before block x");
     auto region = [&]<int S>(int kt) {
         constexpr int S1 = (S + 1) % 4, S3 = (S + 3) % 4;
-        const Rsrc r = descriptors(kt + 3);
+        Rsrc r;
 #pragma unroll
-        for (int u = 0; u < T::NMMA; ++u) {
-            mma_one(y, u);
-            if (u < T::LPT) load_one.template operator()<S3>(u, r, kt + 3);
-            if (u < T::NSLOT) read_slot.template operator()<S1>(0, u, x);
+        for (int q = 0; q < 2 * T::NMMA; ++q) {
+            // step kt+1 has landed (kt+2 may still be in flight)
+            if (q == kPre) sync.template operator()<T::LPT>();
+            if (q < T::NMMA) mma_one(y, q);
+            else mma_one(x, q - T::NMMA);
+            if (q == kPre) r = descriptors(kt + 3);
+            const int k = plan.kind[q], n = plan.index[q];
+            if (k == RegionPlan<T::NMMA, T::NSLOT, T::LPT>::kLoad) load_one.template operator()<S3>(n, r, kt + 3);
+            if (k == RegionPlan<T::NMMA, T::NSLOT, T::LPT>::kReadX) read_slot.template operator()<S1>(0, n, x);
+            if (k == RegionPlan<T::NMMA, T::NSLOT, T::LPT>::kReadY) read_slot.template operator()<S1>(1, n, y);
             __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int u = 0; u < T::NMMA; ++u) {
-            mma_one(x, u);
-            if (u < T::NSLOT) read_slot.template operator()<S1>(1, u, y);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // step kt+2 has landed (kt+3 may still be in flight)
-        sync.template operator()<T::LPT>();
     };
 
     if (nk4 > 0) {
@@ -299,8 +354,6 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
             if (u < T::NSLOT) read_slot.template operator()<0>(1, u, y);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // step 1 has landed
-        sync.template operator()<T::LPT>();
     }
 
     // Each pass of this loop runs four regions; the last region of the last
@@ -311,9 +364,9 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         region.template operator()<2>(kt + 2);
         region.template operator()<3>(kt + 3);
     }
-    // the zero-filling loads past the end must land before the ring is reused
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
+    // the zero-filling loads past the end must land, and every wave must be
+    // done with its fragment reads, before the ring is reused
+    sync.template operator()<0>();
 
     // ---- epilogue: ReLU, fp16 (nearest even) into LDS, then row stores ----
     // Lane holds, for result rows d = 8q + 4*(lane/32) + r (r = 0..3), the
