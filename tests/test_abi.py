@@ -65,9 +65,12 @@ def test_strerror_and_tiles():
 
 
 def test_tile_selection_is_host_only():
-    # large square -> the 256x256 tile; few rows -> the skinny tile
+    # large square -> the 256x256 tile; few rows -> a split-K tile sized to M
     assert gr.select_tile(4096, 4096, 4096) == 0
-    assert gr.select_tile(16, 8192, 8192) == 3
+    assert "splitk_16x" in gr.tile_name(gr.select_tile(16, 8192, 8192))
+    assert "splitk_32x" in gr.tile_name(gr.select_tile(17, 8192, 8192))
+    assert "splitk_64x" in gr.tile_name(gr.select_tile(64, 4096, 4096))
+    assert "splitk" not in gr.tile_name(gr.select_tile(65, 4096, 4096))
     # K or N not a multiple of 8 -> the generic element-wise path
     assert gr.select_tile(64, 64, 7) == -1
     assert gr.select_tile(64, 9, 64) == -1

@@ -123,7 +123,7 @@ def test_edge_shapes_every_tile(M, N, K):
         assert np.array_equal(got, want), f"tile {tile}: {np.sum(got != want)} mismatches"
 
 
-@pytest.mark.parametrize("tile", range(4))
+@pytest.mark.parametrize("tile", range(7))
 @pytest.mark.parametrize("w", [workloads.SQUARE_1024, workloads.RAGGED], ids=lambda w: w.name)
 def test_each_tile_on_workloads(w, tile):
     say(f"[tile] {w.name} tile={tile} {gr.tile_name(tile)}")
@@ -131,6 +131,64 @@ def test_each_tile_on_workloads(w, tile):
     A, B = workloads.as_u16(a), workloads.as_u16(b)
     want, absdot = oracle.gemm_relu_f16(A, B, want_absdot=True)
     parity.check(run(a, b, tile=tile), want, absdot=absdot, K=w.K, label=f"tile {tile}")
+
+
+# ---------------------------------------------------------------------------
+# split-K: partial sums across workgroups, combined by the last one
+# ---------------------------------------------------------------------------
+
+SPLITK_SHAPES = [(16, 8192, 8192), (1, 4096, 8192), (5, 1032, 1000), (16, 136, 129 * 8),
+                 (17, 520, 4096), (32, 128, 64), (40, 2056, 3000), (64, 4096, 4096), (9, 8, 8)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLITK_SHAPES)
+def test_splitk_bit_exact_and_repeatable(M, N, K):
+    tile = gr.select_tile(M, N, K)
+    say(f"[splitk] M={M} N={N} K={K} tile={gr.tile_name(tile)}")
+    assert "splitk" in gr.tile_name(tile)
+    a, b = workloads.make_inputs(M, N, K, dist="intsmall", seed=3 * M + N + K)
+    want = oracle.gemm_relu_f16(workloads.as_u16(a), workloads.as_u16(b))
+    ad, bd = a.cuda(), b.cuda()
+    out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    # several launches in a row on one workspace: the tile counters reset themselves
+    for rep in range(3):
+        out.fill_(7.0)
+        gr.gemm_relu(ad, bd, out=out)
+        torch.cuda.synchronize()
+        got = workloads.as_u16(out.cpu())
+        assert np.array_equal(got, want), f"launch {rep}: {np.sum(got != want)} mismatches"
+
+
+@pytest.mark.parametrize("tile", [4, 5, 6])
+def test_splitk_tiles_on_larger_m(tile):
+    # a pinned split-K tile on more rows than it holds: several row tiles
+    M, N, K = 100, 264, 1032
+    say(f"[splitk rows] tile={gr.tile_name(tile)} M={M} N={N} K={K}")
+    a, b = workloads.make_inputs(M, N, K, dist="normal", seed=11)
+    A, B = workloads.as_u16(a), workloads.as_u16(b)
+    want, absdot = oracle.gemm_relu_f16(A, B, want_absdot=True)
+    parity.check(run(a, b, tile=tile), want, absdot=absdot, K=K, label=f"tile {tile}")
+
+
+def test_splitk_two_streams_and_shapes_interleaved():
+    # different streams own different workspaces; shapes that need more
+    # counters or partials than an earlier call grow the workspace
+    shapes = [(16, 1024, 2048), (16, 8192, 8192), (3, 256, 512)]
+    inputs = []
+    for i, (M, N, K) in enumerate(shapes):
+        a, b = workloads.make_inputs(M, N, K, dist="intsmall", seed=100 + i)
+        inputs.append((a.cuda(), b.cuda(), oracle.gemm_relu_f16(workloads.as_u16(a), workloads.as_u16(b))))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for rep in range(2):
+        for i, (ad, bd, want) in enumerate(inputs):
+            s = streams[(i + rep) % 2]
+            with torch.cuda.stream(s):
+                outs.append((gr.gemm_relu(ad, bd), want))
+    torch.cuda.synchronize()
+    for c, want in outs:
+        assert np.array_equal(workloads.as_u16(c.cpu()), want)
 
 
 # ---------------------------------------------------------------------------

@@ -37,6 +37,11 @@ struct Args {
     int tiles_m, tiles_n;
     int group_m;
     int order;  // GEMM_RELU_ORDER_*
+    // split-K kernel only
+    float* partial;      // [splits][M][N] fp32 partial sums (splits > 1)
+    uint32_t* counters;  // one per column tile, zero between launches (splits > 1)
+    int splits;          // workgroups along K
+    int kc;              // K range of one workgroup
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes)
@@ -88,6 +93,21 @@ __device__ __forceinline__ void tile_coords(const Args& a, int& tm, int& tn)
     const int in_g = bid - g * gsize;
     tm = first_m + in_g % gm;
     tn = in_g / gm;
+}
+
+// Transpose an 8x8 block of halves held as 8 rows of 16 bytes: out[c] holds
+// column c (8 values, one per input row).
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8])
+{
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // low half from row 2j, high half from row 2j+1, both at column c
+            out[c][j] = __builtin_amdgcn_perm(in[2 * j + 1][c >> 1], in[2 * j][c >> 1], sel);
+        }
+    }
 }
 
 // ReLU on an fp32 accumulator and the conversion to fp16, round to nearest

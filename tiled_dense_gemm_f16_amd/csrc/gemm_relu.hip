@@ -2,23 +2,28 @@
 // host side of the C ABI declared in include/gemm_relu.h.
 //
 // The computation is the GEMM + ReLU example of "Writing high-performance
-// kernels in TileLang" (section "Escribamos un GEMM"). Two kernel families
+// kernels in TileLang" (section "Escribamos un GEMM"). Three kernel families
 // implement it:
 //  * pipelined.hpp -- the large-tile hot path: direct-to-LDS loads, a
 //    four-stage LDS ring, v_mfma_f32_32x32x16_f16, transposing LDS reads;
 //  * staged.hpp    -- register-staged loads with v_mfma_f32_16x16x32_f16, for
-//    small tiles and for the generic element-wise path (any K, N, alignment).
-// This file holds the tile table, the shape heuristic, argument validation
-// and the launches.
+//    small tiles and for the generic element-wise path (any K, N, alignment);
+//  * splitk.hpp    -- few rows: B streamed through registers, K split across
+//    waves and workgroups, fp32 partials combined by the last workgroup.
+// This file holds the tile table, the shape heuristic, argument validation,
+// the split-K workspaces and the launches.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
 #include <string.h>
 
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "gemm_relu.h"
 #include "pipelined.hpp"
+#include "splitk.hpp"
 #include "staged.hpp"
 
 namespace {
@@ -34,6 +39,18 @@ using S256 = gemm_relu::staged::Tile<256, 256, 64, 2, 2>;  // generic instance o
 using S128 = gemm_relu::staged::Tile<128, 128, 64, 2, 2>;  // the pages' 128x128x64 tile
 using S64 = gemm_relu::staged::Tile<64, 64, 64, 2, 2>;     // 4 waves x 32x32
 using S16 = gemm_relu::staged::Tile<16, 64, 64, 1, 4>;     // 4 waves x 16x16: few rows
+#ifndef GR_SPLITK_NW
+#define GR_SPLITK_NW 4
+#endif
+#ifndef GR_SPLITK_D
+#define GR_SPLITK_D 4
+#endif
+#ifndef GR_SPLITK_TARGET
+#define GR_SPLITK_TARGET 256
+#endif
+using K16 = gemm_relu::splitk::Cfg<1, GR_SPLITK_NW, GR_SPLITK_D>;  // split-K, 16 rows x 128 columns
+using K32 = gemm_relu::splitk::Cfg<2, GR_SPLITK_NW, GR_SPLITK_D>;  // split-K, 32 rows x 128 columns
+using K64 = gemm_relu::splitk::Cfg<4, GR_SPLITK_NW, GR_SPLITK_D>;  // split-K, 64 rows x 128 columns
 
 using LaunchFn = hipError_t (*)(const Args&, hipStream_t);
 
@@ -56,22 +73,55 @@ hipError_t launch_pipelined(const Args& a, hipStream_t s)
     return hipGetLastError();
 }
 
+template <class T>
+hipError_t launch_splitk(const Args& a, hipStream_t s)
+{
+    const int blocks = a.tiles_m * a.tiles_n * a.splits;
+    hipLaunchKernelGGL((gemm_relu::splitk::splitk_kernel<T>), dim3(blocks), dim3(T::NT), 0, s, a);
+    return hipGetLastError();
+}
+
 struct TileEntry {
     const char* name;
     int bm, bn;
     int default_group_m;
-    LaunchFn vec;
-    LaunchFn generic;
+    bool splitk;      // K split across workgroups (needs the workspace)
+    LaunchFn vec;     // K % 8 == 0, N % 8 == 0, 16-byte aligned pointers
+    LaunchFn generic; // anything else
 };
 
 const TileEntry kTiles[] = {
-    {"256x256x32s4_w2x2_mfma32x32x16_lds-dma", 256, 256, 4, launch_pipelined<P256>, launch_staged<S256, false>},
-    {"128x128x64_w2x2_mfma16x16x32", 128, 128, 4, launch_staged<S128, true>, launch_staged<S128, false>},
-    {"64x64x64_w2x2_mfma16x16x32", 64, 64, 4, launch_staged<S64, true>, launch_staged<S64, false>},
-    {"16x64x64_w1x4_mfma16x16x32", 16, 64, 1, launch_staged<S16, true>, launch_staged<S16, false>},
+    {"256x256x32s4_w2x2_mfma32x32x16_lds-dma", 256, 256, 4, false, launch_pipelined<P256>,
+     launch_staged<S256, false>},
+    {"128x128x64_w2x2_mfma16x16x32", 128, 128, 4, false, launch_staged<S128, true>, launch_staged<S128, false>},
+    {"64x64x64_w2x2_mfma16x16x32", 64, 64, 4, false, launch_staged<S64, true>, launch_staged<S64, false>},
+    {"16x64x64_w1x4_mfma16x16x32", 16, 64, 1, false, launch_staged<S16, true>, launch_staged<S16, false>},
+    {"splitk_16x128_w4k_mfma16x16x32_regT", 16, 128, 1, true, launch_splitk<K16>, launch_staged<S16, false>},
+    {"splitk_32x128_w4k_mfma16x16x32_regT", 32, 128, 1, true, launch_splitk<K32>, launch_staged<S64, false>},
+    {"splitk_64x128_w4k_mfma16x16x32_regT", 64, 128, 1, true, launch_splitk<K64>, launch_staged<S64, false>},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kGenericTile = 2;  // tile used by the element-wise path
+constexpr int kSplitK16 = 4, kSplitK32 = 5, kSplitK64 = 6;
+constexpr int kSplitKTN = 128;   // columns of a split-K workgroup
+constexpr int kSplitKStep = GR_SPLITK_NW * 32;  // K granularity of a split-K workgroup (waves x 32)
+constexpr int kTargetBlocks = GR_SPLITK_TARGET;  // workgroups to aim for
+
+// How many workgroups share the K range of one split-K tile, and the K range
+// of each (a multiple of kSplitKStep).
+void choose_splits(int64_t K, int64_t tiles, int& splits, int& kc)
+{
+    int64_t s = tiles >= kTargetBlocks ? 1 : (kTargetBlocks + tiles - 1) / tiles;
+    const int64_t max_s = (K + kSplitKStep - 1) / kSplitKStep;  // at least one step per workgroup
+    if (s > max_s) s = max_s;
+    if (s < 1) s = 1;
+    int64_t c = (K + s - 1) / s;
+    c = (c + kSplitKStep - 1) / kSplitKStep * kSplitKStep;
+    if (c < kSplitKStep) c = kSplitKStep;
+    kc = (int)c;
+    splits = (int)((K + c - 1) / c);
+    if (splits < 1) splits = 1;
+}
 
 bool fast_path_ok(int64_t N, int64_t K, const void* A, const void* B, const void* C)
 {
@@ -80,15 +130,69 @@ bool fast_path_ok(int64_t N, int64_t K, const void* A, const void* B, const void
     return (K % 8 == 0) && (N % 8 == 0) && mis == 0 && K <= (1 << 22) && N <= (1 << 24);
 }
 
-int choose_tile(int64_t M, int64_t N)
+// The split-K kernel addresses A with 32-bit offsets.
+bool splitk_ok(int64_t M, int64_t K) { return M * K * 2 < ((int64_t)1 << 31); }
+
+int choose_tile(int64_t M, int64_t N, int64_t K)
 {
     auto blocks = [&](int t) {
         return ((M + kTiles[t].bm - 1) / kTiles[t].bm) * ((N + kTiles[t].bn - 1) / kTiles[t].bn);
     };
+    // few rows: stream B once, K split to fill the chip
+    if (M <= 64 && splitk_ok(M, K)) return M <= 16 ? kSplitK16 : M <= 32 ? kSplitK32 : kSplitK64;
     if (M <= 16) return 3;
     if (blocks(0) >= 256) return 0;
     if (blocks(1) >= 128) return 1;
     return 2;
+}
+
+// ---------------------------------------------------------------------------
+// Split-K workspaces: one per (device, stream), grown on demand. The first
+// `counter_slots` 32-bit words are tile counters, zero between launches (each
+// launch's last workgroup resets the counters it used); the fp32 partial sums
+// follow at a 256-byte boundary.
+// ---------------------------------------------------------------------------
+
+struct Workspace {
+    char* base = nullptr;
+    size_t counter_slots = 0;
+    size_t partial_bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+size_t counter_bytes(size_t slots) { return (slots * 4 + 255) / 256 * 256; }
+
+int get_workspace(int dev, hipStream_t stream, size_t slots, size_t partial_bytes, uint32_t** counters,
+                  float** partial)
+{
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    Workspace& w = g_ws[std::make_pair(dev, stream)];
+    if (w.base == nullptr || w.counter_slots < slots || w.partial_bytes < partial_bytes) {
+        const size_t ns = slots > w.counter_slots ? slots : w.counter_slots;
+        const size_t np = partial_bytes > w.partial_bytes ? partial_bytes : w.partial_bytes;
+        if (w.base != nullptr) {
+            // earlier launches on this stream may still use the old buffer
+            if (hipStreamSynchronize(stream) != hipSuccess) return GEMM_RELU_EHIP;
+            (void)hipFree(w.base);
+            w = Workspace{};
+        }
+        char* p = nullptr;
+        if (hipMalloc(reinterpret_cast<void**>(&p), counter_bytes(ns) + np) != hipSuccess) {
+            (void)hipGetLastError();
+            return GEMM_RELU_ENOMEM;
+        }
+        if (hipMemsetAsync(p, 0, counter_bytes(ns), stream) != hipSuccess) {
+            (void)hipFree(p);
+            return GEMM_RELU_EHIP;
+        }
+        w.base = p;
+        w.counter_slots = ns;
+        w.partial_bytes = np;
+    }
+    *counters = reinterpret_cast<uint32_t*>(w.base);
+    *partial = reinterpret_cast<float*>(w.base + counter_bytes(w.counter_slots));
+    return GEMM_RELU_OK;
 }
 
 bool overlaps(const void* p, int64_t pbytes, const void* q, int64_t qbytes)
@@ -126,9 +230,9 @@ constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
 signed char g_dev_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
 
-int check_device()
+int check_device(int& dev)
 {
-    int dev = 0;
+    dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return GEMM_RELU_EHIP;
     if (dev < 0 || dev >= kMaxDevices) return GEMM_RELU_EUNSUPPORTED;
     std::lock_guard<std::mutex> lk(g_dev_mu);
@@ -166,7 +270,7 @@ const char* gemm_relu_tile_name(int tile)
 int gemm_relu_select_tile(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* C)
 {
     if (!fast_path_ok(N, K, A, B, C)) return -1;
-    return choose_tile(M, N);
+    return choose_tile(M, N, K);
 }
 
 int gemm_relu_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C,
@@ -175,12 +279,19 @@ int gemm_relu_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, const void*
     int rc = validate(M, N, K, A, B, C, opts);
     if (rc != GEMM_RELU_OK) return rc;
     if (M == 0 || N == 0) return GEMM_RELU_OK;
-    rc = check_device();
+    int dev = 0;
+    rc = check_device(dev);
     if (rc != GEMM_RELU_OK) return rc;
 
     const bool vec = fast_path_ok(N, K, A, B, C);
-    int tile = (opts && opts->tile != GEMM_RELU_TILE_AUTO) ? opts->tile : (vec ? choose_tile(M, N) : kGenericTile);
-    const TileEntry& te = kTiles[tile];
+    const int tile =
+        (opts && opts->tile != GEMM_RELU_TILE_AUTO) ? opts->tile : (vec ? choose_tile(M, N, K) : kGenericTile);
+    // the split-K tiles have no element-wise instance: unaligned shapes take
+    // the generic tile
+    const TileEntry& te = (!vec && kTiles[tile].splitk) ? kTiles[kGenericTile] : kTiles[tile];
+    const bool splitk = vec && te.splitk;
+    if (splitk && !splitk_ok(M, K)) return GEMM_RELU_EUNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
     Args a;
     a.A = static_cast<const uint16_t*>(A);
     a.B = static_cast<const uint16_t*>(B);
@@ -192,8 +303,22 @@ int gemm_relu_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, const void*
     a.tiles_n = (int)((N + te.bn - 1) / te.bn);
     a.group_m = (opts && opts->group_m > 0) ? opts->group_m : te.default_group_m;
     a.order = opts ? opts->block_order : GEMM_RELU_ORDER_DEFAULT;
-    if ((int64_t)a.tiles_m * a.tiles_n > INT32_MAX) return GEMM_RELU_EUNSUPPORTED;
-    const hipError_t e = (vec ? te.vec : te.generic)(a, static_cast<hipStream_t>(stream));
+    a.partial = nullptr;
+    a.counters = nullptr;
+    a.splits = 1;
+    a.kc = (int)(K < 1 ? 1 : K);
+    const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+    if (tiles > INT32_MAX) return GEMM_RELU_EUNSUPPORTED;
+    if (splitk) {
+        choose_splits(K, tiles, a.splits, a.kc);
+        if (tiles * a.splits > INT32_MAX) return GEMM_RELU_EUNSUPPORTED;
+        if (a.splits > 1) {
+            rc = get_workspace(dev, s, (size_t)tiles, (size_t)a.splits * (size_t)M * (size_t)N * 4, &a.counters,
+                               &a.partial);
+            if (rc != GEMM_RELU_OK) return rc;
+        }
+    }
+    const hipError_t e = (vec ? te.vec : te.generic)(a, s);
     return e == hipSuccess ? GEMM_RELU_OK : GEMM_RELU_EHIP;
 }
 

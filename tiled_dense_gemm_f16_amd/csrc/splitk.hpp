@@ -1,0 +1,282 @@
+// Split-K kernel for few rows (M <= 16 * MB): the skinny, decode-like case.
+//
+// Same computation as the TileLang GEMM + ReLU example ("Writing
+// high-performance kernels in TileLang", section "Escribamos un GEMM"):
+// C = fp16(max(A @ B, 0)) with fp32 accumulation. With M this small the
+// whole cost is streaming B from HBM once; the matrix cores are nearly idle.
+// The design keeps as many bytes of B in flight as the chip allows and
+// touches nothing twice:
+//
+//  * A workgroup owns 16 * MB rows and TN = 128 columns of C and one range of
+//    K; each of its
+//    four waves takes a quarter of that range (the reduction is split three
+//    ways: inside an MFMA, across the waves, across workgroups). Splitting K
+//    across CUs when the other dimensions are too small to fill the chip is
+//    the split-and-combine idea of the pages' decode kernel ("Ahora uno
+//    real: MLA decode"), applied here to the GEMM's reduction.
+//  * B goes straight to registers: each lane loads eight consecutive rows of
+//    eight consecutive columns (8 x 16 bytes; a load instruction covers four
+//    rows x 256 contiguous bytes) and transposes the 8 x 8 block in registers,
+//    which yields k-contiguous operands for v_mfma_f32_16x16x32_f16 without a
+//    trip through LDS. D = 4 steps of 32 rows are in flight per wave.
+//  * The B fragment is the first MFMA operand. Matrix op e of a lane uses the
+//    columns 8 * (lane % 16) + e, so the sixteen results of one op are spread
+//    with stride 8, and after the eight ops each lane holds 32 consecutive
+//    columns of one row of C.
+//  * Rows of B past the wave's range, columns past N and rows of A past M
+//    read as zeros (buffer descriptors and out-of-range offsets); the K tail
+//    of A is masked per lane.
+//  * Reduction: the four waves add their fp32 tiles through LDS in a fixed
+//    order. With one workgroup along K the sum goes straight to the ReLU and
+//    the fp16 store. Otherwise each workgroup writes its fp32 partial tile,
+//    and the last one to finish a column tile (a device-scope counter) adds
+//    the partials in split order, applies the ReLU, stores fp16 C and resets
+//    the counter for the next launch. The result does not depend on which
+//    workgroup finishes last.
+//
+// Larger M is covered by more row tiles of 16 * MB rows (each re-reads B).
+//
+// Requirements (checked on the host): N % 8 == 0, K % 8 == 0, 16-byte
+// aligned pointers, kc (the K range of a workgroup) a multiple of 4 * 32,
+// M * K * 2 and 8 * N * 2 below 2^31.
+#pragma once
+
+#include "common.hpp"
+
+namespace gemm_relu {
+namespace splitk {
+
+template <int MB_, int NW_ = 4, int D_ = 4>
+struct Cfg {
+    static constexpr int MB = MB_;          // 16-row blocks
+    static constexpr int BM = 16 * MB;
+    static constexpr int TN = 128;          // columns of a workgroup (all its waves)
+    static constexpr int NW = NW_, NT = kWave * NW;
+    static constexpr int BK = 32;           // rows of B per step
+    static constexpr int D = D_;            // steps in flight per wave
+    static constexpr int RED_ROW = TN + 4;  // fp32 per row of the reduction buffer (padded)
+    static constexpr int ROWS_PER_PASS = NT / 16;  // combine: 16 threads x 8 columns per row
+    static_assert(BM % ROWS_PER_PASS == 0 || ROWS_PER_PASS % BM == 0, "combine rows");
+};
+
+template <class T>
+__global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
+{
+    __shared__ __attribute__((aligned(16))) float red[T::NW][T::BM][T::RED_ROW];
+    __shared__ uint32_t last_flag;
+
+    const int M = p.M, N = p.N, K = p.K;
+    // workgroup -> (row tile, column tile, split); the splits of one tile are
+    // tiles_m * tiles_n workgroups apart
+    const int ntiles = p.tiles_m * p.tiles_n;
+    const int tile = blockIdx.x % ntiles, ks = blockIdx.x / ntiles;
+    const int tm = tile / p.tiles_n, tn = tile % p.tiles_n;
+    const int m0 = tm * T::BM, n0 = tn * T::TN;
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int kw = p.kc / T::NW;
+    const int kbeg = min(K, ks * p.kc + wave * kw);
+    const int kend = min(K, kbeg + kw);
+    const int nsteps = (kend - kbeg + T::BK - 1) / T::BK;
+
+    const int g = lane / 16, i16 = lane % 16;
+    // B: lane reads rows 8g + r (r = 0..7) of a step, columns ncol .. ncol+7
+    const int ncol = n0 + 8 * i16;
+    uint32_t boff[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) boff[r] = (ncol < N) ? (uint32_t)((8 * g + r) * N + ncol) * 2u : kOOB;
+    // A: lane reads row m0 + mb*16 + i16, k-chunk 8g of a step
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, (uint64_t)M * K * 2);
+    uint32_t arow[T::MB];
+#pragma unroll
+    for (int mb = 0; mb < T::MB; ++mb) {
+        const int m = m0 + mb * 16 + i16;
+        arow[mb] = (m < M) ? (uint32_t)m * (uint32_t)K * 2u : kOOB;
+    }
+
+    u32x4 bst[T::D][8];
+    u32x4 ast[T::D][T::MB];
+    // Loads of step s (rows kbeg + 32 s ...) into register slot d. Steps at
+    // or past the end of the range get an empty descriptor (zeros).
+    auto issue = [&](int d, int s) {
+        const int k0 = kbeg + s * T::BK;
+        const int64_t rows = (int64_t)kend - k0;
+        const int64_t brem = (rows > 0 ? rows : 0) * N * 2;
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)min(k0, K) * N, (uint64_t)brem);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) bst[d][r] = load16(rb, boff[r]);
+        const int ka = k0 + 8 * g;
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+            const uint32_t off = (ka < kend && arow[mb] != kOOB) ? arow[mb] + (uint32_t)ka * 2u : kOOB;
+            ast[d][mb] = load16(ra, off);
+        }
+    };
+
+    f32x4 acc[T::MB][8];
+#pragma unroll
+    for (int mb = 0; mb < T::MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[mb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int d) {
+        u32x4 cols[8];
+        transpose8x8(bst[d], cols);
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+            const f16x8 a = __builtin_bit_cast(f16x8, ast[d][mb]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc[mb][e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, cols[e]), a,
+                                                                   acc[mb][e], 0, 0, 0);
+        }
+    };
+
+    // Register ring of D steps: step s lives in slot s % D. The order of the
+    // loads is pinned (scheduling barriers), so that when slot d is consumed
+    // its loads are the oldest outstanding ones and the wait before it leaves
+    // the other D - 1 steps in flight.
+#pragma unroll
+    for (int d = 0; d < T::D; ++d) {
+        issue(d, d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int s0 = 0; s0 < nsteps; s0 += T::D) {
+#pragma unroll
+        for (int d = 0; d < T::D; ++d) {
+            compute(d);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(d, s0 + d + T::D);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // ---- reduction across the four waves (fixed order) ----
+    // Lane holds acc[mb][e][r] = C[mb*16 + i16][n0 + 32g + 8r + e].
+#pragma unroll
+    for (int mb = 0; mb < T::MB; ++mb) {
+        float* row = &red[wave][mb * 16 + i16][32 * g];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            *reinterpret_cast<f32x4*>(row + 8 * r) = f32x4{acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};
+            *reinterpret_cast<f32x4*>(row + 8 * r + 4) =
+                f32x4{acc[mb][4][r], acc[mb][5][r], acc[mb][6][r], acc[mb][7][r]};
+        }
+    }
+    __syncthreads();
+    // Combine: thread t adds the waves' values for rows m0 + t/16 + j*RP
+    // (j = 0, 1, ...), columns n0 + 8*(t%16) .. +7 of the tile.
+    constexpr int RP = T::ROWS_PER_PASS;
+    constexpr int NJ = (T::BM + RP - 1) / RP;
+    const int t = threadIdx.x;
+    const int cm = t / 16, cn = 8 * (t % 16);
+    const int n = n0 + cn;
+    float v[NJ][8];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+        const int rl = cm + j * RP;  // row in the tile
+        if (rl < T::BM) {
+#pragma unroll
+            for (int w = 0; w < T::NW; ++w) {
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(&red[w][rl][cn]);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(&red[w][rl][cn + 4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[j][e] += lo[e];
+                    v[j][e + 4] += hi[e];
+                }
+            }
+        }
+    }
+
+    auto store_c = [&](const float (&vals)[NJ][8]) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int rl = cm + j * RP, m = m0 + rl;
+            if (rl < T::BM && m < M && n < N) {
+                u32x4 h;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) h[q] = relu_pack2(vals[j][2 * q], vals[j][2 * q + 1]);
+                *reinterpret_cast<u32x4*>(p.C + (int64_t)m * N + n) = h;
+            }
+        }
+    };
+
+    if (p.splits == 1) {
+        store_c(v);
+        return;
+    }
+
+    // ---- split across workgroups: partials, then the last workgroup combines ----
+    // The eight XCDs each have their own L2, and a device-wide fence would
+    // write back or invalidate a whole L2 per workgroup. Instead every access
+    // to the shared data (partials, counter) is a device-scope atomic, which
+    // the hardware performs at the level the XCDs share: the partials are
+    // stored that way, this wave waits until its stores are acknowledged
+    // (vmcnt(0)), the workgroup meets, and only then one lane counts the
+    // workgroup in. The last workgroup reads the partials with device-scope
+    // atomic loads, all issued after it saw the final count.
+    // partials travel as 8-byte device-scope atomics (pairs of fp32)
+    auto pack = [](float lo, float hi) -> uint64_t {
+        return (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+    };
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int rl = cm + j * RP, m = m0 + rl;
+        if (rl < T::BM && m < M && n < N) {
+            uint64_t* dst = reinterpret_cast<uint64_t*>(p.partial + ((int64_t)ks * M + m) * N + n);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                __hip_atomic_store(dst + e, pack(v[j][2 * e], v[j][2 * e + 1]), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    wait_vmcnt<0>();  // this wave's partial stores are done
+    __syncthreads();
+    if (t == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = (prev == (uint32_t)(p.splits - 1)) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    // Up to kBatch splits' partials are loaded before any is added, so their
+    // latencies overlap; the additions keep split order.
+    constexpr int kBatch = 8;
+    float sum[NJ][8];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum[j][e] = 0.f;
+    for (int q0 = 0; q0 < p.splits; q0 += kBatch) {
+        uint64_t buf[kBatch][NJ][4];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int rl = cm + j * RP, m = m0 + rl;
+                const bool ok = q0 + b < p.splits && rl < T::BM && m < M && n < N;
+                uint64_t* src = reinterpret_cast<uint64_t*>(p.partial + ((int64_t)(q0 + b) * M + m) * N + n);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    buf[b][j][e] = ok ? __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sum[j][2 * e] += __builtin_bit_cast(float, (uint32_t)buf[b][j][e]);
+                    sum[j][2 * e + 1] += __builtin_bit_cast(float, (uint32_t)(buf[b][j][e] >> 32));
+                }
+        }
+    }
+    store_c(sum);
+    if (t == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace splitk
+}  // namespace gemm_relu

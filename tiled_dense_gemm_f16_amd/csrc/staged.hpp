@@ -26,21 +26,6 @@ namespace staged {
 // on 8 different physical chunks (all 32 four-byte banks of a 128-byte span).
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
-// Transpose an 8x8 block of halves held as 8 rows of 16 bytes: out[c] holds
-// column c (8 values, one per input row).
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8])
-{
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // low half from row 2j, high half from row 2j+1, both at column c
-            out[c][j] = __builtin_amdgcn_perm(in[2 * j + 1][c >> 1], in[2 * j][c >> 1], sel);
-        }
-    }
-}
-
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MIN_WAVES_ = 1>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
