@@ -123,7 +123,7 @@ def test_edge_shapes_every_tile(M, N, K):
         assert np.array_equal(got, want), f"tile {tile}: {np.sum(got != want)} mismatches"
 
 
-@pytest.mark.parametrize("tile", range(7))
+@pytest.mark.parametrize("tile", range(gr.tile_count()))
 @pytest.mark.parametrize("w", [workloads.SQUARE_1024, workloads.RAGGED], ids=lambda w: w.name)
 def test_each_tile_on_workloads(w, tile):
     say(f"[tile] {w.name} tile={tile} {gr.tile_name(tile)}")

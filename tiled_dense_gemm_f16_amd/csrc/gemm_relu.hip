@@ -35,6 +35,8 @@ namespace {
 using gemm_relu::Args;
 
 using P256 = gemm_relu::pipelined::Cfg<256, 256, 2, 2>;   // 4 waves x 128x128, 32x32x16 MFMA
+using P256W8 = gemm_relu::pipelined::Cfg<256, 256, 4, 2>; // 8 waves x 64x128: two waves per SIMD
+using P256S5 = gemm_relu::pipelined::Cfg<256, 256, 2, 2, 5>; // five-slot ring: 4 steps in flight
 using S256 = gemm_relu::staged::Tile<256, 256, 64, 2, 2>;  // generic instance of the same tile
 using S128 = gemm_relu::staged::Tile<128, 128, 64, 2, 2>;  // the pages' 128x128x64 tile
 using S64 = gemm_relu::staged::Tile<64, 64, 64, 2, 2>;     // 4 waves x 32x32
@@ -99,6 +101,10 @@ const TileEntry kTiles[] = {
     {"splitk_16x128_w4k_mfma16x16x32_regT", 16, 128, 1, true, launch_splitk<K16>, launch_staged<S16, false>},
     {"splitk_32x128_w4k_mfma16x16x32_regT", 32, 128, 1, true, launch_splitk<K32>, launch_staged<S64, false>},
     {"splitk_64x128_w4k_mfma16x16x32_regT", 64, 128, 1, true, launch_splitk<K64>, launch_staged<S64, false>},
+    {"256x256x32s4_w4x2_mfma32x32x16_lds-dma", 256, 256, 4, false, launch_pipelined<P256W8>,
+     launch_staged<S256, false>},
+    {"256x256x32s5_w2x2_mfma32x32x16_lds-dma", 256, 256, 4, false, launch_pipelined<P256S5>,
+     launch_staged<S256, false>},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kGenericTile = 2;  // tile used by the element-wise path

@@ -45,14 +45,16 @@
 // 16-byte aligned, BM * K * 2 and 32 * N * 2 below 2^31.
 #pragma once
 
+#include <utility>
+
 #include "common.hpp"
 
 namespace gemm_relu {
 namespace pipelined {
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_ = 4>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = 4;
+    static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = STAGES_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int NW = WAVES_M * WAVES_N, NT = kWave * NW;
     static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;  // wave sub-tile
@@ -71,8 +73,10 @@ struct Cfg {
     static_assert(A_LOADS % NW == 0 && B_LOADS % NW == 0, "loads must split evenly over waves");
     static_assert(TM % 32 == 0 && TN % 128 == 0, "wave sub-tile: 32-row blocks, 128-column units");
     static_assert(2 * LPT < 64, "vmcnt range");
-    static_assert(NSLOT + 3 <= NMMA, "the reads of x must be issued before block x starts");
-    static_assert(STAGES * STAGE_BYTES == BM * BN * 2, "the C tile must fill the LDS ring exactly");
+    static_assert(STAGES >= 3 && STAGES <= 5, "ring of 3 to 5 slots");
+    static_assert((STAGES - 2) * LPT < 64, "vmcnt range");
+    static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
+    static_assert(4 * STAGE_BYTES == BM * BN * 2, "the C tile fills the first four slots exactly");
     static_assert(BN == 256, "the epilogue maps 32 lanes x 16 B onto one row of C");
 };
 
@@ -93,46 +97,31 @@ __device__ __forceinline__ int b_swz(int kr) { return 2 * (kr & 3); }
 // accumulator layout touches land on 32 different chunks.
 __device__ __forceinline__ int c_swz(int r) { return r & 31; }
 
-// Which memory item follows the matrix op at each position of a region of
-// 2 * NMMA ops (positions 0..NMMA-1 use fragments y, the rest x). After
-// position kPre (the barrier and the descriptors), the read slots of x
-// alternate two-to-one with loads until block x begins, then the read slots
-// of y do the same; leftover loads fill the next free positions. Every
-// position holds at most one item.
-template <int NMMA, int NSLOT, int LPT>
+// Which memory items follow the matrix op at each position of a region of
+// 2 * NMMA ops (positions 0..NMMA-1 use fragments y, the rest x). Positions
+// up to PRE hold the barrier and the descriptors. After them:
+//  * the NSLOT read slots of x, one per position, all before block x starts;
+//  * the NSLOT read slots of y, one per position from the start of block x
+//    (after the last op that reads y);
+//  * the LPT loads spread evenly over every position after PRE, at most one
+//    per position (a position may hold a load and a read slot).
+template <int NMMA, int NSLOT, int LPT, int PRE>
 struct RegionPlan {
-    static constexpr int kNone = 0, kReadX = 1, kReadY = 2, kLoad = 3;
-    int kind[2 * NMMA];
-    int index[2 * NMMA];
-    constexpr explicit RegionPlan(int pre) : kind{}, index{}
+    static constexpr int kPositions = 2 * NMMA;
+    int load[kPositions];   // load index or -1
+    int readx[kPositions];  // x read slot or -1
+    int ready[kPositions];  // y read slot or -1
+    constexpr RegionPlan() : load{}, readx{}, ready{}
     {
-        int xi = 0, yi = 0, li = 0;
-        for (int q = pre + 1, run = 0; q < 2 * NMMA; ++q) {
-            const bool block_x = q >= NMMA;
-            int& ri = block_x ? yi : xi;
-            if (!block_x && q == NMMA - 1 && xi < NSLOT) run = 0;  // never leave x reads behind
-            if (ri < NSLOT && (run < 2 || li >= LPT)) {
-                kind[q] = block_x ? kReadY : kReadX;
-                index[q] = ri++;
-                ++run;
-            } else if (li < LPT) {
-                kind[q] = kLoad;
-                index[q] = li++;
-                run = 0;
-            }
+        for (int q = 0; q < kPositions; ++q) load[q] = readx[q] = ready[q] = -1;
+        for (int i = 0; i < NSLOT; ++i) {
+            readx[PRE + 1 + i] = i;
+            ready[NMMA + i] = i;
         }
+        const int span = kPositions - PRE - 1;
+        for (int v = 0; v < LPT; ++v) load[PRE + 1 + (v * span) / LPT] = v;
     }
-    constexpr bool complete(int pre) const
-    {
-        int nx = 0, ny = 0, nl = 0, last_x = -1;
-        for (int q = 0; q < 2 * NMMA; ++q) {
-            if (q <= pre && kind[q] != kNone) return false;
-            if (kind[q] == kReadX) { ++nx; last_x = q; }
-            if (kind[q] == kReadY) ++ny;
-            if (kind[q] == kLoad) ++nl;
-        }
-        return nx == NSLOT && ny == NSLOT && nl == LPT && last_x < NMMA;
-    }
+    static constexpr bool fits() { return PRE + 1 + NSLOT <= NMMA && NSLOT <= NMMA && LPT <= kPositions - PRE - 1; }
 };
 
 template <class T, bool KALIGNED>
@@ -145,11 +134,14 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     __shared__ __attribute__((aligned(1024))) uint16_t st1[T::A_HALVES + T::B_HALVES];
     __shared__ __attribute__((aligned(1024))) uint16_t st2[T::A_HALVES + T::B_HALVES];
     __shared__ __attribute__((aligned(1024))) uint16_t st3[T::A_HALVES + T::B_HALVES];
+    // a fifth slot only when the ring has five (otherwise a zero-size array)
+    __shared__ __attribute__((aligned(1024))) uint16_t st4[T::STAGES > 4 ? T::A_HALVES + T::B_HALVES : 1];
     auto stage_a = [&]<int S>() -> uint16_t* {
         if constexpr (S == 0) return st0;
         else if constexpr (S == 1) return st1;
         else if constexpr (S == 2) return st2;
-        else return st3;
+        else if constexpr (S == 3) return st3;
+        else return st4;
     };
     auto stage_b = [&]<int S>() -> uint16_t* { return stage_a.template operator()<S>() + T::A_HALVES; };
 
@@ -287,65 +279,66 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         asm volatile("" ::: "memory");
     };
 
-    // The ring runs for nk4 = nk rounded up to a multiple of 4 steps, so that
-    // the 4-way unrolled loop has no exits and no branch around the matrix
-    // operations (such branches make the register allocator copy the whole
-    // accumulator). The extra steps multiply zero tiles.
-    const int nk4 = (nk + 3) & ~3;
+    // The ring runs for nkr = nk rounded up to a multiple of STAGES steps, so
+    // that the STAGES-way unrolled loop has no exits and no branch around the
+    // matrix operations (such branches make the register allocator copy the
+    // whole accumulator). The extra steps multiply zero tiles.
+    constexpr int R = T::STAGES, AHEAD = T::STAGES - 1;  // loads run AHEAD steps ahead
+    const int nkr = (nk + R - 1) / R * R;
     Frag x, y;
 
-    // The code of region kt (S = kt % 4): 2 * NMMA matrix ops, those of step
+    // The code of region kt (S = kt % R): 2 * NMMA matrix ops, those of step
     // kt, second half (fragments y), then those of step kt+1, first half
-    // (fragments x). Position q of the region is one matrix op followed by at
-    // most one memory item (see RegionPlan):
+    // (fragments x). Position q of the region is one matrix op followed by
+    // the memory items RegionPlan puts there:
     //  * before position kPre: the barrier. This wave's loads of step kt+1
-    //    have landed and its fragment reads are done, and after it every
-    //    wave's have. The first kPre ops of y do not depend on it and are
+    //    have landed (later steps may still be in flight) and its fragment
+    //    reads are done, and after it every wave's have. The first kPre ops of y do not depend on it and are
     //    issued first, so the matrix cores have work while the waves meet.
-    //  * at position kPre: the descriptors of step kt+3;
-    //  * then, one item per position: the read slots of step kt+1's first
-    //    half (into x, needed by block x), the loads of step kt+3, and from the
-    //    start of block x the read slots of step kt+1's second half (into y).
+    //  * at position kPre: the descriptors of step kt+AHEAD;
+    //  * then the read slots of step kt+1's first half (into x, needed by
+    //    block x), from the start of block x the read slots of its second
+    //    half (into y), and the loads of step kt+AHEAD spread over the region.
     // A wave issues instructions in order, so whatever sits between two
     // matrix ops must issue within one op's 32 cycles or the matrix core
-    // idles: a one-kilobyte direct-to-LDS load and a fragment read never
-    // share a gap.
-    // The loads of step kt+3 overwrite the stage of step kt-1, which every
-    // wave finished reading before this barrier.
-    constexpr int kPre = 2;
-    constexpr RegionPlan<T::NMMA, T::NSLOT, T::LPT> plan(kPre);
-    static_assert(plan.complete(kPre), "every read slot and load must be placed, the x reads before block x");
+    // idles; the four waves' 32 one-kilobyte direct-to-LDS loads of a step,
+    // issued in a burst, held the matrix ops behind them for ~260 cycles.
+    // The loads of step kt+AHEAD overwrite the stage of step kt-1, which
+    // every wave finished reading before this barrier.
+    constexpr int kPre = (T::NMMA - 1 - T::NSLOT) < 2 ? (T::NMMA - 1 - T::NSLOT) : 2;
+    using Plan = RegionPlan<T::NMMA, T::NSLOT, T::LPT, kPre>;
+    static_assert(kPre >= 0 && Plan::fits(), "the region has too few matrix ops for its reads and loads");
+    constexpr Plan plan;
     auto region = [&]<int S>(int kt) {
-        constexpr int S1 = (S + 1) % 4, S3 = (S + 3) % 4;
+        constexpr int S1 = (S + 1) % R, SL = (S + AHEAD) % R;
         Rsrc r;
 #pragma unroll
         for (int q = 0; q < 2 * T::NMMA; ++q) {
-            // step kt+1 has landed (kt+2 may still be in flight)
-            if (q == kPre) sync.template operator()<T::LPT>();
+            // step kt+1 has landed (steps up to kt+AHEAD-1 may still be in flight)
+            if (q == kPre) sync.template operator()<(AHEAD - 2) * T::LPT>();
             if (q < T::NMMA) mma_one(y, q);
             else mma_one(x, q - T::NMMA);
-            if (q == kPre) r = descriptors(kt + 3);
-            const int k = plan.kind[q], n = plan.index[q];
-            if (k == RegionPlan<T::NMMA, T::NSLOT, T::LPT>::kLoad) load_one.template operator()<S3>(n, r, kt + 3);
-            if (k == RegionPlan<T::NMMA, T::NSLOT, T::LPT>::kReadX) read_slot.template operator()<S1>(0, n, x);
-            if (k == RegionPlan<T::NMMA, T::NSLOT, T::LPT>::kReadY) read_slot.template operator()<S1>(1, n, y);
+            if (q == kPre) r = descriptors(kt + AHEAD);
+            if (plan.load[q] >= 0) load_one.template operator()<SL>(plan.load[q], r, kt + AHEAD);
+            if (plan.readx[q] >= 0) read_slot.template operator()<S1>(0, plan.readx[q], x);
+            if (plan.ready[q] >= 0) read_slot.template operator()<S1>(1, plan.ready[q], y);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    if (nk4 > 0) {
-        // prologue: steps 0..2 in flight; wait for step 0, read both of its
-        // halves and run its first half
-        {
-            const Rsrc r0 = descriptors(0), r1 = descriptors(1), r2 = descriptors(2);
+    if (nkr > 0) {
+        // prologue: steps 0..AHEAD-1 in flight; wait for step 0, read both
+        // of its halves and run its first half
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            (
+                [&] {
+                    const Rsrc r0 = descriptors(I);
 #pragma unroll
-            for (int i = 0; i < T::LPT; ++i) load_one.template operator()<0>(i, r0, 0);
-#pragma unroll
-            for (int i = 0; i < T::LPT; ++i) load_one.template operator()<1>(i, r1, 1);
-#pragma unroll
-            for (int i = 0; i < T::LPT; ++i) load_one.template operator()<2>(i, r2, 2);
-        }
-        sync.template operator()<2 * T::LPT>();
+                    for (int i = 0; i < T::LPT; ++i) load_one.template operator()<I>(i, r0, I);
+                }(),
+                ...);
+        }(std::make_integer_sequence<int, AHEAD>{});
+        sync.template operator()<(AHEAD - 1) * T::LPT>();
 #pragma unroll
         for (int s = 0; s < T::NSLOT; ++s) read_slot.template operator()<0>(0, s, x);
 #pragma unroll
@@ -356,13 +349,12 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         }
     }
 
-    // Each pass of this loop runs four regions; the last region of the last
-    // pass multiplies the first half of step nk4, a zero tile.
-    for (int kt = 0; kt < nk4; kt += 4) {
-        region.template operator()<0>(kt);
-        region.template operator()<1>(kt + 1);
-        region.template operator()<2>(kt + 2);
-        region.template operator()<3>(kt + 3);
+    // Each pass of this loop runs R regions; the last region of the last
+    // pass multiplies the first half of step nkr, a zero tile.
+    for (int kt = 0; kt < nkr; kt += R) {
+        [&]<int... S>(std::integer_sequence<int, S...>) {
+            (region.template operator()<S>(kt + S), ...);
+        }(std::make_integer_sequence<int, R>{});
     }
     // the zero-filling loads past the end must land, and every wave must be
     // done with its fragment reads, before the ring is reused
