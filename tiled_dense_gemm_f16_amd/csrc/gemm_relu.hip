@@ -37,10 +37,12 @@ using gemm_relu::Args;
 using P256 = gemm_relu::pipelined::Cfg<256, 256, 2, 2>;   // 4 waves x 128x128, 32x32x16 MFMA
 using P256W8 = gemm_relu::pipelined::Cfg<256, 256, 4, 2>; // 8 waves x 64x128: two waves per SIMD
 using P256S5 = gemm_relu::pipelined::Cfg<256, 256, 2, 2, 5>; // five-slot ring: 4 steps in flight
+using P128 = gemm_relu::pipelined::Cfg<128, 256, 2, 2>;      // 4 waves x 64x128
+using P64 = gemm_relu::pipelined::Cfg<64, 256, 1, 2>;        // 2 waves x 64x128
 using S256 = gemm_relu::staged::Tile<256, 256, 64, 2, 2>;  // generic instance of the same tile
-using S128 = gemm_relu::staged::Tile<128, 128, 64, 2, 2>;  // the pages' 128x128x64 tile
-using S64 = gemm_relu::staged::Tile<64, 64, 64, 2, 2>;     // 4 waves x 32x32
-using S16 = gemm_relu::staged::Tile<16, 64, 64, 1, 4>;     // 4 waves x 16x16: few rows
+using S128 = gemm_relu::staged::Tile<128, 128, 64, 2, 2, 1, 3>;  // the pages' 128x128x64 tile
+using S64 = gemm_relu::staged::Tile<64, 64, 64, 2, 2, 1, 4>;      // 4 waves x 32x32
+using S16 = gemm_relu::staged::Tile<16, 64, 64, 1, 4, 1, 4>;      // 4 waves x 16x16: few rows
 #ifndef GR_SPLITK_NW
 #define GR_SPLITK_NW 4
 #endif
@@ -105,10 +107,14 @@ const TileEntry kTiles[] = {
      launch_staged<S256, false>},
     {"256x256x32s5_w2x2_mfma32x32x16_lds-dma", 256, 256, 4, false, launch_pipelined<P256S5>,
      launch_staged<S256, false>},
+    {"128x256x32s4_w2x2_mfma32x32x16_lds-dma", 128, 256, 4, false, launch_pipelined<P128>,
+     launch_staged<S128, false>},
+    {"64x256x32s4_w1x2_mfma32x32x16_lds-dma", 64, 256, 4, false, launch_pipelined<P64>, launch_staged<S64, false>},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kGenericTile = 2;  // tile used by the element-wise path
 constexpr int kSplitK16 = 4, kSplitK32 = 5, kSplitK64 = 6;
+constexpr int kPipe64 = 10;  // 64x256 pipelined tile
 constexpr int kSplitKTN = 128;   // columns of a split-K workgroup
 constexpr int kSplitKStep = GR_SPLITK_NW * 32;  // K granularity of a split-K workgroup (waves x 32)
 constexpr int kTargetBlocks = GR_SPLITK_TARGET;  // workgroups to aim for
@@ -146,10 +152,9 @@ int choose_tile(int64_t M, int64_t N, int64_t K)
     };
     // few rows: stream B once, K split to fill the chip
     if (M <= 64 && splitk_ok(M, K)) return M <= 16 ? kSplitK16 : M <= 32 ? kSplitK32 : kSplitK64;
-    if (M <= 16) return 3;
-    if (blocks(0) >= 256) return 0;
-    if (blocks(1) >= 128) return 1;
-    return 2;
+    if (blocks(0) >= 256) return 0;  // enough 256x256 tiles to fill the chip
+    if (N >= 192) return kPipe64;     // 64x256 pipelined tiles, two workgroups per CU
+    return 2;                         // narrow: 64x64 register-staged tiles
 }
 
 // ---------------------------------------------------------------------------

@@ -68,15 +68,21 @@ struct Cfg {
     static constexpr int B_ROW_BYTES = BN * 2;
     static constexpr int NMMA = FM * FN;                           // matrix ops per half-step
     static constexpr int NSLOT = FM + FN;                          // fragment-read slots per half-step
-    // epilogue: the fp16 C tile, BN * 2 bytes per row, fills the ring exactly
-    static constexpr int C_ROWS_PER_STAGE = STAGE_BYTES / (BN * 2);
+    // epilogue: the fp16 C tile (BN * 2 bytes per row) goes through the first
+    // slots of the ring, C_ROWS_PER_STAGE rows per slot: the largest
+    // multiple of 32 rows that fits in a slot, rounded down to a power of two
+    // so that blocks of 32 rows never straddle two slots
+    static constexpr int C_ROWS_FIT = STAGE_BYTES / (BN * 2);
+    static constexpr int C_ROWS_PER_STAGE = C_ROWS_FIT >= 128 ? 128 : C_ROWS_FIT >= 64 ? 64 : 32;
+    static constexpr int C_ROWS_PER_PASS = NT / (BN / 8);  // rows stored per pass (16 B per lane)
     static_assert(A_LOADS % NW == 0 && B_LOADS % NW == 0, "loads must split evenly over waves");
     static_assert(TM % 32 == 0 && TN % 128 == 0, "wave sub-tile: 32-row blocks, 128-column units");
     static_assert(2 * LPT < 64, "vmcnt range");
     static_assert(STAGES >= 3 && STAGES <= 5, "ring of 3 to 5 slots");
     static_assert((STAGES - 2) * LPT < 64, "vmcnt range");
     static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
-    static_assert(4 * STAGE_BYTES == BM * BN * 2, "the C tile fills the first four slots exactly");
+    static_assert(C_ROWS_FIT >= 32 && BM <= STAGES * C_ROWS_PER_STAGE, "the C tile must fit in the ring");
+    static_assert(C_ROWS_PER_STAGE % C_ROWS_PER_PASS == 0, "a store pass stays in one slot");
     static_assert(BN == 256, "the epilogue maps 32 lanes x 16 B onto one row of C");
 };
 
@@ -133,15 +139,13 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     __shared__ __attribute__((aligned(1024))) uint16_t st0[T::A_HALVES + T::B_HALVES];
     __shared__ __attribute__((aligned(1024))) uint16_t st1[T::A_HALVES + T::B_HALVES];
     __shared__ __attribute__((aligned(1024))) uint16_t st2[T::A_HALVES + T::B_HALVES];
-    __shared__ __attribute__((aligned(1024))) uint16_t st3[T::A_HALVES + T::B_HALVES];
-    // a fifth slot only when the ring has five (otherwise a zero-size array)
-    __shared__ __attribute__((aligned(1024))) uint16_t st4[T::STAGES > 4 ? T::A_HALVES + T::B_HALVES : 1];
+    // the last array holds slot 3 and, in a five-slot ring, slot 4
+    __shared__ __attribute__((aligned(1024))) uint16_t st3[(T::STAGES - 3) * (T::A_HALVES + T::B_HALVES)];
     auto stage_a = [&]<int S>() -> uint16_t* {
         if constexpr (S == 0) return st0;
         else if constexpr (S == 1) return st1;
         else if constexpr (S == 2) return st2;
-        else if constexpr (S == 3) return st3;
-        else return st4;
+        else return st3 + (S - 3) * (T::A_HALVES + T::B_HALVES);
     };
     auto stage_b = [&]<int S>() -> uint16_t* { return stage_a.template operator()<S>() + T::A_HALVES; };
 
@@ -364,7 +368,7 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     // Lane holds, for result rows d = 8q + 4*(lane/32) + r (r = 0..3), the
     // column 16*(j%4) + 64*(q/2) + 8*(q%2) + 4*(lane/32) + r of unit j/4.
     auto c_stage = [&](int s) -> char* {
-        return reinterpret_cast<char*>(s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3);
+        return reinterpret_cast<char*>(s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3 + (s - 3) * (T::A_HALVES + T::B_HALVES));
     };
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
@@ -387,11 +391,12 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    constexpr int kRowsPerPass = T::NT / 32;  // 32 lanes x 16 B per row
+    constexpr int kRowsPerPass = T::C_ROWS_PER_PASS;  // BN / 8 lanes x 16 B per row
+    constexpr int kLanesPerRow = T::BN / 8;
 #pragma unroll
     for (int it = 0; it < T::BM / kRowsPerPass; ++it) {
-        const int rl = it * kRowsPerPass + (int)threadIdx.x / 32;
-        const int c = threadIdx.x % 32;
+        const int rl = it * kRowsPerPass + (int)threadIdx.x / kLanesPerRow;
+        const int c = threadIdx.x % kLanesPerRow;
         const char* cs = c_stage((it * kRowsPerPass) / T::C_ROWS_PER_STAGE);
         const u32x4 v = *reinterpret_cast<const u32x4*>(cs + (rl % T::C_ROWS_PER_STAGE) * (T::BN * 2) +
                                                         ((c ^ c_swz(rl)) * 16));

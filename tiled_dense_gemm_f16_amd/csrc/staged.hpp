@@ -26,7 +26,7 @@ namespace staged {
 // on 8 different physical chunks (all 32 four-byte banks of a 128-byte span).
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MIN_WAVES_ = 1>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MIN_WAVES_ = 1, int PREFETCH_ = 1>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -41,6 +41,9 @@ struct Tile {
     static constexpr int STAGE_HALVES = (BM + BN) * BK;
     static constexpr int LDS_BYTES = 2 * STAGE_HALVES * 2;
     static constexpr int MIN_WAVES = MIN_WAVES_;
+    // k-steps whose loads are in flight in registers (vector path only)
+    static constexpr int PREFETCH = PREFETCH_;
+    static_assert(PREFETCH >= 1 && PREFETCH <= 8, "register ring depth");
     static_assert(BK == 64, "the swizzle assumes 8 chunks per row");
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole MFMA blocks");
     static_assert(BM % WAVES_M == 0 && BN % WAVES_N == 0, "waves must divide the tile");
@@ -60,9 +63,10 @@ __device__ __forceinline__ void load_tile(const Args& p, int m0, int n0, int k0,
     const int K = p.K, N = p.N, M = p.M;
     if constexpr (VEC) {
         // A: BM rows x KC chunks, block base at row m0, column k0
-        const uint16_t* abase = p.A + (int64_t)m0 * K + k0;
-        const uint64_t arem = ((uint64_t)(M - m0) * (uint64_t)K - (uint64_t)k0) * 2u;
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, arem);
+        // (a step past the end of K gets an empty descriptor: zeros)
+        const int64_t arem = ((int64_t)(M - m0) * K - k0) * 2;
+        const uint16_t* abase = p.A + (int64_t)m0 * K + (k0 < K ? k0 : K);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, (uint64_t)(k0 < K && arem > 0 ? arem : 0));
         const bool ktail = (k0 + T::BK > K);
 #pragma unroll
         for (int i = 0; i < T::A_PER_T; ++i) {
@@ -76,9 +80,9 @@ __device__ __forceinline__ void load_tile(const Args& p, int m0, int n0, int k0,
         // B: BK rows x BN columns as 8x8 units; unit u -> k-block u % KC,
         // n-block u / KC (8 consecutive lanes cover one n-block's 8 k-blocks,
         // so the transposed LDS writes below hit 8 different chunks)
-        const uint16_t* bbase = p.B + (int64_t)k0 * N;
-        const uint64_t brem = (uint64_t)(K - k0) * (uint64_t)N * 2u;
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bbase, brem);
+        const int64_t brem = ((int64_t)K - k0) * N * 2;
+        const uint16_t* bbase = p.B + (int64_t)(k0 < K ? k0 : K) * N;
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bbase, (uint64_t)(brem > 0 ? brem : 0));
 #pragma unroll
         for (int i = 0; i < T::B_PER_T; ++i) {
             const int u = t + i * T::NT;
@@ -203,20 +207,62 @@ __global__ void __launch_bounds__(T::NT, T::MIN_WAVES) staged_kernel(Args p)
         for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = (p.K + T::BK - 1) / T::BK;
-    Staging<T> st;
-    if (nk > 0) {
-        load_tile<T, VEC>(p, m0, n0, 0, st);
-        store_tile<T>(smem, smem + T::BM * T::BK, st);
-        __syncthreads();
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-        uint16_t* cur = smem + (kt & 1) * T::STAGE_HALVES;
-        uint16_t* nxt = smem + ((kt + 1) & 1) * T::STAGE_HALVES;
-        const bool more = kt + 1 < nk;
-        if (more) load_tile<T, VEC>(p, m0, n0, (kt + 1) * T::BK, st);
-        compute_tile<T>(cur, cur + T::BM * T::BK, acc, wm, wn, lane);
-        if (more) store_tile<T>(nxt, nxt + T::BM * T::BK, st);
-        __syncthreads();
+    if constexpr (!VEC || T::PREFETCH == 1) {
+        Staging<T> st;
+        if (nk > 0) {
+            load_tile<T, VEC>(p, m0, n0, 0, st);
+            store_tile<T>(smem, smem + T::BM * T::BK, st);
+            __syncthreads();
+        }
+        for (int kt = 0; kt < nk; ++kt) {
+            uint16_t* cur = smem + (kt & 1) * T::STAGE_HALVES;
+            uint16_t* nxt = smem + ((kt + 1) & 1) * T::STAGE_HALVES;
+            const bool more = kt + 1 < nk;
+            if (more) load_tile<T, VEC>(p, m0, n0, (kt + 1) * T::BK, st);
+            compute_tile<T>(cur, cur + T::BM * T::BK, acc, wm, wn, lane);
+            if (more) store_tile<T>(nxt, nxt + T::BM * T::BK, st);
+            __syncthreads();
+        }
+    } else {
+        // Register ring of D = PREFETCH k-steps: step s lives in slot s % D.
+        // While step kt is multiplied out of LDS, step kt+1 is moved from its
+        // slot into the other LDS buffer and the loads of step kt+1+D are
+        // issued into the slot it frees, so D steps of loads are in flight:
+        // with small tiles one step's multiply is far shorter than a load's
+        // latency. The loop body has no branches (they make the compiler
+        // drain every load before each LDS store): it runs for nk rounded up
+        // to a multiple of D, and steps past the end of K load and multiply
+        // zeros.
+        constexpr int D = T::PREFETCH;
+        Staging<T> st[D];
+        auto issue = [&](int slot, int s) { load_tile<T, true>(p, m0, n0, s * T::BK, st[slot]); };
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            issue(d, d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int nkd = (nk + D - 1) / D * D;
+        if (nk > 0) {
+            store_tile<T>(smem, smem + T::BM * T::BK, st[0]);
+            __syncthreads();
+            issue(0, D);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int kt0 = 0; kt0 < nkd; kt0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int kt = kt0 + d;
+                uint16_t* cur = smem + (kt & 1) * T::STAGE_HALVES;
+                uint16_t* nxt = smem + ((kt + 1) & 1) * T::STAGE_HALVES;
+                compute_tile<T>(cur, cur + T::BM * T::BK, acc, wm, wn, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                store_tile<T>(nxt, nxt + T::BM * T::BK, st[(d + 1) % D]);
+                __syncthreads();
+                issue((d + 1) % D, kt + 1 + D);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        wait_vmcnt<0>();  // the loads past the end must land before the kernel ends
     }
 
     // Epilogue: ReLU on the fp32 accumulator, round to fp16 (nearest even),
