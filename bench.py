@@ -1,12 +1,14 @@
 """Throughput of C = ReLU(A @ B) (fp16 in, fp32 accumulate, fp16 out) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--graph G] [--no-cpu-baseline]
 
 A step is one call of gemm_relu_f16 on one batch of synthetic input that is
 already resident in HBM: the whole hot path (tile loads, MFMA main loop, ReLU,
 fp16 store) in one kernel. W untimed steps are followed by K timed ones,
-bracketed by stream synchronisation; the line printed on stdout is one JSON
-object. Extra per-workload lines (``--all``) go to stderr.
+bracketed by stream synchronisation; the calls are captured G at a time into a
+HIP graph and replayed (--graph 0 launches them one by one). The line printed
+on stdout is one JSON object. Extra per-workload lines (``--all``) go to
+stderr.
 
 The CPU baseline leg times the oracle (plain C, all host threads) on a bounded
 slice of the same workload -- leading rows of C -- and scales it to TFLOP/s.
@@ -31,24 +33,30 @@ PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA: 256 CU x 4096 FLOP/clk x 2
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "TFLOP/s and % of MI355X dense FP16 MFMA peak, fp16 GEMM+ReLU 4096³"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_relu.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "tiled_dense_gemm_f16_amd", "csrc", f) for f in ("gemm_relu.hip", "common.hpp", "pipelined.hpp", "staged.hpp")] + [
-                  os.path.join(ROOT, "include", "gemm_relu.h")]
+CSRC = os.path.join(ROOT, "tiled_dense_gemm_f16_amd", "csrc")
 
 
-def source_hash() -> str:
+def kernel_sources(tile: str) -> list[str]:
+    """Device sources of the kernel family that runs a tile."""
+    family = "pipelined.hpp" if "lds-dma" in tile else "splitk.hpp" if "splitk" in tile else "staged.hpp"
+    return [os.path.join(CSRC, "common.hpp"), os.path.join(CSRC, family)]
+
+
+def source_hash(tile: str) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in kernel_sources(tile):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str) -> float | None:
+def measured_traffic(workload: str, tile: str) -> float | None:
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; otherwise None."""
+    was taken on the current source of the kernel that runs `tile`;
+    otherwise None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    cur = source_hash()
+    cur = source_hash(tile)
     entries, entry = [], {}
     for line in open(TRAFFIC_FILE):
         line = line.strip()
@@ -63,7 +71,7 @@ def measured_traffic(workload: str) -> float | None:
     if entry:
         entries.append(entry)
     for e in entries:
-        if e.get("workload") == workload and e.get("source_sha256") == cur:
+        if e.get("workload") == workload and e.get("tile") == tile and e.get("kernel_source_sha256") == cur:
             try:
                 return float(e["traffic_bytes_per_launch"])
             except (KeyError, ValueError):
@@ -74,12 +82,21 @@ def measured_traffic(workload: str) -> float | None:
 ROTATE_BYTES = 768 << 20  # well above the 256 MB last-level (MALL) cache
 
 
-def time_gpu(w, steps: int, warmup: int, tile=None):
-    """Times `steps` back-to-back launches, and 200 single launches bracketed
-    by their own events, on torch's current stream. Successive launches cycle
-    through R copies of (A, B) with R * (|A| + |B|) >= 768 MiB (at most 8), so
-    the inputs of a launch are not left in the last-level cache by the
-    previous ones: every launch reads its inputs from HBM."""
+def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0):
+    """Times `steps` back-to-back launches on one stream, bracketed by two
+    events on that stream. Successive launches cycle through R copies of
+    (A, B) with R * (|A| + |B|) >= 768 MiB (at most 8), so the inputs of a
+    launch are not left in the last-level cache by the previous ones: every
+    launch reads its inputs from HBM.
+
+    With graph_batch = G > 0 the launches are captured G at a time into a HIP
+    graph (after the warm-up, so any workspace already exists and nothing is
+    allocated or cleared inside the graph) and the timed region replays it
+    steps / G times: the device throughput without the host's per-call
+    launch cost, which otherwise dominates for kernels of a few microseconds.
+
+    Also times 200 single launches, each between its own pair of events, for
+    the duration of one launch."""
     import torch
     import tiled_dense_gemm_f16_amd as gr
 
@@ -89,39 +106,53 @@ def time_gpu(w, steps: int, warmup: int, tile=None):
     ads = [a.cuda() for _ in range(rot)]
     bds = [b.cuda() for _ in range(rot)]
     c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
-    stream = torch.cuda.current_stream()
+    stream = torch.cuda.Stream()
     opts = gr.make_opts(tile)
     args = [(w.M, w.N, w.K, ads[i].data_ptr(), bds[i].data_ptr(), c.data_ptr(), stream.cuda_stream, opts)
             for i in range(rot)]
-    for i in range(warmup):
-        st = gr.gemm_relu_f16_ex(*args[i % rot])
-        if st != gr.OK:
-            raise RuntimeError(gr.strerror(st))
     torch.cuda.synchronize()
-    # the whole timed region between two events on the launch stream
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(steps):
-        gr.gemm_relu_f16_ex(*args[i % rot])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    # per-launch event pairs (same stream) for the kernel's own duration
-    nper = min(steps, 200)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nper)]
-    for i, (e0, e1) in enumerate(evs):
-        e0.record(stream)
-        gr.gemm_relu_f16_ex(*args[i % rot])
-        e1.record(stream)
-    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            st = gr.gemm_relu_f16_ex(*args[i % rot])
+            if st != gr.OK:
+                raise RuntimeError(gr.strerror(st))
+        torch.cuda.synchronize()
+        graph = None
+        if graph_batch > 0:
+            steps = max(graph_batch, steps // graph_batch * graph_batch)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for i in range(graph_batch):
+                    gr.gemm_relu_f16_ex(*args[i % rot])
+            graph.replay()
+            torch.cuda.synchronize()
+        # the whole timed region between two events on the launch stream
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        if graph is not None:
+            for _ in range(steps // graph_batch):
+                graph.replay()
+        else:
+            for i in range(steps):
+                gr.gemm_relu_f16_ex(*args[i % rot])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        total_ms = t0.elapsed_time(t1)
+        # per-launch event pairs (same stream) for the kernel's own duration
+        nper = min(steps, 200)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nper)]
+        for i, (e0, e1) in enumerate(evs):
+            e0.record(stream)
+            gr.gemm_relu_f16_ex(*args[i % rot])
+            e1.record(stream)
+        torch.cuda.synchronize()
     per = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
-    # the output of the last launch, on input copy (nper - 1) % rot: all copies are equal
     tile_id = gr.select_tile(w.M, w.N, w.K, ads[0].data_ptr(), bds[0].data_ptr(), c.data_ptr()) if tile is None else tile
-    return {"total_ms": total_ms, "ms_per_step": total_ms / steps,
+    return {"total_ms": total_ms, "steps": steps, "ms_per_step": total_ms / steps,
             "launch_ms_mean": float(per.mean()), "launch_ms_median": float(np.median(per)),
             "launch_ms_min": float(per.min()), "tile": gr.tile_name(tile_id) if tile_id >= 0 else "generic",
-            "rotation": rot, "c": c, "a": a, "b": b}
+            "rotation": rot, "graph_batch": graph_batch, "c": c, "a": a, "b": b}
 
 
 def cpu_baseline(w, gpu_c, target_s: float = 12.0):
@@ -157,7 +188,8 @@ def cpu_baseline(w, gpu_c, target_s: float = 12.0):
 def result_line(w, r, steps, warmup, cpu=None):
     bound = "hbm" if 2 * w.M * w.N * w.K / w.min_bytes < 315 and w.M <= 64 else "mfma"
     value = w.flops / (r["ms_per_step"] * 1e-3) / 1e12
-    launch_s = r["launch_ms_mean"] * 1e-3
+    # one launch per step: the kernel's average duration over the timed region
+    launch_s = r["ms_per_step"] * 1e-3
     if bound == "mfma":
         achieved = w.flops / launch_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
@@ -166,8 +198,8 @@ def result_line(w, r, steps, warmup, cpu=None):
         achieved = w.min_bytes / launch_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = measured_traffic(w.name)
-    line = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+    roof["traffic"] = measured_traffic(w.name, r["tile"])
+    line = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": r["steps"],
             "warmup": warmup, "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f16", "accum_dtype": "f32", "data": "synthetic",
             "pct_of_fp16_peak": round(100 * value / PEAK_FP16_TFLOPS, 2),
@@ -175,10 +207,12 @@ def result_line(w, r, steps, warmup, cpu=None):
                        "scale": w.scale, "seed": w.seed, "tile": r["tile"], "input_copies_rotated": r["rotation"],
                        "parallelism": "single GPU"},
             "roofline": roof,
-            "kernel_ms": {"mean": round(r["launch_ms_mean"], 5), "median": round(r["launch_ms_median"], 5),
-                          "min": round(r["launch_ms_min"], 5)},
+            "kernel_ms_timed_region_mean": round(r["ms_per_step"], 5),
+            "graph_batch": r["graph_batch"],
+            "single_launch_event_ms": {"mean": round(r["launch_ms_mean"], 5), "median": round(r["launch_ms_median"], 5),
+                                       "min": round(r["launch_ms_min"], 5)},
             "hbm_gbs_at_min_bytes": round(w.min_bytes / (r["ms_per_step"] * 1e-3) / 1e9, 1),
-            "source_sha256": source_hash()}
+            "kernel_source_sha256": source_hash(r["tile"])}
     if cpu is not None:
         line["cpu_baseline"] = cpu
     return line
@@ -194,6 +228,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--all", action="store_true", help="also time every workload (lines on stderr)")
+    ap.add_argument("--graph", type=int, default=50, metavar="G",
+                    help="capture G launches per HIP graph and replay it (0: launch one by one from the host)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run an element-wise copy (negation) of MIB MiB, 20 times: a kernel of known "
                          "traffic, used to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -223,14 +259,14 @@ def main(argv=None) -> int:
     gr.load()
 
     w = workloads.BY_NAME[args.workload]
-    r = time_gpu(w, args.steps, args.warmup, args.tile)
-    print(f"[bench] {w.name}: {r['ms_per_step'] * 1e3:.2f} us/step, kernel mean "
-          f"{r['launch_ms_mean'] * 1e3:.2f} us, tile {r['tile']}", file=sys.stderr, flush=True)
+    r = time_gpu(w, args.steps, args.warmup, args.tile, args.graph)
+    print(f"[bench] {w.name}: {r['ms_per_step'] * 1e3:.2f} us/step (graph batch {r['graph_batch']}), "
+          f"single launches {r['launch_ms_mean'] * 1e3:.2f} us, tile {r['tile']}", file=sys.stderr, flush=True)
     if args.all:
         for ow in workloads.ALL:
             if ow is w:
                 continue
-            orr = time_gpu(ow, max(args.steps // 4, 50), max(args.warmup // 4, 10))
+            orr = time_gpu(ow, max(args.steps // 4, 50), max(args.warmup // 4, 10), None, args.graph)
             print(json.dumps(result_line(ow, orr, max(args.steps // 4, 50), max(args.warmup // 4, 10))),
                   file=sys.stderr, flush=True)
     cpu = None
