@@ -1,4 +1,5 @@
-"""CPU oracle for C = ReLU(A @ B) (fp16 in, fp16 out) -- TEST INFRASTRUCTURE.
+"""CPU oracle for C = ReLU(A @ B) and C = GELU(A @ B + bias) (fp16 in, fp16
+out) -- TEST INFRASTRUCTURE.
 
 Only ``tests/``, the package smoke check in ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package. The product path
@@ -66,6 +67,12 @@ def _load():
         lib.oracle_gemm_relu_f16_rows.restype = ctypes.c_int
         lib.oracle_gemm_relu_f16_points.argtypes = [i64, i64, i64, p, p, i64, p, p, p, p, p]
         lib.oracle_gemm_relu_f16_points.restype = ctypes.c_int
+        lib.oracle_gelu.argtypes = [ctypes.c_double]
+        lib.oracle_gelu.restype = ctypes.c_double
+        lib.oracle_gemm_bias_gelu_f16_rows.argtypes = [i64, i64, i64, p, p, p, p, p, p, i64, i64]
+        lib.oracle_gemm_bias_gelu_f16_rows.restype = ctypes.c_int
+        lib.oracle_gemm_bias_gelu_f16_points.argtypes = [i64, i64, i64, p, p, p, i64, p, p, p, p, p]
+        lib.oracle_gemm_bias_gelu_f16_points.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -103,20 +110,22 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
-def gemm_relu_f16(A: np.ndarray, B: np.ndarray, *, want_pre: bool = False,
-                  want_absdot: bool = False, rows: tuple[int, int] | None = None):
-    """C = ReLU(A @ B) as fp16 bit patterns.
+def gelu(x) -> np.ndarray:
+    """GELU(x) = x * Phi(x) in float64, element by element."""
+    lib = _load()
+    v = np.asarray(x, dtype=np.float64)
+    return np.vectorize(lib.oracle_gelu, otypes=[np.float64])(v)
 
-    A: uint16 [M, K], B: uint16 [K, N]. With ``rows=(r0, r1)`` only those rows
-    are computed and returned (shape [r1-r0, N]). Optionally also returns the
-    float64 pre-activation sums and sum_k |a||b| for the same rows.
-    """
+
+def _rows(A, B, bias, want_pre, want_absdot, rows):
     M, K = A.shape
     K2, N = B.shape
     if K2 != K:
         raise ValueError("inner dimensions differ")
     A = _u16(A, (M, K))
     B = _u16(B, (K, N))
+    if bias is not None:
+        bias = _u16(bias, (N,))
     r0, r1 = (0, M) if rows is None else rows
     # the C routine indexes C, pre and absdot as full [M, N] arrays; only the
     # requested rows are touched, so offset the base pointers accordingly
@@ -130,10 +139,14 @@ def gemm_relu_f16(A: np.ndarray, B: np.ndarray, *, want_pre: bool = False,
             return None
         return ctypes.c_void_p(arr.ctypes.data - r0 * N * itemsize)
 
-    rc = _load().oracle_gemm_relu_f16_rows(M, N, K, _ptr(A), _ptr(B), base(C, 2),
-                                           base(pre, 8), base(sab, 8), r0, r1)
+    lib = _load()
+    if bias is None:
+        rc = lib.oracle_gemm_relu_f16_rows(M, N, K, _ptr(A), _ptr(B), base(C, 2), base(pre, 8), base(sab, 8), r0, r1)
+    else:
+        rc = lib.oracle_gemm_bias_gelu_f16_rows(M, N, K, _ptr(A), _ptr(B), _ptr(bias), base(C, 2), base(pre, 8),
+                                                base(sab, 8), r0, r1)
     if rc != 0:
-        raise RuntimeError("oracle_gemm_relu_f16_rows failed")
+        raise RuntimeError("oracle rows routine failed")
     out = [C]
     if want_pre:
         out.append(pre)
@@ -142,15 +155,15 @@ def gemm_relu_f16(A: np.ndarray, B: np.ndarray, *, want_pre: bool = False,
     return out[0] if len(out) == 1 else tuple(out)
 
 
-def gemm_relu_f16_points(A: np.ndarray, B: np.ndarray, ii, jj, *, want_pre: bool = False,
-                         want_absdot: bool = False):
-    """Elements C[ii[t], jj[t]] of ReLU(A @ B) as fp16 bit patterns."""
+def _points(A, B, bias, ii, jj, want_pre, want_absdot):
     M, K = A.shape
     K2, N = B.shape
     if K2 != K:
         raise ValueError("inner dimensions differ")
     A = _u16(A, (M, K))
     B = _u16(B, (K, N))
+    if bias is not None:
+        bias = _u16(bias, (N,))
     ii = np.ascontiguousarray(ii, dtype=np.int64)
     jj = np.ascontiguousarray(jj, dtype=np.int64)
     if ii.shape != jj.shape or ii.ndim != 1:
@@ -158,13 +171,50 @@ def gemm_relu_f16_points(A: np.ndarray, B: np.ndarray, ii, jj, *, want_pre: bool
     out = np.zeros(ii.shape, dtype=np.uint16)
     pre = np.zeros(ii.shape, dtype=np.float64) if want_pre else None
     sab = np.zeros(ii.shape, dtype=np.float64) if want_absdot else None
-    rc = _load().oracle_gemm_relu_f16_points(M, N, K, _ptr(A), _ptr(B), ii.size, _ptr(ii),
-                                             _ptr(jj), _ptr(out), _ptr(pre), _ptr(sab))
+    lib = _load()
+    if bias is None:
+        rc = lib.oracle_gemm_relu_f16_points(M, N, K, _ptr(A), _ptr(B), ii.size, _ptr(ii), _ptr(jj), _ptr(out),
+                                             _ptr(pre), _ptr(sab))
+    else:
+        rc = lib.oracle_gemm_bias_gelu_f16_points(M, N, K, _ptr(A), _ptr(B), _ptr(bias), ii.size, _ptr(ii),
+                                                  _ptr(jj), _ptr(out), _ptr(pre), _ptr(sab))
     if rc != 0:
-        raise RuntimeError("oracle_gemm_relu_f16_points failed")
+        raise RuntimeError("oracle points routine failed")
     res = [out]
     if want_pre:
         res.append(pre)
     if want_absdot:
         res.append(sab)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def gemm_relu_f16(A: np.ndarray, B: np.ndarray, *, want_pre: bool = False,
+                  want_absdot: bool = False, rows: tuple[int, int] | None = None):
+    """C = ReLU(A @ B) as fp16 bit patterns.
+
+    A: uint16 [M, K], B: uint16 [K, N]. With ``rows=(r0, r1)`` only those rows
+    are computed and returned (shape [r1-r0, N]). Optionally also returns the
+    float64 pre-activation sums and sum_k |a||b| for the same rows.
+    """
+    return _rows(A, B, None, want_pre, want_absdot, rows)
+
+
+def gemm_relu_f16_points(A: np.ndarray, B: np.ndarray, ii, jj, *, want_pre: bool = False,
+                         want_absdot: bool = False):
+    """Elements C[ii[t], jj[t]] of ReLU(A @ B) as fp16 bit patterns."""
+    return _points(A, B, None, ii, jj, want_pre, want_absdot)
+
+
+def gemm_bias_gelu_f16(A: np.ndarray, B: np.ndarray, bias: np.ndarray, *, want_pre: bool = False,
+                       want_absdot: bool = False, rows: tuple[int, int] | None = None):
+    """C = GELU(A @ B + bias) as fp16 bit patterns; bias: uint16 [N], one value per column.
+
+    ``pre`` (if asked for) is the float64 value A @ B + bias before GELU.
+    """
+    return _rows(A, B, bias, want_pre, want_absdot, rows)
+
+
+def gemm_bias_gelu_f16_points(A: np.ndarray, B: np.ndarray, bias: np.ndarray, ii, jj, *,
+                              want_pre: bool = False, want_absdot: bool = False):
+    """Elements C[ii[t], jj[t]] of GELU(A @ B + bias) as fp16 bit patterns."""
+    return _points(A, B, bias, ii, jj, want_pre, want_absdot)

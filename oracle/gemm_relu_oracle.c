@@ -20,6 +20,19 @@
  *   3. y = pre > 0 ? pre : +0 (the ReLU);
  *   4. encode y to fp16 with round to nearest, ties to even.
  *
+ * The second operation is the fused epilogue of "TileLang simplifica la
+ * creación de kernels GPU de alto rendimiento" (section "Fusionar operaciones
+ * para reducir viajes a memoria"): the bias is added to the accumulator and
+ * GELU applied before the single write of C. The page names GELU without a
+ * formula; the oracle uses its definition, GELU(x) = x * Phi(x) with Phi the
+ * standard normal distribution function, Phi(x) = erfc(-x / sqrt 2) / 2.
+ * The page does not give the bias's type or shape either; the reading here
+ * is one fp16 value per column of C (bias[j] added to every row), decoded
+ * exactly like A and B:
+ *
+ *   pre[i][j] = sum over k (ascending) of a[i][k] * b[k][j]  +  bias[j]
+ *   C[i][j]   = fp16_rne( GELU(pre[i][j]) )
+ *
  * Readings where the pages are silent: the final rounding is IEEE
  * round-to-nearest-even (what an ordinary fp32 -> fp16 conversion does);
  * overflow past the largest finite fp16 becomes +inf; fp16 subnormals are
@@ -103,6 +116,15 @@ static uint16_t relu_to_f16(double pre)
     return oracle_f64_to_f16_rne(pre > 0.0 ? pre : 0.0);
 }
 
+/* GELU by its definition: x * Phi(x), with the standard normal distribution
+   function written Phi(x) = erfc(-x / sqrt 2) / 2 -- the same function as
+   (1 + erf(x / sqrt 2)) / 2, without the cancellation of that form for
+   negative x. */
+double oracle_gelu(double x)
+{
+    return x * (0.5 * erfc(-x / sqrt(2.0)));
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP
@@ -112,16 +134,27 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* The epilogue: ReLU (bias == NULL) or bias + GELU. */
+static uint16_t finish(double acc, const uint16_t* bias, int64_t j, double* pre_out)
+{
+    if (!bias) {
+        if (pre_out) *pre_out = acc;
+        return relu_to_f16(acc);
+    }
+    const double pre = acc + oracle_f16_to_f64(bias[j]);
+    if (pre_out) *pre_out = pre;
+    return oracle_f64_to_f16_rne(oracle_gelu(pre));
+}
+
 /*
- * Rows [row0, row1) of C = ReLU(A @ B). C points at row 0 of the full C
- * (leading dimension N). pre, if not NULL, receives the double pre-activation
- * sums (same indexing as C); absdot, if not NULL, receives sum_k |a||b|.
+ * Rows [row0, row1) of C. C points at row 0 of the full C (leading
+ * dimension N). pre, if not NULL, receives the double pre-activation values
+ * (same indexing as C); absdot, if not NULL, receives sum_k |a||b|.
  * Returns 0, or -1 on a bad argument or allocation failure.
  */
-int oracle_gemm_relu_f16_rows(int64_t M, int64_t N, int64_t K,
-                              const uint16_t* A, const uint16_t* B, uint16_t* C,
-                              double* pre, double* absdot,
-                              int64_t row0, int64_t row1)
+static int rows_impl(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
+                     const uint16_t* bias, uint16_t* C, double* pre, double* absdot,
+                     int64_t row0, int64_t row1)
 {
     if (M < 0 || N < 0 || K < 0 || row0 < 0 || row1 > M || row0 > row1) return -1;
     if (N == 0 || row0 == row1) return 0;
@@ -154,8 +187,7 @@ int oracle_gemm_relu_f16_rows(int64_t M, int64_t N, int64_t K,
                     }
                 }
                 for (int64_t j = 0; j < N; ++j) {
-                    C[i * N + j] = relu_to_f16(acc[j]);
-                    if (pre) pre[i * N + j] = acc[j];
+                    C[i * N + j] = finish(acc[j], bias, j, pre ? &pre[i * N + j] : NULL);
                     if (sab) absdot[i * N + j] = sab[j];
                 }
             }
@@ -167,22 +199,13 @@ int oracle_gemm_relu_f16_rows(int64_t M, int64_t N, int64_t K,
     return err ? -1 : 0;
 }
 
-/* The whole of C = ReLU(A @ B). */
-int oracle_gemm_relu_f16(int64_t M, int64_t N, int64_t K,
-                         const uint16_t* A, const uint16_t* B, uint16_t* C,
-                         double* pre, double* absdot)
-{
-    return oracle_gemm_relu_f16_rows(M, N, K, A, B, C, pre, absdot, 0, M);
-}
-
 /*
- * Selected elements (ii[t], jj[t]) of C = ReLU(A @ B), each summed in the same
- * k-ascending order as the full routine, so it gives the same values there.
+ * Selected elements (ii[t], jj[t]), each summed in the same k-ascending order
+ * as the full routine, so it gives the same values there.
  */
-int oracle_gemm_relu_f16_points(int64_t M, int64_t N, int64_t K,
-                                const uint16_t* A, const uint16_t* B,
-                                int64_t npts, const int64_t* ii, const int64_t* jj,
-                                uint16_t* out, double* pre, double* absdot)
+static int points_impl(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
+                       const uint16_t* bias, int64_t npts, const int64_t* ii, const int64_t* jj,
+                       uint16_t* out, double* pre, double* absdot)
 {
     if (M < 0 || N < 0 || K < 0 || npts < 0) return -1;
     for (int64_t t = 0; t < npts; ++t)
@@ -197,9 +220,54 @@ int oracle_gemm_relu_f16_points(int64_t M, int64_t N, int64_t K,
             acc += a * b;
             s += fabs(a) * fabs(b);
         }
-        out[t] = relu_to_f16(acc);
-        if (pre) pre[t] = acc;
+        out[t] = finish(acc, bias, j, pre ? &pre[t] : NULL);
         if (absdot) absdot[t] = s;
     }
     return 0;
+}
+
+/* Rows [row0, row1) of C = ReLU(A @ B). */
+int oracle_gemm_relu_f16_rows(int64_t M, int64_t N, int64_t K,
+                              const uint16_t* A, const uint16_t* B, uint16_t* C,
+                              double* pre, double* absdot,
+                              int64_t row0, int64_t row1)
+{
+    return rows_impl(M, N, K, A, B, NULL, C, pre, absdot, row0, row1);
+}
+
+/* The whole of C = ReLU(A @ B). */
+int oracle_gemm_relu_f16(int64_t M, int64_t N, int64_t K,
+                         const uint16_t* A, const uint16_t* B, uint16_t* C,
+                         double* pre, double* absdot)
+{
+    return rows_impl(M, N, K, A, B, NULL, C, pre, absdot, 0, M);
+}
+
+/* Selected elements of C = ReLU(A @ B). */
+int oracle_gemm_relu_f16_points(int64_t M, int64_t N, int64_t K,
+                                const uint16_t* A, const uint16_t* B,
+                                int64_t npts, const int64_t* ii, const int64_t* jj,
+                                uint16_t* out, double* pre, double* absdot)
+{
+    return points_impl(M, N, K, A, B, NULL, npts, ii, jj, out, pre, absdot);
+}
+
+/* Rows [row0, row1) of C = GELU(A @ B + bias), bias: N fp16 values (one per column). */
+int oracle_gemm_bias_gelu_f16_rows(int64_t M, int64_t N, int64_t K,
+                                   const uint16_t* A, const uint16_t* B, const uint16_t* bias,
+                                   uint16_t* C, double* pre, double* absdot,
+                                   int64_t row0, int64_t row1)
+{
+    if (!bias && N > 0) return -1;
+    return rows_impl(M, N, K, A, B, bias, C, pre, absdot, row0, row1);
+}
+
+/* Selected elements of C = GELU(A @ B + bias). */
+int oracle_gemm_bias_gelu_f16_points(int64_t M, int64_t N, int64_t K,
+                                     const uint16_t* A, const uint16_t* B, const uint16_t* bias,
+                                     int64_t npts, const int64_t* ii, const int64_t* jj,
+                                     uint16_t* out, double* pre, double* absdot)
+{
+    if (!bias && N > 0) return -1;
+    return points_impl(M, N, K, A, B, bias, npts, ii, jj, out, pre, absdot);
 }

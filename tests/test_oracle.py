@@ -470,3 +470,181 @@ def test_planted_mistake_is_caught(mutant, tmp_path):
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
     assert _pin_suite(mod) != [], f"planted mistake {mutant} went unnoticed"
+
+
+# ---------------------------------------------------------------------------
+# 9. the fused bias + GELU epilogue (C = GELU(A @ B + bias))
+# ---------------------------------------------------------------------------
+
+def exact_rne_f16_signed(y: Fraction) -> int:
+    return (0x8000 | exact_rne_f16(-y)) if y < 0 else exact_rne_f16(y)
+
+
+def mp_gelu(x: Fraction) -> Fraction:
+    """GELU of an exact rational, evaluated with 80-digit arithmetic and
+    returned as the exact binary value of that result."""
+    import mpmath
+    with mpmath.workdps(80):
+        xm = mpmath.mpf(x.numerator) / x.denominator
+        g = xm * mpmath.ncdf(xm)
+        man, exp = int(g.man), int(g.exp)
+        sign = -1 if g < 0 else 1
+        v = Fraction(abs(man)) * (Fraction(2) ** exp)
+        return sign * v if g != 0 else Fraction(0)
+
+
+def test_gelu_textbook_values():
+    # standard normal distribution function at 1, 2, 3, -1 (normal tables, 15 digits)
+    for x, phi in ((1.0, 0.841344746068543), (2.0, 0.977249868051821), (3.0, 0.998650101968370),
+                   (-1.0, 0.158655253931457), (0.5, 0.691462461274013)):
+        assert abs(float(oracle.gelu(x)) - x * phi) <= 2e-15 * abs(x)
+    assert float(oracle.gelu(0.0)) == 0.0
+    assert float(oracle.gelu(12.0)) == 12.0          # Phi(12) rounds to 1 in double
+    assert float(oracle.gelu(-40.0)) == 0.0          # Phi(-40) underflows
+
+
+def test_gelu_against_library_normal_cdf():
+    from scipy.special import ndtr
+    x = np.linspace(-9.0, 9.0, 3601)
+    g = oracle.gelu(x)
+    ref = x * ndtr(x)
+    nz = np.abs(ref) > 1e-300
+    assert np.max(np.abs(g[nz] - ref[nz]) / np.abs(ref[nz])) < 1e-13
+
+
+def test_gelu_odd_part_is_identity():
+    # x * Phi(x) - (-x) * Phi(-x) = x * (Phi(x) + Phi(-x)) = x
+    x = np.random.default_rng(3).uniform(-8.0, 8.0, 5000)
+    d = oracle.gelu(x) - oracle.gelu(-x)
+    assert np.max(np.abs(d - x) / np.maximum(np.abs(x), 1e-300)) < 4e-16 * 8
+
+
+def _bias_gelu_exact(A, B, bias):
+    M, K = A.shape
+    _, N = B.shape
+    Af = [[exact_f16_value(int(A[i, k])) for k in range(K)] for i in range(M)]
+    Bf = [[exact_f16_value(int(B[k, j])) for j in range(N)] for k in range(K)]
+    bf = [exact_f16_value(int(bias[j])) for j in range(N)]
+    out = np.zeros((M, N), dtype=np.uint16)
+    pres = []
+    for i in range(M):
+        row = []
+        for j in range(N):
+            s = sum((Af[i][k] * Bf[k][j] for k in range(K)), Fraction(0)) + bf[j]
+            row.append(s)
+            out[i, j] = exact_rne_f16_signed(mp_gelu(s))
+        pres.append(row)
+    return out, pres
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 2), (7, 3, 5), (5, 17, 16), (16, 4, 17), (2, 9, 0)])
+def test_bias_gelu_brute_force_exact(M, N, K):
+    rng = np.random.default_rng(M * 7919 + N * 31 + K)
+    A = rand_f16_bits(rng, (M, K))
+    B = rand_f16_bits(rng, (K, N))
+    bias = rand_f16_bits(rng, (N,))
+    want, pres = _bias_gelu_exact(A, B, bias)
+    got, pre, absdot = oracle.gemm_bias_gelu_f16(A, B, bias, want_pre=True, want_absdot=True)
+    for i in range(M):
+        for j in range(N):
+            if got[i, j] == want[i, j]:
+                continue
+            # a flip is allowed only if an fp16 rounding boundary lies within the
+            # oracle's double-precision error: the sum's bound, scaled by
+            # GELU's slope (< 1.13), plus a few ulps of the double GELU
+            exact = pres[i][j]
+            bound = (Fraction(K + 1) * Fraction(1, 2 ** 53) * (Fraction(absdot[i, j]) + abs(exact)) * Fraction(113, 100)
+                     + Fraction(8, 2 ** 53) * abs(mp_gelu(exact)) + Fraction(1, 2 ** 1000))
+            g = mp_gelu(exact)
+            if exact_rne_f16_signed(g - bound) == exact_rne_f16_signed(g + bound):
+                pytest.fail(f"({i},{j}): oracle {got[i, j]:#06x} exact {want[i, j]:#06x}")
+    ii, jj = np.divmod(np.arange(M * N), N)
+    assert np.array_equal(oracle.gemm_bias_gelu_f16_points(A, B, bias, ii, jj), got.ravel())
+
+
+def test_bias_is_per_column():
+    # K = 0: every row of C is GELU(bias); A = I: C = GELU(B + bias) elementwise
+    bias = f16_bits([-3.0, -0.5, 0.0, 0.25, 1.0, 2.5, 7.0])
+    N = bias.size
+    A0 = np.zeros((4, 0), dtype=np.uint16)
+    B0 = np.zeros((0, N), dtype=np.uint16)
+    C = oracle.gemm_bias_gelu_f16(A0, B0, bias)
+    row = np.array([exact_rne_f16_signed(mp_gelu(exact_f16_value(int(b)))) for b in bias], dtype=np.uint16)
+    assert np.array_equal(C, np.tile(row, (4, 1)))
+    rng = np.random.default_rng(12)
+    K = 5
+    I = f16_bits(np.eye(K))
+    B = rand_f16_bits(rng, (K, N))
+    C = oracle.gemm_bias_gelu_f16(I, B, bias)
+    want = np.array([[exact_rne_f16_signed(mp_gelu(exact_f16_value(int(B[i, j])) + exact_f16_value(int(bias[j]))))
+                      for j in range(N)] for i in range(K)], dtype=np.uint16)
+    assert np.array_equal(C, want)
+
+
+def test_bias_gelu_zero_bias_and_sign_structure():
+    # with bias 0, GELU(s) - GELU(-s) = s links C(A) and C(-A) to the plain sum
+    a, b = workloads.make_inputs(6, 9, 40, dist="intsmall", seed=21)
+    A, B = workloads.as_u16(a), workloads.as_u16(b)
+    An = workloads.as_u16((-a).contiguous())
+    z = np.zeros(9, dtype=np.uint16)
+    gp, pre = oracle.gemm_bias_gelu_f16(A, B, z, want_pre=True)
+    gn = oracle.gemm_bias_gelu_f16(An, B, z)
+    s = a.numpy().astype(np.int64) @ b.numpy().astype(np.int64)
+    assert np.array_equal(pre, s.astype(np.float64))
+    vp = gp.view(np.float16).astype(np.float64)
+    vn = gn.view(np.float16).astype(np.float64)
+    # each fp16 result is within half an ulp of its value, so the identity holds to two half-ulps
+    ulp = lambda v: np.exp2(np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -14))) - 10)
+    assert np.all(np.abs((vp - vn) - s) <= 0.5 * ulp(vp) + 0.5 * ulp(vn) + 0.5 * ulp(s.astype(np.float64)))
+
+
+BIAS_MUTANTS = {
+    "bias_sign": ("const double pre = acc + oracle_f16_to_f64(bias[j]);",
+                  "const double pre = acc - oracle_f16_to_f64(bias[j]);"),
+    "bias_dropped": ("const double pre = acc + oracle_f16_to_f64(bias[j]);", "const double pre = acc;"),
+    "bias_by_row": ("C[i * N + j] = finish(acc[j], bias, j,", "C[i * N + j] = finish(acc[j], bias, i % (N > 0 ? N : 1),"),
+    "gelu_tanh_form": ("return x * (0.5 * erfc(-x / sqrt(2.0)));",
+                       "return 0.5 * x * (1.0 + tanh(0.7978845608028654 * (x + 0.044715 * x * x * x)));"),
+    "gelu_as_relu": ("return oracle_f64_to_f16_rne(oracle_gelu(pre));",
+                     "return oracle_f64_to_f16_rne(pre > 0.0 ? pre : 0.0);"),
+    "gelu_before_bias": ("const double pre = acc + oracle_f16_to_f64(bias[j]);",
+                         "const double pre = oracle_gelu(acc) + oracle_f16_to_f64(bias[j]) - oracle_gelu(0.0) * 0.0;"),
+}
+
+
+def _bias_pin_suite(mod) -> list[str]:
+    fails = []
+    for x, phi in ((1.0, 0.841344746068543), (2.0, 0.977249868051821), (-1.0, 0.158655253931457)):
+        if abs(float(mod.gelu(x)) - x * phi) > 2e-15 * abs(x):
+            fails.append("textbook")
+    for shape in ((3, 5, 2), (5, 17, 16), (2, 9, 0)):
+        M, N, K = shape
+        rng = np.random.default_rng(M * 7919 + N * 31 + K)
+        A = rand_f16_bits(rng, (M, K))
+        B = rand_f16_bits(rng, (K, N))
+        bias = rand_f16_bits(rng, (N,))
+        want, _ = _bias_gelu_exact(A, B, bias)
+        if not np.array_equal(mod.gemm_bias_gelu_f16(A, B, bias), want):
+            fails.append(f"brute{shape}")
+    return fails
+
+
+def test_bias_pins_pass_on_real_oracle():
+    assert _bias_pin_suite(oracle) == []
+
+
+@pytest.mark.parametrize("mutant", sorted(BIAS_MUTANTS))
+def test_planted_bias_gelu_mistake_is_caught(mutant, tmp_path):
+    import importlib.util
+    src_dir = os.path.join(os.path.dirname(HERE), "oracle")
+    old, new = BIAS_MUTANTS[mutant]
+    text = open(os.path.join(src_dir, "gemm_relu_oracle.c")).read()
+    assert text.count(old) >= 1, f"mutation anchor for {mutant} not found"
+    dst = tmp_path / "oracle_mut"
+    dst.mkdir()
+    (dst / "gemm_relu_oracle.c").write_text(text.replace(old, new, 1))
+    shutil.copy(os.path.join(src_dir, "__init__.py"), dst / "__init__.py")
+    spec = importlib.util.spec_from_file_location(f"oracle_bmut_{mutant}", dst / "__init__.py")
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert _bias_pin_suite(mod) != [], f"planted mistake {mutant} went unnoticed"
