@@ -82,7 +82,7 @@ def measured_traffic(workload: str, tile: str) -> float | None:
 ROTATE_BYTES = 768 << 20  # well above the 256 MB last-level (MALL) cache
 
 
-def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0):
+def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0, epilogue: str = "relu"):
     """Times `steps` back-to-back launches on one stream, bracketed by two
     events on that stream. Successive launches cycle through R copies of
     (A, B) with R * (|A| + |B|) >= 768 MiB (at most 8), so the inputs of a
@@ -108,12 +108,22 @@ def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0):
     c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
     stream = torch.cuda.Stream()
     opts = gr.make_opts(tile)
-    args = [(w.M, w.N, w.K, ads[i].data_ptr(), bds[i].data_ptr(), c.data_ptr(), stream.cuda_stream, opts)
-            for i in range(rot)]
+    if epilogue == "bias_gelu":
+        # the fused bias + GELU epilogue: a bias on the scale of the sums
+        gen = torch.Generator(device="cpu")
+        gen.manual_seed(w.seed + 1)
+        bias = (torch.randn(w.N, generator=gen) * (w.K ** 0.5) * w.scale * w.scale).half().cuda()
+        call = gr.gemm_bias_gelu_f16_ex
+        args = [(w.M, w.N, w.K, ads[i].data_ptr(), bds[i].data_ptr(), bias.data_ptr(), c.data_ptr(),
+                 stream.cuda_stream, opts) for i in range(rot)]
+    else:
+        call = gr.gemm_relu_f16_ex
+        args = [(w.M, w.N, w.K, ads[i].data_ptr(), bds[i].data_ptr(), c.data_ptr(), stream.cuda_stream, opts)
+                for i in range(rot)]
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for i in range(warmup):
-            st = gr.gemm_relu_f16_ex(*args[i % rot])
+            st = call(*args[i % rot])
             if st != gr.OK:
                 raise RuntimeError(gr.strerror(st))
         torch.cuda.synchronize()
@@ -123,7 +133,7 @@ def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0):
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph, stream=stream):
                 for i in range(graph_batch):
-                    gr.gemm_relu_f16_ex(*args[i % rot])
+                    call(*args[i % rot])
             graph.replay()
             torch.cuda.synchronize()
         # the whole timed region between two events on the launch stream
@@ -135,7 +145,7 @@ def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0):
                 graph.replay()
         else:
             for i in range(steps):
-                gr.gemm_relu_f16_ex(*args[i % rot])
+                call(*args[i % rot])
         t1.record(stream)
         torch.cuda.synchronize()
         total_ms = t0.elapsed_time(t1)
@@ -144,7 +154,7 @@ def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nper)]
         for i, (e0, e1) in enumerate(evs):
             e0.record(stream)
-            gr.gemm_relu_f16_ex(*args[i % rot])
+            call(*args[i % rot])
             e1.record(stream)
         torch.cuda.synchronize()
     per = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
@@ -152,7 +162,7 @@ def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0):
     return {"total_ms": total_ms, "steps": steps, "ms_per_step": total_ms / steps,
             "launch_ms_mean": float(per.mean()), "launch_ms_median": float(np.median(per)),
             "launch_ms_min": float(per.min()), "tile": gr.tile_name(tile_id) if tile_id >= 0 else "generic",
-            "rotation": rot, "graph_batch": graph_batch, "c": c, "a": a, "b": b}
+            "rotation": rot, "graph_batch": graph_batch, "epilogue": epilogue, "c": c, "a": a, "b": b}
 
 
 def cpu_baseline(w, gpu_c, target_s: float = 12.0):
@@ -204,7 +214,8 @@ def result_line(w, r, steps, warmup, cpu=None):
             "scaling": "weak", "vs_baseline": None, "dtype": "f16", "accum_dtype": "f32", "data": "synthetic",
             "pct_of_fp16_peak": round(100 * value / PEAK_FP16_TFLOPS, 2),
             "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dist": w.dist,
-                       "scale": w.scale, "seed": w.seed, "tile": r["tile"], "input_copies_rotated": r["rotation"],
+                       "scale": w.scale, "seed": w.seed, "tile": r["tile"], "epilogue": r["epilogue"],
+                       "input_copies_rotated": r["rotation"],
                        "parallelism": "single GPU"},
             "roofline": roof,
             "kernel_ms_timed_region_mean": round(r["ms_per_step"], 5),
@@ -228,6 +239,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--all", action="store_true", help="also time every workload (lines on stderr)")
+    ap.add_argument("--epilogue", choices=("relu", "bias_gelu"), default="relu",
+                    help="relu: C = ReLU(A @ B) (the headline); bias_gelu: C = GELU(A @ B + bias)")
     ap.add_argument("--graph", type=int, default=50, metavar="G",
                     help="capture G launches per HIP graph and replay it (0: launch one by one from the host)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -259,18 +272,18 @@ def main(argv=None) -> int:
     gr.load()
 
     w = workloads.BY_NAME[args.workload]
-    r = time_gpu(w, args.steps, args.warmup, args.tile, args.graph)
+    r = time_gpu(w, args.steps, args.warmup, args.tile, args.graph, args.epilogue)
     print(f"[bench] {w.name}: {r['ms_per_step'] * 1e3:.2f} us/step (graph batch {r['graph_batch']}), "
           f"single launches {r['launch_ms_mean'] * 1e3:.2f} us, tile {r['tile']}", file=sys.stderr, flush=True)
     if args.all:
         for ow in workloads.ALL:
             if ow is w:
                 continue
-            orr = time_gpu(ow, max(args.steps // 4, 50), max(args.warmup // 4, 10), None, args.graph)
+            orr = time_gpu(ow, max(args.steps // 4, 50), max(args.warmup // 4, 10), None, args.graph, args.epilogue)
             print(json.dumps(result_line(ow, orr, max(args.steps // 4, 50), max(args.warmup // 4, 10))),
                   file=sys.stderr, flush=True)
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.epilogue == "relu":
         cpu = cpu_baseline(w, r, args.cpu_seconds)
     print(json.dumps(result_line(w, r, args.steps, args.warmup, cpu)), flush=True)
     return 0

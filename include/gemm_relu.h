@@ -1,5 +1,6 @@
 /*
- * gemm_relu.h -- C ABI of the MI355X (gfx950) fp16 GEMM with a fused ReLU.
+ * gemm_relu.h -- C ABI of the MI355X (gfx950) fp16 GEMM with a fused ReLU
+ * (and the same GEMM with a fused bias + GELU epilogue).
  *
  * Operation (the GEMM + ReLU example of "Writing high-performance kernels in
  * TileLang", section "Escribamos un GEMM"): for fp16 matrices A (M x K) and
@@ -26,6 +27,17 @@
  * on `stream` and returns without waiting. Faults during execution surface at
  * the caller's next synchronisation of that stream. Calls on different streams
  * may run concurrently.
+ *
+ * Workspace: for few rows (M <= 64) the K dimension is split across
+ * workgroups, whose fp32 partial sums meet in a library-owned workspace
+ * (partials plus one counter per output tile). The library allocates it with
+ * hipMalloc on the first such call for a (device, stream) pair, clears its
+ * counters with an asynchronous memset on that stream, keeps it until the
+ * process ends, and grows it (after synchronising that stream) when a later
+ * call needs more. Each launch leaves the counters at zero, so calls on one
+ * stream reuse it in order; calls on different streams use different
+ * workspaces. Two host threads enqueueing on the same stream at the same
+ * time race on the workspace. Failure to allocate gives GEMM_RELU_ENOMEM.
  *
  * Errors: every entry point returns a gemm_relu_status. All argument checks
  * happen before any HIP runtime call, so a rejected call has no side effects.
@@ -88,6 +100,33 @@ int gemm_relu_f16(int64_t M, int64_t N, int64_t K,
 int gemm_relu_f16_ex(int64_t M, int64_t N, int64_t K,
                      const void* A, const void* B, void* C, void* stream,
                      const gemm_relu_opts* opts);
+
+/*
+ * C = GELU(A @ B + bias) in fp16: the fused epilogue of "TileLang simplifica
+ * la creación de kernels GPU de alto rendimiento" (section "Fusionar
+ * operaciones para reducir viajes a memoria"), where the bias addition and
+ * the GELU run on the accumulator in registers and C is written once:
+ *
+ *     C[i][j] = fp16( GELU( sum_k A[i][k] * B[k][j] + bias[j] ) )
+ *
+ * with GELU(x) = x * Phi(x), Phi the standard normal distribution function
+ * (the definition; no tanh approximation). The products are accumulated in
+ * fp32, the bias is added in fp32, GELU is evaluated in fp32 and the result
+ * rounded once to fp16, to nearest even.
+ *   bias : device pointer to N fp16 values, one per column of C (read only;
+ *          may be NULL only if N == 0; must not overlap C)
+ * All other arguments, the layout, ownership, execution and errors are those
+ * of gemm_relu_f16 / gemm_relu_f16_ex, with these additions: a NULL bias
+ * with N > 0 or a bias overlapping C gives GEMM_RELU_EINVAL, an odd bias
+ * address GEMM_RELU_EUNSUPPORTED.
+ */
+int gemm_bias_gelu_f16(int64_t M, int64_t N, int64_t K,
+                       const void* A, const void* B, const void* bias, void* C, void* stream);
+
+/* Same as gemm_bias_gelu_f16; opts (may be NULL) pins the tile and block order. */
+int gemm_bias_gelu_f16_ex(int64_t M, int64_t N, int64_t K,
+                          const void* A, const void* B, const void* bias, void* C, void* stream,
+                          const gemm_relu_opts* opts);
 
 /* A static, human-readable message for a status code. */
 const char* gemm_relu_strerror(int status);

@@ -21,12 +21,13 @@ HEADER = os.path.join(ROOT, "include", "gemm_relu.h")
 def declared_functions() -> list[str]:
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gemm_relu_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gemm_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert "gemm_relu_f16" in names and "gemm_relu_f16_ex" in names
+    assert "gemm_bias_gelu_f16" in names and "gemm_bias_gelu_f16_ex" in names
     assert set(names) == set(gr.EXPORTED)
 
 
@@ -112,6 +113,16 @@ def test_bad_opts_rejected():
     o = gr.make_opts()
     o.reserved[2] = 1
     assert gr.gemm_relu_f16_ex(4, 4, 4, FAKE, FAKE * 2, FAKE * 3, 0, o) == gr.EINVAL
+
+
+def test_bias_gelu_arguments_rejected():
+    # no bias with columns to write, an odd bias address, a bias overlapping C
+    assert gr.gemm_bias_gelu_f16(4, 4, 4, FAKE, FAKE * 2, 0, FAKE * 3) == gr.EINVAL
+    assert gr.gemm_bias_gelu_f16(4, 4, 4, FAKE, FAKE * 2, FAKE * 4 + 1, FAKE * 3) == gr.EUNSUPPORTED
+    assert gr.gemm_bias_gelu_f16(4, 4, 4, FAKE, FAKE * 2, FAKE * 3 + 8, FAKE * 3) == gr.EINVAL
+    assert gr.gemm_bias_gelu_f16(-1, 4, 4, FAKE, FAKE * 2, FAKE * 4, FAKE * 3) == gr.EINVAL
+    # nothing to write: a no-op without touching the device
+    assert gr.gemm_bias_gelu_f16(0, 5, 5, 0, FAKE, FAKE * 4, 0) == gr.OK
 
 
 def test_empty_output_is_a_no_op():

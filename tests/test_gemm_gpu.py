@@ -192,6 +192,83 @@ def test_splitk_two_streams_and_shapes_interleaved():
 
 
 # ---------------------------------------------------------------------------
+# the fused bias + GELU epilogue: C = GELU(A @ B + bias)
+# ---------------------------------------------------------------------------
+
+def make_bias(N, seed, scale=1.0):
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    return (torch.randn(N, generator=gen) * scale).to(torch.float16)
+
+
+def run_gelu(a_cpu, b_cpu, bias_cpu, **kw) -> np.ndarray:
+    c = gr.gemm_bias_gelu(a_cpu.cuda(), b_cpu.cuda(), bias_cpu.cuda(), **kw)
+    torch.cuda.synchronize()
+    return workloads.as_u16(c.cpu())
+
+
+@pytest.mark.parametrize("w", [workloads.SQUARE_256, workloads.SQUARE_1024, workloads.RAGGED,
+                               workloads.SKINNY], ids=lambda w: w.name)
+def test_bias_gelu_workload_parity(w):
+    say(f"[gelu] {w.name} tile={gr.select_tile(w.M, w.N, w.K)}")
+    a, b = workloads.workload_inputs(w)
+    # bias on the scale of the sums, so both terms matter
+    scale = float(np.sqrt(w.K)) * w.scale * w.scale
+    bias = make_bias(w.N, seed=w.N, scale=scale)
+    A, B, BI = workloads.as_u16(a), workloads.as_u16(b), workloads.as_u16(bias)
+    want, absdot = oracle.gemm_bias_gelu_f16(A, B, BI, want_absdot=True)
+    st = parity.check_gelu(run_gelu(a, b, bias), want, absdot=absdot, K=w.K,
+                           bias_abs=np.abs(parity.f16_values(BI))[None, :], label=w.name)
+    say(f"  {st}")
+
+
+def test_bias_gelu_4096_sampled():
+    w = workloads.SQUARE_4096
+    say(f"[gelu] {w.name} sampled, tile={gr.select_tile(w.M, w.N, w.K)}")
+    a, b = workloads.workload_inputs(w)
+    bias = make_bias(w.N, seed=7, scale=64.0)
+    A, B, BI = workloads.as_u16(a), workloads.as_u16(b), workloads.as_u16(bias)
+    got = run_gelu(a, b, bias)
+    bias_abs = np.abs(parity.f16_values(BI))
+    for r0, r1 in ((0, 4), (2046, 2050), (4092, 4096)):
+        want, absdot = oracle.gemm_bias_gelu_f16(A, B, BI, rows=(r0, r1), want_absdot=True)
+        parity.check_gelu(got[r0:r1], want, absdot=absdot, K=w.K, bias_abs=bias_abs[None, :], label=f"rows {r0}:{r1}")
+    rng = np.random.default_rng(77)
+    ii = rng.integers(0, w.M, 2048)
+    jj = rng.integers(0, w.N, 2048)
+    want, absdot = oracle.gemm_bias_gelu_f16_points(A, B, BI, ii, jj, want_absdot=True)
+    parity.check_gelu(got[ii, jj], want, absdot=absdot, K=w.K, bias_abs=bias_abs[jj], label="points")
+
+
+@pytest.mark.parametrize("tile", range(gr.tile_count()))
+def test_bias_gelu_every_tile_ragged(tile):
+    M, N, K = 200, 264, 136
+    say(f"[gelu tile] {gr.tile_name(tile)} M={M} N={N} K={K}")
+    a, b = workloads.make_inputs(M, N, K, dist="uniform", scale=1.0, seed=31)
+    bias = make_bias(N, seed=32, scale=3.0)
+    A, B, BI = workloads.as_u16(a), workloads.as_u16(b), workloads.as_u16(bias)
+    want, absdot = oracle.gemm_bias_gelu_f16(A, B, BI, want_absdot=True)
+    parity.check_gelu(run_gelu(a, b, bias, tile=tile), want, absdot=absdot, K=K,
+                      bias_abs=np.abs(parity.f16_values(BI))[None, :], label=f"tile {tile}")
+
+
+@pytest.mark.parametrize("M,N,K", [(33, 47, 129), (16, 8192, 1024), (300, 264, 64), (1, 8, 8), (77, 40, 24)])
+def test_bias_gelu_integer_sums(M, N, K):
+    # integer inputs make the fp32 sum exact; only GELU's fp32 evaluation can
+    # move a result, by at most one fp16 unit at a rounding boundary
+    a, b = workloads.make_inputs(M, N, K, dist="intsmall", seed=M + 3 * N + K)
+    bias = make_bias(N, seed=N, scale=2.0)
+    A, B, BI = workloads.as_u16(a), workloads.as_u16(b), workloads.as_u16(bias)
+    want = oracle.gemm_bias_gelu_f16(A, B, BI)
+    got = run_gelu(a, b, bias)
+    diff = np.abs(got.astype(np.int32) - want.astype(np.int32))
+    sign_zero = ((got | want) & 0x7FFF) == 0  # +0 and -0
+    diff[sign_zero] = 0
+    assert diff.max() <= 1, f"max difference {diff.max()} fp16 units"
+    assert (diff != 0).mean() < 0.01, f"{(diff != 0).sum()} of {diff.size} differ by one unit"
+
+
+# ---------------------------------------------------------------------------
 # memory safety: NaN guard bands after the inputs, sentinels around C
 # ---------------------------------------------------------------------------
 

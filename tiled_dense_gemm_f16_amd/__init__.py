@@ -1,4 +1,5 @@
-"""MI355X (gfx950) fp16 GEMM with a fused ReLU: C = ReLU(A @ B).
+"""MI355X (gfx950) fp16 GEMM with a fused ReLU: C = ReLU(A @ B) (and with a
+fused bias + GELU epilogue: C = GELU(A @ B + bias)).
 
 The computation is the GEMM + ReLU example of "Writing high-performance
 kernels in TileLang" (section "Escribamos un GEMM"), implemented as
@@ -7,6 +8,6 @@ This package is the thin Python binding of that ABI.
 """
 from ._binding import (  # noqa: F401
     EHIP, EINVAL, ENOMEM, EUNSUPPORTED, EXPORTED, LIB_PATH, OK, ORDER_DEFAULT, ORDER_ROW_MAJOR,
-    TILE_AUTO, GemmReluError, Opts, gemm_relu, gemm_relu_f16, gemm_relu_f16_ex, load, make_opts,
-    select_tile, strerror, tile_count, tile_name,
+    TILE_AUTO, GemmReluError, Opts, gemm_bias_gelu, gemm_bias_gelu_f16, gemm_bias_gelu_f16_ex, gemm_relu,
+    gemm_relu_f16, gemm_relu_f16_ex, load, make_opts, select_tile, strerror, tile_count, tile_name,
 )

@@ -32,8 +32,8 @@ class Opts(ctypes.Structure):
 _lock = threading.Lock()
 _lib = None
 
-EXPORTED = ("gemm_relu_f16", "gemm_relu_f16_ex", "gemm_relu_strerror", "gemm_relu_tile_count",
-            "gemm_relu_tile_name", "gemm_relu_select_tile")
+EXPORTED = ("gemm_relu_f16", "gemm_relu_f16_ex", "gemm_bias_gelu_f16", "gemm_bias_gelu_f16_ex",
+            "gemm_relu_strerror", "gemm_relu_tile_count", "gemm_relu_tile_name", "gemm_relu_select_tile")
 
 
 def load():
@@ -51,6 +51,10 @@ def load():
         lib.gemm_relu_f16.restype = i32
         lib.gemm_relu_f16_ex.argtypes = [i64, i64, i64, p, p, p, p, ctypes.POINTER(Opts)]
         lib.gemm_relu_f16_ex.restype = i32
+        lib.gemm_bias_gelu_f16.argtypes = [i64, i64, i64, p, p, p, p, p]
+        lib.gemm_bias_gelu_f16.restype = i32
+        lib.gemm_bias_gelu_f16_ex.argtypes = [i64, i64, i64, p, p, p, p, p, ctypes.POINTER(Opts)]
+        lib.gemm_bias_gelu_f16_ex.restype = i32
         lib.gemm_relu_strerror.argtypes = [i32]
         lib.gemm_relu_strerror.restype = ctypes.c_char_p
         lib.gemm_relu_tile_count.argtypes = []
@@ -92,6 +96,18 @@ def gemm_relu_f16_ex(M: int, N: int, K: int, A: int, B: int, C: int, stream: int
                                    ctypes.byref(opts) if opts is not None else None)
 
 
+def gemm_bias_gelu_f16(M: int, N: int, K: int, A: int, B: int, bias: int, C: int, stream: int = 0) -> int:
+    """Raw C-ABI call of C = GELU(A @ B + bias) with integer device pointers; returns the status code."""
+    return load().gemm_bias_gelu_f16(M, N, K, A or None, B or None, bias or None, C or None, stream or None)
+
+
+def gemm_bias_gelu_f16_ex(M: int, N: int, K: int, A: int, B: int, bias: int, C: int, stream: int = 0,
+                          opts: Opts | None = None) -> int:
+    """Raw C-ABI call of C = GELU(A @ B + bias) with launch options; returns the status code."""
+    return load().gemm_bias_gelu_f16_ex(M, N, K, A or None, B or None, bias or None, C or None, stream or None,
+                                        ctypes.byref(opts) if opts is not None else None)
+
+
 def tile_count() -> int:
     return int(load().gemm_relu_tile_count())
 
@@ -104,12 +120,7 @@ def select_tile(M: int, N: int, K: int, A: int = 0, B: int = 0, C: int = 0) -> i
     return int(load().gemm_relu_select_tile(M, N, K, A or None, B or None, C or None))
 
 
-def gemm_relu(a, b, out=None, *, tile: int | None = None, block_order: int = ORDER_DEFAULT,
-              group_m: int = 0, stream=None):
-    """C = ReLU(a @ b) for fp16 CUDA(HIP) tensors a[M,K], b[K,N]; returns out[M,N].
-
-    Enqueued on torch's current stream (or ``stream``); does not synchronise.
-    """
+def _check_operands(a, b, out):
     import torch
 
     if a.dtype != torch.float16 or b.dtype != torch.float16:
@@ -129,9 +140,41 @@ def gemm_relu(a, b, out=None, *, tile: int | None = None, block_order: int = ORD
             raise ValueError("out must be float16 [M, N] on the inputs' device")
         if not out.is_contiguous():
             raise ValueError("out must be contiguous")
+    return M, N, K, out
+
+
+def gemm_relu(a, b, out=None, *, tile: int | None = None, block_order: int = ORDER_DEFAULT,
+              group_m: int = 0, stream=None):
+    """C = ReLU(a @ b) for fp16 CUDA(HIP) tensors a[M,K], b[K,N]; returns out[M,N].
+
+    Enqueued on torch's current stream (or ``stream``); does not synchronise.
+    """
+    import torch
+
+    M, N, K, out = _check_operands(a, b, out)
     s = stream if stream is not None else torch.cuda.current_stream(a.device)
     opts = make_opts(tile, block_order, group_m)
     with torch.cuda.device(a.device):
-        _check(gemm_relu_f16_ex(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(),
-                                s.cuda_stream, opts))
+        _check(gemm_relu_f16_ex(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), s.cuda_stream, opts))
+    return out
+
+
+def gemm_bias_gelu(a, b, bias, out=None, *, tile: int | None = None, block_order: int = ORDER_DEFAULT,
+                   group_m: int = 0, stream=None):
+    """C = GELU(a @ b + bias) for fp16 tensors a[M,K], b[K,N], bias[N]; returns out[M,N].
+
+    Enqueued on torch's current stream (or ``stream``); does not synchronise.
+    """
+    import torch
+
+    M, N, K, out = _check_operands(a, b, out)
+    if bias.dtype != torch.float16 or bias.dim() != 1 or bias.shape[0] != N:
+        raise ValueError(f"bias must be float16 [{N}]")
+    if not bias.is_cuda or bias.device != a.device or not bias.is_contiguous():
+        raise ValueError("bias must be contiguous on the inputs' device")
+    s = stream if stream is not None else torch.cuda.current_stream(a.device)
+    opts = make_opts(tile, block_order, group_m)
+    with torch.cuda.device(a.device):
+        _check(gemm_bias_gelu_f16_ex(M, N, K, a.data_ptr(), b.data_ptr(), bias.data_ptr(), out.data_ptr(),
+                                     s.cuda_stream, opts))
     return out

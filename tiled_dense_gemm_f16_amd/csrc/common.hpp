@@ -37,6 +37,9 @@ struct Args {
     int tiles_m, tiles_n;
     int group_m;
     int order;  // GEMM_RELU_ORDER_*
+    // epilogue: kActRelu, or kActBiasGelu with bias[N] (fp16, one per column)
+    int act;
+    const uint16_t* bias;
     // split-K kernel only
     float* partial;      // [splits][M][N] fp32 partial sums (splits > 1)
     uint32_t* counters;  // one per column tile, zero between launches (splits > 1)
@@ -110,18 +113,115 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
     }
 }
 
-// ReLU on an fp32 accumulator and the conversion to fp16, round to nearest
-// even (v_cvt_f16_f32 under the default rounding mode), as a bit pattern.
-__device__ __forceinline__ uint32_t relu_pack2(float lo, float hi)
+// Epilogues. ReLU is the GEMM + ReLU example's ("Writing high-performance
+// kernels in TileLang", section "Escribamos un GEMM"); bias + GELU is the
+// fused epilogue of "TileLang simplifica la creación de kernels GPU de alto
+// rendimiento" (section "Fusionar operaciones para reducir viajes a
+// memoria"): v + bias[n], then GELU(x) = x * Phi(x), Phi the standard normal
+// distribution function, all in fp32.
+constexpr int kActRelu = 0;
+constexpr int kActBiasGelu = 1;
+
+__device__ __forceinline__ float relu(float x) { return fmaxf(x, 0.0f); }
+
+// erfc(z) for z >= 0 with a fractional error below 1.2e-7 at every z: the
+// Chebyshev-fitted approximation of Numerical Recipes (Press, Teukolsky,
+// Vetterling, Flannery; section 6.2, "erfcc"),
+//   erfc(z) ~ t * exp(-z^2 + P(t)),  t = 1 / (1 + z/2),
+// P a degree-9 polynomial, evaluated here by Horner's rule: one reciprocal,
+// nine FMAs and one exp, against about fifty instructions for the library's
+// erfcf. In fp32 the result stays within a few parts in 1e6 of erfc, far
+// below the fp16 output's resolution.
+__device__ __forceinline__ float erfc_nonneg(float z)
 {
-    const _Float16 a = (_Float16)fmaxf(lo, 0.0f);
-    const _Float16 b = (_Float16)fmaxf(hi, 0.0f);
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
+    float s = 0.17087277f;
+    s = fmaf(s, t, -0.82215223f);
+    s = fmaf(s, t, 1.48851587f);
+    s = fmaf(s, t, -1.13520398f);
+    s = fmaf(s, t, 0.27886807f);
+    s = fmaf(s, t, -0.18628806f);
+    s = fmaf(s, t, 0.09678418f);
+    s = fmaf(s, t, 0.37409196f);
+    s = fmaf(s, t, 1.00002368f);
+    s = fmaf(s, t, -1.26551223f);
+    return t * __expf(fmaf(-z, z, s));
 }
 
-__device__ __forceinline__ uint16_t relu_f16(float x)
+// GELU(x) = x * Phi(x). With q = Phi(-|x|) = erfc(|x| / sqrt 2) / 2 (always in
+// (0, 1/2], no cancellation): x * q for x < 0, x - x * q for x >= 0.
+__device__ __forceinline__ float gelu(float x)
 {
-    return __builtin_bit_cast(uint16_t, (_Float16)fmaxf(x, 0.0f));
+    const float q = 0.5f * erfc_nonneg(fabsf(x) * 0.70710678118654752f);
+    return x < 0.0f ? x * q : fmaf(-x, q, x);
+}
+
+// bias of column n (zero past N, where nothing is stored)
+__device__ __forceinline__ float bias_at(const Args& p, int n)
+{
+    return n < p.N ? (float)__builtin_bit_cast(_Float16, p.bias[n]) : 0.0f;
+}
+
+// Two consecutive outputs (columns n, n+1) through the epilogue and the
+// conversion to fp16, round to nearest even (v_cvt_f16_f32 under the default
+// rounding mode), as a packed bit pattern.
+template <int ACT>
+__device__ __forceinline__ uint32_t epi_pack2(const Args& p, float lo, float hi, int n)
+{
+    float a, b;
+    if constexpr (ACT == kActBiasGelu) {
+        a = gelu(lo + bias_at(p, n));
+        b = gelu(hi + bias_at(p, n + 1));
+    } else {
+        a = relu(lo);
+        b = relu(hi);
+    }
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+
+// Bias of columns n .. n+3 (n % 4 == 0, N % 8 == 0: the vector paths), one
+// 8-byte load; columns past N read zeros.
+__device__ __forceinline__ f32x4 bias4(const Args& p, int n)
+{
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(p.bias, (uint64_t)p.N * 2);
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, n < p.N ? n * 2 : (int)kOOB, 0, 0);
+    f32x4 b;
+    b[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] & 0xFFFF));
+    b[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] >> 16));
+    b[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] & 0xFFFF));
+    b[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] >> 16));
+    return b;
+}
+
+// Two consecutive outputs with their biases already loaded.
+template <int ACT>
+__device__ __forceinline__ uint32_t epi_pack2b(float lo, float hi, float blo, float bhi)
+{
+    float a, b;
+    if constexpr (ACT == kActBiasGelu) {
+        a = gelu(lo + blo);
+        b = gelu(hi + bhi);
+    } else {
+        a = relu(lo);
+        b = relu(hi);
+    }
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+
+template <int ACT>
+__device__ __forceinline__ uint16_t epi_f16(const Args& p, float x, int n)
+{
+    const float y = (ACT == kActBiasGelu) ? gelu(x + bias_at(p, n)) : relu(x);
+    return __builtin_bit_cast(uint16_t, (_Float16)y);
+}
+
+// Runs body.template operator()<ACT>() with the epilogue the call asked for:
+// one branch around the whole epilogue, none in the main loop.
+template <class F>
+__device__ __forceinline__ void with_epilogue(const Args& p, F&& body)
+{
+    if (p.act == kActBiasGelu) body.template operator()<kActBiasGelu>();
+    else body.template operator()<kActRelu>();
 }
 
 }  // namespace gemm_relu

@@ -236,6 +236,16 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, const void* B, cons
     return GEMM_RELU_OK;
 }
 
+// The bias of the bias + GELU epilogue: N fp16 values, 2-byte aligned, not
+// overlapping C.
+int validate_bias(int64_t M, int64_t N, const void* bias, const void* C)
+{
+    if (N > 0 && !bias) return GEMM_RELU_EINVAL;
+    if (((uintptr_t)bias & 1u) != 0) return GEMM_RELU_EUNSUPPORTED;
+    if (M > 0 && overlaps(C, 2 * M * N, bias, 2 * N)) return GEMM_RELU_EINVAL;
+    return GEMM_RELU_OK;
+}
+
 // gfx950 check, once per device id.
 constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
@@ -253,6 +263,63 @@ int check_device(int& dev)
         g_dev_ok[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
     }
     return g_dev_ok[dev] == 1 ? GEMM_RELU_OK : GEMM_RELU_EUNSUPPORTED;
+}
+
+// Validated call -> tile choice, split-K workspace, launch. `act` selects the
+// epilogue (kActRelu, or kActBiasGelu with `bias`).
+int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, void* stream,
+        const gemm_relu_opts* opts, int act, const void* bias)
+{
+    int rc = validate(M, N, K, A, B, C, opts);
+    if (rc != GEMM_RELU_OK) return rc;
+    if (act == gemm_relu::kActBiasGelu) {
+        rc = validate_bias(M, N, bias, C);
+        if (rc != GEMM_RELU_OK) return rc;
+    }
+    if (M == 0 || N == 0) return GEMM_RELU_OK;
+    int dev = 0;
+    rc = check_device(dev);
+    if (rc != GEMM_RELU_OK) return rc;
+
+    const bool vec = fast_path_ok(N, K, A, B, C);
+    const int tile =
+        (opts && opts->tile != GEMM_RELU_TILE_AUTO) ? opts->tile : (vec ? choose_tile(M, N, K) : kGenericTile);
+    // the split-K tiles have no element-wise instance: unaligned shapes take
+    // the generic tile
+    const TileEntry& te = (!vec && kTiles[tile].splitk) ? kTiles[kGenericTile] : kTiles[tile];
+    const bool splitk = vec && te.splitk;
+    if (splitk && !splitk_ok(M, K)) return GEMM_RELU_EUNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Args a;
+    a.A = static_cast<const uint16_t*>(A);
+    a.B = static_cast<const uint16_t*>(B);
+    a.C = static_cast<uint16_t*>(C);
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.tiles_m = (int)((M + te.bm - 1) / te.bm);
+    a.tiles_n = (int)((N + te.bn - 1) / te.bn);
+    a.group_m = (opts && opts->group_m > 0) ? opts->group_m : te.default_group_m;
+    a.order = opts ? opts->block_order : GEMM_RELU_ORDER_DEFAULT;
+    a.act = act;
+    a.bias = static_cast<const uint16_t*>(bias);
+    a.partial = nullptr;
+    a.counters = nullptr;
+    a.splits = 1;
+    a.kc = (int)(K < 1 ? 1 : K);
+    const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+    if (tiles > INT32_MAX) return GEMM_RELU_EUNSUPPORTED;
+    if (splitk) {
+        choose_splits(K, tiles, a.splits, a.kc);
+        if (tiles * a.splits > INT32_MAX) return GEMM_RELU_EUNSUPPORTED;
+        if (a.splits > 1) {
+            rc = get_workspace(dev, s, (size_t)tiles, (size_t)a.splits * (size_t)M * (size_t)N * 4, &a.counters,
+                               &a.partial);
+            if (rc != GEMM_RELU_OK) return rc;
+        }
+    }
+    const hipError_t e = (vec ? te.vec : te.generic)(a, s);
+    return e == hipSuccess ? GEMM_RELU_OK : GEMM_RELU_EHIP;
 }
 
 }  // namespace
@@ -287,55 +354,24 @@ int gemm_relu_select_tile(int64_t M, int64_t N, int64_t K, const void* A, const 
 int gemm_relu_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C,
                      void* stream, const gemm_relu_opts* opts)
 {
-    int rc = validate(M, N, K, A, B, C, opts);
-    if (rc != GEMM_RELU_OK) return rc;
-    if (M == 0 || N == 0) return GEMM_RELU_OK;
-    int dev = 0;
-    rc = check_device(dev);
-    if (rc != GEMM_RELU_OK) return rc;
-
-    const bool vec = fast_path_ok(N, K, A, B, C);
-    const int tile =
-        (opts && opts->tile != GEMM_RELU_TILE_AUTO) ? opts->tile : (vec ? choose_tile(M, N, K) : kGenericTile);
-    // the split-K tiles have no element-wise instance: unaligned shapes take
-    // the generic tile
-    const TileEntry& te = (!vec && kTiles[tile].splitk) ? kTiles[kGenericTile] : kTiles[tile];
-    const bool splitk = vec && te.splitk;
-    if (splitk && !splitk_ok(M, K)) return GEMM_RELU_EUNSUPPORTED;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    Args a;
-    a.A = static_cast<const uint16_t*>(A);
-    a.B = static_cast<const uint16_t*>(B);
-    a.C = static_cast<uint16_t*>(C);
-    a.M = (int)M;
-    a.N = (int)N;
-    a.K = (int)K;
-    a.tiles_m = (int)((M + te.bm - 1) / te.bm);
-    a.tiles_n = (int)((N + te.bn - 1) / te.bn);
-    a.group_m = (opts && opts->group_m > 0) ? opts->group_m : te.default_group_m;
-    a.order = opts ? opts->block_order : GEMM_RELU_ORDER_DEFAULT;
-    a.partial = nullptr;
-    a.counters = nullptr;
-    a.splits = 1;
-    a.kc = (int)(K < 1 ? 1 : K);
-    const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
-    if (tiles > INT32_MAX) return GEMM_RELU_EUNSUPPORTED;
-    if (splitk) {
-        choose_splits(K, tiles, a.splits, a.kc);
-        if (tiles * a.splits > INT32_MAX) return GEMM_RELU_EUNSUPPORTED;
-        if (a.splits > 1) {
-            rc = get_workspace(dev, s, (size_t)tiles, (size_t)a.splits * (size_t)M * (size_t)N * 4, &a.counters,
-                               &a.partial);
-            if (rc != GEMM_RELU_OK) return rc;
-        }
-    }
-    const hipError_t e = (vec ? te.vec : te.generic)(a, s);
-    return e == hipSuccess ? GEMM_RELU_OK : GEMM_RELU_EHIP;
+    return run(M, N, K, A, B, C, stream, opts, gemm_relu::kActRelu, nullptr);
 }
 
 int gemm_relu_f16(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, void* stream)
 {
-    return gemm_relu_f16_ex(M, N, K, A, B, C, stream, nullptr);
+    return run(M, N, K, A, B, C, stream, nullptr, gemm_relu::kActRelu, nullptr);
+}
+
+int gemm_bias_gelu_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias,
+                          void* C, void* stream, const gemm_relu_opts* opts)
+{
+    return run(M, N, K, A, B, C, stream, opts, gemm_relu::kActBiasGelu, bias);
+}
+
+int gemm_bias_gelu_f16(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias,
+                       void* C, void* stream)
+{
+    return run(M, N, K, A, B, C, stream, nullptr, gemm_relu::kActBiasGelu, bias);
 }
 
 }  // extern "C"

@@ -364,31 +364,44 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     // done with its fragment reads, before the ring is reused
     sync.template operator()<0>();
 
-    // ---- epilogue: ReLU, fp16 (nearest even) into LDS, then row stores ----
+    // ---- epilogue: ReLU (or bias + GELU), fp16 (nearest even) into LDS, then
+    // row stores ----
     // Lane holds, for result rows d = 8q + 4*(lane/32) + r (r = 0..3), the
     // column 16*(j%4) + 64*(q/2) + 8*(q%2) + 4*(lane/32) + r of unit j/4.
     auto c_stage = [&](int s) -> char* {
         return reinterpret_cast<char*>(s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3 + (s - 3) * (T::A_HALVES + T::B_HALVES));
     };
+    with_epilogue(p, [&]<int ACT>() {
+        // the bias of this lane's columns, loaded once for all its rows
+        f32x4 bias[T::FN][4];
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i) {
-        const int rl = wm * T::TM + 32 * i + lane % 32;  // row in the tile
-        // the 32 rows of block i lie in one stage array
-        char* cs = c_stage(__builtin_amdgcn_readfirstlane((wm * T::TM + 32 * i) / T::C_ROWS_PER_STAGE));
-        char* crow = cs + (rl % T::C_ROWS_PER_STAGE) * (T::BN * 2);
-#pragma unroll
-        for (int j = 0; j < T::FN; ++j) {
+        for (int j = 0; j < T::FN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int cl = wn * T::TN + 128 * (j / 4) + 16 * (j % 4) + 64 * (q / 2) + 8 * (q % 2) +
                                4 * (lane / 32);
-                u32x2 w;
-                w[0] = relu_pack2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-                w[1] = relu_pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                *reinterpret_cast<u32x2*>(crow + (((cl / 8) ^ c_swz(rl)) * 16) + (cl % 8) * 2) = w;
+                bias[j][q] = (ACT == kActBiasGelu) ? bias4(p, n0 + cl) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) {
+            const int rl = wm * T::TM + 32 * i + lane % 32;  // row in the tile
+            // the 32 rows of block i lie in one stage array
+            char* cs = c_stage(__builtin_amdgcn_readfirstlane((wm * T::TM + 32 * i) / T::C_ROWS_PER_STAGE));
+            char* crow = cs + (rl % T::C_ROWS_PER_STAGE) * (T::BN * 2);
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int cl = wn * T::TN + 128 * (j / 4) + 16 * (j % 4) + 64 * (q / 2) + 8 * (q % 2) +
+                                   4 * (lane / 32);
+                    u32x2 w;
+                    w[0] = epi_pack2b<ACT>(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], bias[j][q][0], bias[j][q][1]);
+                    w[1] = epi_pack2b<ACT>(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3], bias[j][q][2], bias[j][q][3]);
+                    *reinterpret_cast<u32x2*>(crow + (((cl / 8) ^ c_swz(rl)) * 16) + (cl % 8) * 2) = w;
+                }
             }
         }
-    }
+    });
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     constexpr int kRowsPerPass = T::C_ROWS_PER_PASS;  // BN / 8 lanes x 16 B per row

@@ -191,17 +191,28 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
         }
     }
 
+    // ReLU (or bias + GELU), fp16 (nearest even), 16-byte stores
     auto store_c = [&](const float (&vals)[NJ][8]) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int rl = cm + j * RP, m = m0 + rl;
-            if (rl < T::BM && m < M && n < N) {
-                u32x4 h;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) h[q] = relu_pack2(vals[j][2 * q], vals[j][2 * q + 1]);
-                *reinterpret_cast<u32x4*>(p.C + (int64_t)m * N + n) = h;
+        with_epilogue(p, [&]<int ACT>() {
+            // the bias of this thread's 8 columns, loaded once for all its rows
+            f32x4 blo = f32x4{0.f, 0.f, 0.f, 0.f}, bhi = blo;
+            if constexpr (ACT == kActBiasGelu) {
+                blo = bias4(p, n);
+                bhi = bias4(p, n + 4);
             }
-        }
+            const float bv[8] = {blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int rl = cm + j * RP, m = m0 + rl;
+                if (rl < T::BM && m < M && n < N) {
+                    u32x4 h;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        h[q] = epi_pack2b<ACT>(vals[j][2 * q], vals[j][2 * q + 1], bv[2 * q], bv[2 * q + 1]);
+                    *reinterpret_cast<u32x4*>(p.C + (int64_t)m * N + n) = h;
+                }
+            }
+        });
     };
 
     if (p.splits == 1) {

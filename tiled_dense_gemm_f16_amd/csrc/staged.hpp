@@ -265,33 +265,42 @@ __global__ void __launch_bounds__(T::NT, T::MIN_WAVES) staged_kernel(Args p)
         wait_vmcnt<0>();  // the loads past the end must land before the kernel ends
     }
 
-    // Epilogue: ReLU on the fp32 accumulator, round to fp16 (nearest even),
-    // store. Lane holds rows m, columns n .. n+3 of each 16x16 block.
+    // Epilogue: ReLU (or bias + GELU) on the fp32 accumulator, round to fp16
+    // (nearest even), store. Lane holds rows m, columns n .. n+3 of each 16x16
+    // block.
     const int lr = lane & 15, lg = lane >> 4;
+    with_epilogue(p, [&]<int ACT>() {
+        // vector path: the bias of this lane's columns, loaded once for all its rows
+        f32x4 bias[T::FN];
 #pragma unroll
-    for (int fm = 0; fm < T::FM; ++fm) {
-        const int m = m0 + wm * T::TM + fm * 16 + lr;
+        for (int fn = 0; fn < T::FN; ++fn)
+            bias[fn] = (VEC && ACT == kActBiasGelu) ? bias4(p, n0 + wn * T::TN + fn * 16 + lg * 4)
+                                                    : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int fn = 0; fn < T::FN; ++fn) {
-            const int n = n0 + wn * T::TN + fn * 16 + lg * 4;
-            const f32x4 v = acc[fm][fn];
-            if (m < p.M) {
-                uint16_t* dst = p.C + (int64_t)m * p.N + n;
-                if constexpr (VEC) {
-                    if (n < p.N) {
-                        u32x2 w;
-                        w[0] = relu_pack2(v[0], v[1]);
-                        w[1] = relu_pack2(v[2], v[3]);
-                        *reinterpret_cast<u32x2*>(dst) = w;
+        for (int fm = 0; fm < T::FM; ++fm) {
+            const int m = m0 + wm * T::TM + fm * 16 + lr;
+#pragma unroll
+            for (int fn = 0; fn < T::FN; ++fn) {
+                const int n = n0 + wn * T::TN + fn * 16 + lg * 4;
+                const f32x4 v = acc[fm][fn];
+                if (m < p.M) {
+                    uint16_t* dst = p.C + (int64_t)m * p.N + n;
+                    if constexpr (VEC) {
+                        if (n < p.N) {
+                            u32x2 w;
+                            w[0] = epi_pack2b<ACT>(v[0], v[1], bias[fn][0], bias[fn][1]);
+                            w[1] = epi_pack2b<ACT>(v[2], v[3], bias[fn][2], bias[fn][3]);
+                            *reinterpret_cast<u32x2*>(dst) = w;
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (n + r < p.N) dst[r] = epi_f16<ACT>(p, v[r], n + r);
                     }
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (n + r < p.N) dst[r] = relu_f16(v[r]);
                 }
             }
         }
-    }
+    });
 }
 
 }  // namespace staged
