@@ -135,6 +135,42 @@ const char* gemm_relu_strerror(int status);
 int gemm_relu_tile_count(void);
 const char* gemm_relu_tile_name(int tile);
 
+/* Kernel families of gemm_relu_tile_desc.family. */
+#define GEMM_RELU_FAMILY_PIPELINED 0 /* direct-to-LDS loads into a ring of LDS stages */
+#define GEMM_RELU_FAMILY_STAGED 1    /* loads through registers into a double-buffered LDS tile */
+#define GEMM_RELU_FAMILY_SPLITK 2    /* waves and workgroups split K; fp32 partials are summed */
+
+/*
+ * The launch parameters of one compiled tile: the search space of an offline
+ * tuner, which explores tile sizes, the K depth of a step, the pipeline depth
+ * and the thread count, and leaves out configurations over the LDS budget
+ * ("Writing high-performance kernels in TileLang", sections "GEMM con Tensor
+ * Cores y decisiones que cambian la velocidad" and "El ajuste automático
+ * encuentra configuraciones específicas para cada GPU"). Every compiled tile
+ * already fits the 160 KiB of LDS of a gfx950 compute unit; configurations
+ * that do not are rejected when the library is compiled.
+ */
+typedef struct gemm_relu_tile_desc {
+    int32_t bm, bn;          /* rows and columns of C per workgroup */
+    int32_t bk;              /* K depth of one pipeline step */
+    int32_t stages;          /* K steps held per workgroup: LDS ring slots (pipelined), LDS buffers
+                                (staged) or register ring depth per wave (split-K) */
+    int32_t waves_m, waves_n, waves_k; /* wave grid; waves_k > 1 when the waves split K */
+    int32_t threads;         /* threads per workgroup (64 per wave) */
+    int32_t lds_bytes;       /* static LDS per workgroup */
+    int32_t split_k;         /* 1 when K is also split across workgroups through the workspace */
+    int32_t default_group_m; /* tile-rows per group of the grouped order when opts leave it 0 */
+    int32_t family;          /* GEMM_RELU_FAMILY_* */
+    int32_t reserved[4];     /* zero */
+} gemm_relu_tile_desc;
+
+/*
+ * Fills *desc for a tile id < gemm_relu_tile_count(). Returns GEMM_RELU_EINVAL
+ * for a NULL desc and GEMM_RELU_EUNSUPPORTED for an unknown id (desc is then
+ * left untouched). Host-only; makes no HIP call.
+ */
+int gemm_relu_tile_info(int tile, gemm_relu_tile_desc* desc);
+
 /*
  * The tile the library would use for this problem without opts, or -1 for the
  * generic element-wise path that serves shapes whose K or N is not a multiple

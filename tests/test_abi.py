@@ -66,18 +66,88 @@ def test_strerror_and_tiles():
 
 
 def test_tile_selection_is_host_only():
-    # large square -> the 256x256 tile; few rows -> a split-K tile sized to M
+    # the cost model's choices on shapes where the offline sweep's winner is
+    # clear: few rows -> split-K tiles; otherwise the largest tile that still
+    # fills the 256 compute units
+    name = lambda *s: gr.tile_name(gr.select_tile(*s))  # noqa: E731
     assert gr.select_tile(4096, 4096, 4096) == 0
-    assert "splitk_16x" in gr.tile_name(gr.select_tile(16, 8192, 8192))
-    assert "splitk_32x" in gr.tile_name(gr.select_tile(17, 8192, 8192))
-    assert "splitk_64x" in gr.tile_name(gr.select_tile(64, 4096, 4096))
-    assert "splitk" not in gr.tile_name(gr.select_tile(65, 4096, 4096))
+    assert name(16, 8192, 8192).startswith("splitk_16x")
+    assert name(1, 8192, 8192).startswith("splitk_16x")
+    assert name(4096, 64, 4096).startswith("splitk_16x")  # narrow: 256 tiles of 16x128
+    assert gr.select_tile(3072, 3072, 3072) == 0  # 144 tiles of 256x256
+    assert name(2560, 2560, 2560).startswith("128x256")  # 200 tiles
+    assert name(2048, 2048, 2048).startswith("64x256")  # 256 tiles
+    assert name(1024, 1024, 1024).startswith("splitk_32x")  # 256 tiles of 32x128
+    assert name(1000, 1016, 1000).startswith("splitk_32x")
+    assert name(512, 4096, 8192).startswith("splitk_64x")  # 256 tiles of 64x128
+    assert name(256, 256, 256).startswith("16x64")  # latency-bound
+    # the split-K kernel's 32-bit A offsets: M*K*2 must stay below 2^31
+    assert "splitk" not in name(65536, 256, 16384)
     # K or N not a multiple of 8 -> the generic element-wise path
     assert gr.select_tile(64, 64, 7) == -1
     assert gr.select_tile(64, 9, 64) == -1
     # misaligned pointers -> generic path
     assert gr.select_tile(64, 64, 64, 0x1000, 0x2002, 0x3000) == -1
     assert gr.select_tile(64, 64, 64, 0x1000, 0x2000, 0x3000) >= 0
+
+
+def test_tile_info_describes_every_tile():
+    # the tuner's search space: each compiled tile's parameters agree with its
+    # name, and every tile fits the 160 KiB of LDS of a gfx950 compute unit
+    for t in range(gr.tile_count()):
+        d = gr.tile_info(t)
+        name = gr.tile_name(t)
+        assert d["lds_bytes"] <= 160 * 1024, name
+        assert d["threads"] == 64 * d["waves_m"] * d["waves_n"] * d["waves_k"], name
+        assert f"{d['bm']}x{d['bn']}" in name, name
+        assert d["family"] in (gr.FAMILY_PIPELINED, gr.FAMILY_STAGED, gr.FAMILY_SPLITK)
+        assert bool(d["split_k"]) == ("splitk" in name) == (d["family"] == gr.FAMILY_SPLITK), name
+        if d["family"] == gr.FAMILY_PIPELINED:
+            assert f"x{d['bk']}s{d['stages']}_w{d['waves_m']}x{d['waves_n']}" in name, name
+            assert d["lds_bytes"] == d["stages"] * (d["bm"] + d["bn"]) * d["bk"] * 2, name
+        elif d["family"] == gr.FAMILY_STAGED:
+            assert d["lds_bytes"] == 2 * (d["bm"] + d["bn"]) * d["bk"] * 2, name
+    lib = gr.load()
+    d = gr.TileDesc()
+    assert lib.gemm_relu_tile_info(gr.tile_count(), ctypes.byref(d)) == gr.EUNSUPPORTED
+    assert lib.gemm_relu_tile_info(-1, ctypes.byref(d)) == gr.EUNSUPPORTED
+    assert lib.gemm_relu_tile_info(0, None) == gr.EINVAL
+
+
+def test_tuner_candidates():
+    from tiled_dense_gemm_f16_amd import tune
+
+    c = tune.candidates(4096, 4096, 4096)
+    tiles = {x["tile"] for x in c}
+    assert tiles == set(range(gr.tile_count()))
+    for x in c:
+        d = gr.tile_info(x["tile"])
+        if x["block_order"] == gr.ORDER_ROW_MAJOR:
+            assert x["group_m"] == 0 and not d["split_k"]
+        assert x["group_m"] <= -(-4096 // d["bm"])
+    # a grid one tile-row high has no block order to choose
+    assert all(x["group_m"] == 0 and x["block_order"] == gr.ORDER_DEFAULT for x in tune.candidates(16, 8192, 8192))
+    # a tighter LDS budget prunes the big tiles
+    small = tune.candidates(1024, 1024, 1024, lds_limit=64 * 1024)
+    assert small and all(gr.tile_info(x["tile"])["lds_bytes"] <= 64 * 1024 for x in small)
+
+
+def test_tuner_table_roundtrip(tmp_path):
+    from tiled_dense_gemm_f16_amd import tune
+
+    path = str(tmp_path / "tuned.json")
+    res = {"shape": [64, 128, 256], "epilogue": "relu", "arch": "gfx950",
+           "results": [{"ok": True}], "best": {"tile": 2, "tile_name": gr.tile_name(2), "block_order": 0,
+                                             "group_m": 2, "us": 3.0}}
+    tune.save(res, path)
+    assert tune.lookup(path, "gfx950", "relu", 64, 128, 256) == {"tile": 2, "block_order": 0, "group_m": 2}
+    assert tune.lookup(path, "gfx950", "bias_gelu", 64, 128, 256) is None
+    assert tune.lookup(path, "gfx942", "relu", 64, 128, 256) is None
+    # an entry whose tile id now names a different kernel is not applied
+    res["best"]["tile_name"] = "no-such-tile"
+    res["shape"] = [1, 2, 3]
+    tune.save(res, path)
+    assert tune.lookup(path, "gfx950", "relu", 1, 2, 3) is None
 
 
 FAKE = 0x10000  # never dereferenced: these calls must fail validation first

@@ -29,11 +29,26 @@ class Opts(ctypes.Structure):
                 ("group_m", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
+FAMILY_PIPELINED, FAMILY_STAGED, FAMILY_SPLITK = 0, 1, 2
+
+
+class TileDesc(ctypes.Structure):
+    _fields_ = [("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
+                ("stages", ctypes.c_int32), ("waves_m", ctypes.c_int32), ("waves_n", ctypes.c_int32),
+                ("waves_k", ctypes.c_int32), ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("split_k", ctypes.c_int32), ("default_group_m", ctypes.c_int32), ("family", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 4)]
+
+    def as_dict(self) -> dict:
+        return {f: int(getattr(self, f)) for f, _ in self._fields_ if f != "reserved"}
+
+
 _lock = threading.Lock()
 _lib = None
 
 EXPORTED = ("gemm_relu_f16", "gemm_relu_f16_ex", "gemm_bias_gelu_f16", "gemm_bias_gelu_f16_ex",
-            "gemm_relu_strerror", "gemm_relu_tile_count", "gemm_relu_tile_name", "gemm_relu_select_tile")
+            "gemm_relu_strerror", "gemm_relu_tile_count", "gemm_relu_tile_name", "gemm_relu_tile_info",
+            "gemm_relu_select_tile")
 
 
 def load():
@@ -61,6 +76,8 @@ def load():
         lib.gemm_relu_tile_count.restype = i32
         lib.gemm_relu_tile_name.argtypes = [i32]
         lib.gemm_relu_tile_name.restype = ctypes.c_char_p
+        lib.gemm_relu_tile_info.argtypes = [i32, ctypes.POINTER(TileDesc)]
+        lib.gemm_relu_tile_info.restype = i32
         lib.gemm_relu_select_tile.argtypes = [i64, i64, i64, p, p, p]
         lib.gemm_relu_select_tile.restype = i32
         _lib = lib
@@ -114,6 +131,13 @@ def tile_count() -> int:
 
 def tile_name(tile: int) -> str:
     return load().gemm_relu_tile_name(int(tile)).decode()
+
+
+def tile_info(tile: int) -> dict:
+    """Launch parameters of a compiled tile (see gemm_relu_tile_desc)."""
+    d = TileDesc()
+    _check(load().gemm_relu_tile_info(int(tile), ctypes.byref(d)))
+    return d.as_dict()
 
 
 def select_tile(M: int, N: int, K: int, A: int = 0, B: int = 0, C: int = 0) -> int:

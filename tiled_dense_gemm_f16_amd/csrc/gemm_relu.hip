@@ -85,36 +85,57 @@ hipError_t launch_splitk(const Args& a, hipStream_t s)
     return hipGetLastError();
 }
 
+// Launch parameters of each family's configurations, for gemm_relu_tile_info.
+template <class T>
+constexpr gemm_relu_tile_desc pipelined_desc(int group_m)
+{
+    return {T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, 1, T::NT, T::STAGES * T::STAGE_BYTES,
+            0, group_m, GEMM_RELU_FAMILY_PIPELINED, {0, 0, 0, 0}};
+}
+
+template <class T>
+constexpr gemm_relu_tile_desc staged_desc(int group_m)
+{
+    return {T::BM, T::BN, T::BK, 2, T::WAVES_M, T::WAVES_N, 1, T::NT, T::LDS_BYTES,
+            0, group_m, GEMM_RELU_FAMILY_STAGED, {0, 0, 0, 0}};
+}
+
+template <class T>
+constexpr gemm_relu_tile_desc splitk_desc()
+{
+    return {T::BM, T::TN, T::BK, T::D, 1, 1, T::NW, T::NT,
+            (int)(sizeof(float) * T::NW * T::BM * T::RED_ROW + sizeof(uint32_t)),
+            1, 1, GEMM_RELU_FAMILY_SPLITK, {0, 0, 0, 0}};
+}
+
 struct TileEntry {
     const char* name;
-    int bm, bn;
-    int default_group_m;
-    bool splitk;      // K split across workgroups (needs the workspace)
+    gemm_relu_tile_desc desc;
     LaunchFn vec;     // K % 8 == 0, N % 8 == 0, 16-byte aligned pointers
     LaunchFn generic; // anything else
 };
 
 const TileEntry kTiles[] = {
-    {"256x256x32s4_w2x2_mfma32x32x16_lds-dma", 256, 256, 4, false, launch_pipelined<P256>,
+    {"256x256x32s4_w2x2_mfma32x32x16_lds-dma", pipelined_desc<P256>(4), launch_pipelined<P256>,
      launch_staged<S256, false>},
-    {"128x128x64_w2x2_mfma16x16x32", 128, 128, 4, false, launch_staged<S128, true>, launch_staged<S128, false>},
-    {"64x64x64_w2x2_mfma16x16x32", 64, 64, 4, false, launch_staged<S64, true>, launch_staged<S64, false>},
-    {"16x64x64_w1x4_mfma16x16x32", 16, 64, 1, false, launch_staged<S16, true>, launch_staged<S16, false>},
-    {"splitk_16x128_w4k_mfma16x16x32_regT", 16, 128, 1, true, launch_splitk<K16>, launch_staged<S16, false>},
-    {"splitk_32x128_w4k_mfma16x16x32_regT", 32, 128, 1, true, launch_splitk<K32>, launch_staged<S64, false>},
-    {"splitk_64x128_w4k_mfma16x16x32_regT", 64, 128, 1, true, launch_splitk<K64>, launch_staged<S64, false>},
-    {"256x256x32s4_w4x2_mfma32x32x16_lds-dma", 256, 256, 4, false, launch_pipelined<P256W8>,
-     launch_staged<S256, false>},
-    {"256x256x32s5_w2x2_mfma32x32x16_lds-dma", 256, 256, 4, false, launch_pipelined<P256S5>,
-     launch_staged<S256, false>},
-    {"128x256x32s4_w2x2_mfma32x32x16_lds-dma", 128, 256, 4, false, launch_pipelined<P128>,
+    {"128x128x64_w2x2_mfma16x16x32", staged_desc<S128>(4), launch_staged<S128, true>,
      launch_staged<S128, false>},
-    {"64x256x32s4_w1x2_mfma32x32x16_lds-dma", 64, 256, 4, false, launch_pipelined<P64>, launch_staged<S64, false>},
+    {"64x64x64_w2x2_mfma16x16x32", staged_desc<S64>(4), launch_staged<S64, true>, launch_staged<S64, false>},
+    {"16x64x64_w1x4_mfma16x16x32", staged_desc<S16>(1), launch_staged<S16, true>, launch_staged<S16, false>},
+    {"splitk_16x128_w4k_mfma16x16x32_regT", splitk_desc<K16>(), launch_splitk<K16>, launch_staged<S16, false>},
+    {"splitk_32x128_w4k_mfma16x16x32_regT", splitk_desc<K32>(), launch_splitk<K32>, launch_staged<S64, false>},
+    {"splitk_64x128_w4k_mfma16x16x32_regT", splitk_desc<K64>(), launch_splitk<K64>, launch_staged<S64, false>},
+    {"256x256x32s4_w4x2_mfma32x32x16_lds-dma", pipelined_desc<P256W8>(4), launch_pipelined<P256W8>,
+     launch_staged<S256, false>},
+    {"256x256x32s5_w2x2_mfma32x32x16_lds-dma", pipelined_desc<P256S5>(4), launch_pipelined<P256S5>,
+     launch_staged<S256, false>},
+    {"128x256x32s4_w2x2_mfma32x32x16_lds-dma", pipelined_desc<P128>(4), launch_pipelined<P128>,
+     launch_staged<S128, false>},
+    {"64x256x32s4_w1x2_mfma32x32x16_lds-dma", pipelined_desc<P64>(4), launch_pipelined<P64>,
+     launch_staged<S64, false>},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kGenericTile = 2;  // tile used by the element-wise path
-constexpr int kSplitK16 = 4, kSplitK32 = 5, kSplitK64 = 6;
-constexpr int kPipe64 = 10;  // 64x256 pipelined tile
 constexpr int kSplitKTN = 128;   // columns of a split-K workgroup
 constexpr int kSplitKStep = GR_SPLITK_NW * 32;  // K granularity of a split-K workgroup (waves x 32)
 constexpr int kTargetBlocks = GR_SPLITK_TARGET;  // workgroups to aim for
@@ -145,16 +166,72 @@ bool fast_path_ok(int64_t N, int64_t K, const void* A, const void* B, const void
 // The split-K kernel addresses A with 32-bit offsets.
 bool splitk_ok(int64_t M, int64_t K) { return M * K * 2 < ((int64_t)1 << 31); }
 
+// The shape heuristic: a cost model whose constants were fitted to an offline
+// sweep (tune.py) of every tile and block order over 38 shapes, from 1 to 8192
+// rows, 64 to 8192 columns and 256 to 12288 deep. A tile's predicted time is
+//   rounds x (2 bm bn kc FLOP) / rate,   rounds = ceil(workgroups / 256),
+// floored by the HBM time of the algorithmic bytes, plus for split-K launches
+// the cost of writing and re-reading the fp32 partials and of the combine.
+// The rate is what one compute unit sustains on that tile (larger tiles reuse
+// each loaded byte more; the fitted rates already include the clock the chip
+// holds under load). The model picks the measured fastest tile on 31 of the
+// 38 shapes and is within 15 % of it on the rest (1 % slower on average);
+// the rules it replaced, which looked at M and the 256x256 tile count alone,
+// were up to 6x slower on shapes they were not written for.
+struct AutoTile {
+    int id;
+    double tflops_per_cu;
+};
+constexpr AutoTile kAutoTiles[] = {
+    {0, 6.96},  // 256x256 pipelined
+    {9, 5.24},  // 128x256 pipelined
+    {10, 3.21}, // 64x256 pipelined
+    {6, 2.13},  // split-K 64x128
+    {5, 1.59},  // split-K 32x128
+    {4, 1.12},  // split-K 16x128
+    {2, 0.895}, // 64x64 staged
+    {3, 0.273}, // 16x64 staged
+};
+constexpr double kComputeUnits = 256.0;
+constexpr double kHbmBytesPerUs = 6.68e6;          // 6.68 TB/s
+constexpr double kPartialUsPerByte = 0.97e-6;      // partials: written once, read once
+constexpr double kCombineUs = 3.25;                // last-workgroup combine and counters
+
+struct Prediction {
+    double us;       // predicted time
+    double compute;  // its compute part: breaks ties between HBM-bound tiles
+};
+
+Prediction predict(const AutoTile& at, int64_t M, int64_t N, int64_t K)
+{
+    const gemm_relu_tile_desc& d = kTiles[at.id].desc;
+    const int64_t tiles = ((M + d.bm - 1) / d.bm) * ((N + d.bn - 1) / d.bn);
+    int splits = 1, kc = (int)K;
+    if (d.split_k) choose_splits(K, tiles, splits, kc);
+    const double rounds = (double)((tiles * splits + (int64_t)kComputeUnits - 1) / (int64_t)kComputeUnits);
+    const double compute = rounds * 2.0 * d.bm * d.bn * (double)kc / (at.tflops_per_cu * 1e6);
+    const double memory = 2.0 * ((double)M * K + (double)K * N + (double)M * N) / kHbmBytesPerUs;
+    const double combine = splits > 1 ? kPartialUsPerByte * 8.0 * (double)M * N * splits + kCombineUs : 0.0;
+    return {(compute > memory ? compute : memory) + combine, compute};
+}
+
+// The tile of least predicted time; among tiles bound by the same HBM time,
+// the one with the least compute (the fewest padded rows).
 int choose_tile(int64_t M, int64_t N, int64_t K)
 {
-    auto blocks = [&](int t) {
-        return ((M + kTiles[t].bm - 1) / kTiles[t].bm) * ((N + kTiles[t].bn - 1) / kTiles[t].bn);
-    };
-    // few rows: stream B once, K split to fill the chip
-    if (M <= 64 && splitk_ok(M, K)) return M <= 16 ? kSplitK16 : M <= 32 ? kSplitK32 : kSplitK64;
-    if (blocks(0) >= 256) return 0;  // enough 256x256 tiles to fill the chip
-    if (N >= 192) return kPipe64;     // 64x256 pipelined tiles, two workgroups per CU
-    return 2;                         // narrow: 64x64 register-staged tiles
+    const bool sk = splitk_ok(M, K);
+    int best = -1;
+    Prediction bp{0.0, 0.0};
+    for (const AutoTile& at : kAutoTiles) {
+        if (kTiles[at.id].desc.split_k && !sk) continue;
+        const Prediction p = predict(at, M, N, K);
+        const bool tie = p.us - bp.us < 1e-9 * bp.us && bp.us - p.us < 1e-9 * bp.us;
+        if (best < 0 || (tie ? p.compute < bp.compute : p.us < bp.us)) {
+            best = at.id;
+            bp = p;
+        }
+    }
+    return best;
 }
 
 // ---------------------------------------------------------------------------
@@ -286,8 +363,8 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, 
         (opts && opts->tile != GEMM_RELU_TILE_AUTO) ? opts->tile : (vec ? choose_tile(M, N, K) : kGenericTile);
     // the split-K tiles have no element-wise instance: unaligned shapes take
     // the generic tile
-    const TileEntry& te = (!vec && kTiles[tile].splitk) ? kTiles[kGenericTile] : kTiles[tile];
-    const bool splitk = vec && te.splitk;
+    const TileEntry& te = (!vec && kTiles[tile].desc.split_k) ? kTiles[kGenericTile] : kTiles[tile];
+    const bool splitk = vec && te.desc.split_k;
     if (splitk && !splitk_ok(M, K)) return GEMM_RELU_EUNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     Args a;
@@ -297,9 +374,9 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, 
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
-    a.tiles_m = (int)((M + te.bm - 1) / te.bm);
-    a.tiles_n = (int)((N + te.bn - 1) / te.bn);
-    a.group_m = (opts && opts->group_m > 0) ? opts->group_m : te.default_group_m;
+    a.tiles_m = (int)((M + te.desc.bm - 1) / te.desc.bm);
+    a.tiles_n = (int)((N + te.desc.bn - 1) / te.desc.bn);
+    a.group_m = (opts && opts->group_m > 0) ? opts->group_m : te.desc.default_group_m;
     a.order = opts ? opts->block_order : GEMM_RELU_ORDER_DEFAULT;
     a.act = act;
     a.bias = static_cast<const uint16_t*>(bias);
@@ -343,6 +420,14 @@ int gemm_relu_tile_count(void) { return kNumTiles; }
 const char* gemm_relu_tile_name(int tile)
 {
     return (tile >= 0 && tile < kNumTiles) ? kTiles[tile].name : "";
+}
+
+int gemm_relu_tile_info(int tile, gemm_relu_tile_desc* desc)
+{
+    if (!desc) return GEMM_RELU_EINVAL;
+    if (tile < 0 || tile >= kNumTiles) return GEMM_RELU_EUNSUPPORTED;
+    *desc = kTiles[tile].desc;
+    return GEMM_RELU_OK;
 }
 
 int gemm_relu_select_tile(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* C)
