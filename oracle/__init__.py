@@ -73,6 +73,11 @@ def _load():
         lib.oracle_gemm_bias_gelu_f16_rows.restype = ctypes.c_int
         lib.oracle_gemm_bias_gelu_f16_points.argtypes = [i64, i64, i64, p, p, p, i64, p, p, p, p, p]
         lib.oracle_gemm_bias_gelu_f16_points.restype = ctypes.c_int
+        i32 = ctypes.c_int
+        lib.oracle_gemm_f16_rows_t.argtypes = [i64, i64, i64, p, i32, p, i32, p, p, p, p, i64, i64]
+        lib.oracle_gemm_f16_rows_t.restype = ctypes.c_int
+        lib.oracle_gemm_f16_points_t.argtypes = [i64, i64, i64, p, i32, p, i32, p, i64, p, p, p, p, p]
+        lib.oracle_gemm_f16_points_t.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -117,13 +122,20 @@ def gelu(x) -> np.ndarray:
     return np.vectorize(lib.oracle_gelu, otypes=[np.float64])(v)
 
 
-def _rows(A, B, bias, want_pre, want_absdot, rows):
-    M, K = A.shape
-    K2, N = B.shape
+def _dims(A, B, trans_a, trans_b):
+    """M, N, K of op(A) @ op(B) from the stored shapes: A is [M, K], or [K, M]
+    when trans_a; B is [K, N], or [N, K] when trans_b."""
+    M, K = A.shape[::-1] if trans_a else A.shape
+    K2, N = B.shape[::-1] if trans_b else B.shape
     if K2 != K:
         raise ValueError("inner dimensions differ")
-    A = _u16(A, (M, K))
-    B = _u16(B, (K, N))
+    return M, N, K
+
+
+def _rows(A, B, bias, want_pre, want_absdot, rows, trans_a=False, trans_b=False):
+    M, N, K = _dims(A, B, trans_a, trans_b)
+    A = _u16(A, A.shape)
+    B = _u16(B, B.shape)
     if bias is not None:
         bias = _u16(bias, (N,))
     r0, r1 = (0, M) if rows is None else rows
@@ -140,7 +152,10 @@ def _rows(A, B, bias, want_pre, want_absdot, rows):
         return ctypes.c_void_p(arr.ctypes.data - r0 * N * itemsize)
 
     lib = _load()
-    if bias is None:
+    if trans_a or trans_b:
+        rc = lib.oracle_gemm_f16_rows_t(M, N, K, _ptr(A), int(trans_a), _ptr(B), int(trans_b), _ptr(bias),
+                                        base(C, 2), base(pre, 8), base(sab, 8), r0, r1)
+    elif bias is None:
         rc = lib.oracle_gemm_relu_f16_rows(M, N, K, _ptr(A), _ptr(B), base(C, 2), base(pre, 8), base(sab, 8), r0, r1)
     else:
         rc = lib.oracle_gemm_bias_gelu_f16_rows(M, N, K, _ptr(A), _ptr(B), _ptr(bias), base(C, 2), base(pre, 8),
@@ -155,13 +170,10 @@ def _rows(A, B, bias, want_pre, want_absdot, rows):
     return out[0] if len(out) == 1 else tuple(out)
 
 
-def _points(A, B, bias, ii, jj, want_pre, want_absdot):
-    M, K = A.shape
-    K2, N = B.shape
-    if K2 != K:
-        raise ValueError("inner dimensions differ")
-    A = _u16(A, (M, K))
-    B = _u16(B, (K, N))
+def _points(A, B, bias, ii, jj, want_pre, want_absdot, trans_a=False, trans_b=False):
+    M, N, K = _dims(A, B, trans_a, trans_b)
+    A = _u16(A, A.shape)
+    B = _u16(B, B.shape)
     if bias is not None:
         bias = _u16(bias, (N,))
     ii = np.ascontiguousarray(ii, dtype=np.int64)
@@ -172,7 +184,10 @@ def _points(A, B, bias, ii, jj, want_pre, want_absdot):
     pre = np.zeros(ii.shape, dtype=np.float64) if want_pre else None
     sab = np.zeros(ii.shape, dtype=np.float64) if want_absdot else None
     lib = _load()
-    if bias is None:
+    if trans_a or trans_b:
+        rc = lib.oracle_gemm_f16_points_t(M, N, K, _ptr(A), int(trans_a), _ptr(B), int(trans_b), _ptr(bias),
+                                          ii.size, _ptr(ii), _ptr(jj), _ptr(out), _ptr(pre), _ptr(sab))
+    elif bias is None:
         rc = lib.oracle_gemm_relu_f16_points(M, N, K, _ptr(A), _ptr(B), ii.size, _ptr(ii), _ptr(jj), _ptr(out),
                                              _ptr(pre), _ptr(sab))
     else:
@@ -189,32 +204,36 @@ def _points(A, B, bias, ii, jj, want_pre, want_absdot):
 
 
 def gemm_relu_f16(A: np.ndarray, B: np.ndarray, *, want_pre: bool = False,
-                  want_absdot: bool = False, rows: tuple[int, int] | None = None):
-    """C = ReLU(A @ B) as fp16 bit patterns.
+                  want_absdot: bool = False, rows: tuple[int, int] | None = None,
+                  trans_a: bool = False, trans_b: bool = False):
+    """C = ReLU(op(A) @ op(B)) as fp16 bit patterns.
 
-    A: uint16 [M, K], B: uint16 [K, N]. With ``rows=(r0, r1)`` only those rows
-    are computed and returned (shape [r1-r0, N]). Optionally also returns the
+    A: uint16 [M, K] (or [K, M] stored, with trans_a), B: uint16 [K, N] (or
+    [N, K] stored, with trans_b). With ``rows=(r0, r1)`` only those rows are
+    computed and returned (shape [r1-r0, N]). Optionally also returns the
     float64 pre-activation sums and sum_k |a||b| for the same rows.
     """
-    return _rows(A, B, None, want_pre, want_absdot, rows)
+    return _rows(A, B, None, want_pre, want_absdot, rows, trans_a, trans_b)
 
 
 def gemm_relu_f16_points(A: np.ndarray, B: np.ndarray, ii, jj, *, want_pre: bool = False,
-                         want_absdot: bool = False):
-    """Elements C[ii[t], jj[t]] of ReLU(A @ B) as fp16 bit patterns."""
-    return _points(A, B, None, ii, jj, want_pre, want_absdot)
+                         want_absdot: bool = False, trans_a: bool = False, trans_b: bool = False):
+    """Elements C[ii[t], jj[t]] of ReLU(op(A) @ op(B)) as fp16 bit patterns."""
+    return _points(A, B, None, ii, jj, want_pre, want_absdot, trans_a, trans_b)
 
 
 def gemm_bias_gelu_f16(A: np.ndarray, B: np.ndarray, bias: np.ndarray, *, want_pre: bool = False,
-                       want_absdot: bool = False, rows: tuple[int, int] | None = None):
+                       want_absdot: bool = False, rows: tuple[int, int] | None = None,
+                       trans_a: bool = False, trans_b: bool = False):
     """C = GELU(A @ B + bias) as fp16 bit patterns; bias: uint16 [N], one value per column.
 
     ``pre`` (if asked for) is the float64 value A @ B + bias before GELU.
     """
-    return _rows(A, B, bias, want_pre, want_absdot, rows)
+    return _rows(A, B, bias, want_pre, want_absdot, rows, trans_a, trans_b)
 
 
 def gemm_bias_gelu_f16_points(A: np.ndarray, B: np.ndarray, bias: np.ndarray, ii, jj, *,
-                              want_pre: bool = False, want_absdot: bool = False):
-    """Elements C[ii[t], jj[t]] of GELU(A @ B + bias) as fp16 bit patterns."""
-    return _points(A, B, bias, ii, jj, want_pre, want_absdot)
+                              want_pre: bool = False, want_absdot: bool = False,
+                              trans_a: bool = False, trans_b: bool = False):
+    """Elements C[ii[t], jj[t]] of GELU(op(A) @ op(B) + bias) as fp16 bit patterns."""
+    return _points(A, B, bias, ii, jj, want_pre, want_absdot, trans_a, trans_b)

@@ -33,6 +33,17 @@
  *   pre[i][j] = sum over k (ascending) of a[i][k] * b[k][j]  +  bias[j]
  *   C[i][j]   = fp16_rne( GELU(pre[i][j]) )
  *
+ * Transposed operands. The tile-level product of the same TileLang example
+ * takes transpose_A / transpose_B flags (the notes under the program in
+ * section "Escribamos un GEMM"): C = epilogue(op(A) @ op(B)), where op(A) is
+ * either A as stored (M x K, leading dimension K) or the transpose of a
+ * stored K x M matrix (leading dimension M), and op(B) is either B as stored
+ * (K x N, leading dimension N) or the transpose of a stored N x K matrix
+ * (leading dimension K). Only where the elements are read changes:
+ *
+ *   op(A)[i][k] = op_a ? A[k*M + i] : A[i*K + k]
+ *   op(B)[k][j] = op_b ? B[j*K + k] : B[k*N + j]
+ *
  * Readings where the pages are silent: the final rounding is IEEE
  * round-to-nearest-even (what an ordinary fp32 -> fp16 conversion does);
  * overflow past the largest finite fp16 becomes +inf; fp16 subnormals are
@@ -134,6 +145,17 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Element (i, k) of op(A), and element (k, j) of op(B), as stored. */
+static uint16_t a_elem(const uint16_t* A, int op_a, int64_t M, int64_t K, int64_t i, int64_t k)
+{
+    return op_a ? A[k * M + i] : A[i * K + k];
+}
+
+static uint16_t b_elem(const uint16_t* B, int op_b, int64_t K, int64_t N, int64_t k, int64_t j)
+{
+    return op_b ? B[j * K + k] : B[k * N + j];
+}
+
 /* The epilogue: ReLU (bias == NULL) or bias + GELU. */
 static uint16_t finish(double acc, const uint16_t* bias, int64_t j, double* pre_out)
 {
@@ -152,17 +174,19 @@ static uint16_t finish(double acc, const uint16_t* bias, int64_t j, double* pre_
  * (same indexing as C); absdot, if not NULL, receives sum_k |a||b|.
  * Returns 0, or -1 on a bad argument or allocation failure.
  */
-static int rows_impl(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
-                     const uint16_t* bias, uint16_t* C, double* pre, double* absdot,
+static int rows_impl(int64_t M, int64_t N, int64_t K, const uint16_t* A, int op_a, const uint16_t* B,
+                     int op_b, const uint16_t* bias, uint16_t* C, double* pre, double* absdot,
                      int64_t row0, int64_t row1)
 {
     if (M < 0 || N < 0 || K < 0 || row0 < 0 || row1 > M || row0 > row1) return -1;
     if (N == 0 || row0 == row1) return 0;
+    /* op(B) decoded once, row k of op(B) at bd + k*N */
     double* bd = NULL;
     if (K > 0) {
         bd = (double*)malloc((size_t)K * (size_t)N * sizeof(double));
         if (!bd) return -1;
-        oracle_decode_f16(B, bd, K * N);
+        for (int64_t k = 0; k < K; ++k)
+            for (int64_t j = 0; j < N; ++j) bd[k * N + j] = oracle_f16_to_f64(b_elem(B, op_b, K, N, k, j));
     }
     int err = 0;
 #pragma omp parallel
@@ -178,7 +202,7 @@ static int rows_impl(int64_t M, int64_t N, int64_t K, const uint16_t* A, const u
                 for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
                 if (sab) for (int64_t j = 0; j < N; ++j) sab[j] = 0.0;
                 for (int64_t k = 0; k < K; ++k) {
-                    const double a = oracle_f16_to_f64(A[i * K + k]);
+                    const double a = oracle_f16_to_f64(a_elem(A, op_a, M, K, i, k));
                     const double* brow = bd + k * N;
                     for (int64_t j = 0; j < N; ++j) acc[j] += a * brow[j];
                     if (sab) {
@@ -203,8 +227,8 @@ static int rows_impl(int64_t M, int64_t N, int64_t K, const uint16_t* A, const u
  * Selected elements (ii[t], jj[t]), each summed in the same k-ascending order
  * as the full routine, so it gives the same values there.
  */
-static int points_impl(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
-                       const uint16_t* bias, int64_t npts, const int64_t* ii, const int64_t* jj,
+static int points_impl(int64_t M, int64_t N, int64_t K, const uint16_t* A, int op_a, const uint16_t* B,
+                       int op_b, const uint16_t* bias, int64_t npts, const int64_t* ii, const int64_t* jj,
                        uint16_t* out, double* pre, double* absdot)
 {
     if (M < 0 || N < 0 || K < 0 || npts < 0) return -1;
@@ -215,8 +239,8 @@ static int points_impl(int64_t M, int64_t N, int64_t K, const uint16_t* A, const
         const int64_t i = ii[t], j = jj[t];
         double acc = 0.0, s = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-            const double a = oracle_f16_to_f64(A[i * K + k]);
-            const double b = oracle_f16_to_f64(B[k * N + j]);
+            const double a = oracle_f16_to_f64(a_elem(A, op_a, M, K, i, k));
+            const double b = oracle_f16_to_f64(b_elem(B, op_b, K, N, k, j));
             acc += a * b;
             s += fabs(a) * fabs(b);
         }
@@ -232,7 +256,7 @@ int oracle_gemm_relu_f16_rows(int64_t M, int64_t N, int64_t K,
                               double* pre, double* absdot,
                               int64_t row0, int64_t row1)
 {
-    return rows_impl(M, N, K, A, B, NULL, C, pre, absdot, row0, row1);
+    return rows_impl(M, N, K, A, 0, B, 0, NULL, C, pre, absdot, row0, row1);
 }
 
 /* The whole of C = ReLU(A @ B). */
@@ -240,7 +264,7 @@ int oracle_gemm_relu_f16(int64_t M, int64_t N, int64_t K,
                          const uint16_t* A, const uint16_t* B, uint16_t* C,
                          double* pre, double* absdot)
 {
-    return rows_impl(M, N, K, A, B, NULL, C, pre, absdot, 0, M);
+    return rows_impl(M, N, K, A, 0, B, 0, NULL, C, pre, absdot, 0, M);
 }
 
 /* Selected elements of C = ReLU(A @ B). */
@@ -249,7 +273,7 @@ int oracle_gemm_relu_f16_points(int64_t M, int64_t N, int64_t K,
                                 int64_t npts, const int64_t* ii, const int64_t* jj,
                                 uint16_t* out, double* pre, double* absdot)
 {
-    return points_impl(M, N, K, A, B, NULL, npts, ii, jj, out, pre, absdot);
+    return points_impl(M, N, K, A, 0, B, 0, NULL, npts, ii, jj, out, pre, absdot);
 }
 
 /* Rows [row0, row1) of C = GELU(A @ B + bias), bias: N fp16 values (one per column). */
@@ -259,7 +283,7 @@ int oracle_gemm_bias_gelu_f16_rows(int64_t M, int64_t N, int64_t K,
                                    int64_t row0, int64_t row1)
 {
     if (!bias && N > 0) return -1;
-    return rows_impl(M, N, K, A, B, bias, C, pre, absdot, row0, row1);
+    return rows_impl(M, N, K, A, 0, B, 0, bias, C, pre, absdot, row0, row1);
 }
 
 /* Selected elements of C = GELU(A @ B + bias). */
@@ -269,5 +293,28 @@ int oracle_gemm_bias_gelu_f16_points(int64_t M, int64_t N, int64_t K,
                                      uint16_t* out, double* pre, double* absdot)
 {
     if (!bias && N > 0) return -1;
-    return points_impl(M, N, K, A, B, bias, npts, ii, jj, out, pre, absdot);
+    return points_impl(M, N, K, A, 0, B, 0, bias, npts, ii, jj, out, pre, absdot);
+}
+
+/*
+ * Rows [row0, row1) of C = epilogue(op(A) @ op(B)) with op_a, op_b in {0, 1}
+ * (0: as stored, 1: transposed, see above); bias NULL gives the ReLU epilogue,
+ * otherwise bias + GELU.
+ */
+int oracle_gemm_f16_rows_t(int64_t M, int64_t N, int64_t K, const uint16_t* A, int op_a,
+                           const uint16_t* B, int op_b, const uint16_t* bias, uint16_t* C,
+                           double* pre, double* absdot, int64_t row0, int64_t row1)
+{
+    if ((op_a != 0 && op_a != 1) || (op_b != 0 && op_b != 1)) return -1;
+    return rows_impl(M, N, K, A, op_a, B, op_b, bias, C, pre, absdot, row0, row1);
+}
+
+/* Selected elements of C = epilogue(op(A) @ op(B)). */
+int oracle_gemm_f16_points_t(int64_t M, int64_t N, int64_t K, const uint16_t* A, int op_a,
+                             const uint16_t* B, int op_b, const uint16_t* bias, int64_t npts,
+                             const int64_t* ii, const int64_t* jj, uint16_t* out, double* pre,
+                             double* absdot)
+{
+    if ((op_a != 0 && op_a != 1) || (op_b != 0 && op_b != 1)) return -1;
+    return points_impl(M, N, K, A, op_a, B, op_b, bias, npts, ii, jj, out, pre, absdot);
 }

@@ -405,8 +405,8 @@ def test_thread_count_independence():
 MUTANTS = {
     "drop_last_k_term": ("acc[j] += a * brow[j];", "if (k + 1 < K) acc[j] += a * brow[j];"),
     "transposed_b": ("const double* brow = bd + k * N;", "const double* brow = bd + (k % (N > 0 ? N : 1)) * N;"),
-    "wrong_a_index": ("oracle_f16_to_f64(A[i * K + k]);\n                    const double* brow",
-                      "oracle_f16_to_f64(A[k * M + i < M * K ? k * M + i : 0]);\n                    const double* brow"),
+    "wrong_a_index": ("return op_a ? A[k * M + i] : A[i * K + k];",
+                      "return op_a ? A[k * M + i] : A[(k * M + i) % (M * K)];"),
     "no_relu": ("return oracle_f64_to_f16_rne(pre > 0.0 ? pre : 0.0);", "return oracle_f64_to_f16_rne(pre);"),
     "relu_as_abs": ("return oracle_f64_to_f16_rne(pre > 0.0 ? pre : 0.0);", "return oracle_f64_to_f16_rne(fabs(pre));"),
     "ties_away": ("return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
@@ -648,3 +648,120 @@ def test_planted_bias_gelu_mistake_is_caught(mutant, tmp_path):
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
     assert _bias_pin_suite(mod) != [], f"planted mistake {mutant} went unnoticed"
+
+
+# ---------------------------------------------------------------------------
+# 10. transposed operands: C = epilogue(op(A) @ op(B)), op = as stored or the
+#     transpose of the stored matrix (the transpose_A / transpose_B flags of
+#     the tile-level product in "Escribamos un GEMM")
+# ---------------------------------------------------------------------------
+
+LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
+
+
+def _stored(logical: np.ndarray, trans: bool) -> np.ndarray:
+    """How a logical operand is laid out in memory under a transpose flag."""
+    return np.ascontiguousarray(logical.T) if trans else logical
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (7, 2, 16), (5, 17, 3), (16, 3, 17)])
+def test_transposed_brute_force_exact(ta, tb, M, N, K):
+    # the exact rational sums of the logical product, with the stored layout
+    # made by numpy's transpose: a wrong index in the oracle's transposed
+    # reads shows up as a different value
+    rng = np.random.default_rng(M * 1009 + N * 101 + K + 7 * ta + 13 * tb)
+    A = rand_f16_bits(rng, (M, K))
+    B = rand_f16_bits(rng, (K, N))
+    want, sums = exact_gemm_relu(A, B)
+    As, Bs = _stored(A, ta), _stored(B, tb)
+    got, pre, absdot = oracle.gemm_relu_f16(As, Bs, want_pre=True, want_absdot=True, trans_a=ta, trans_b=tb)
+    assert got.shape == (M, N)
+    for i in range(M):
+        for j in range(N):
+            bound = Fraction(K) * Fraction(1, 2 ** 53) * Fraction(absdot[i, j])
+            assert abs(Fraction(pre[i, j]) - sums[i][j]) <= bound
+            if got[i, j] != want[i, j]:
+                lo = exact_rne_f16(max(sums[i][j] - bound, Fraction(0)))
+                hi = exact_rne_f16(max(sums[i][j] + bound, Fraction(0)))
+                assert lo != hi, f"({i},{j}) layout {ta},{tb}"
+    ii, jj = np.divmod(np.arange(M * N), N)
+    pts = oracle.gemm_relu_f16_points(As, Bs, ii, jj, trans_a=ta, trans_b=tb)
+    assert np.array_equal(pts, got.ravel())
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_transposed_integer_exact(ta, tb):
+    # integer-valued inputs: every double sum is exact, so the result is the
+    # int64 matrix product of the logical operands, bit for bit
+    M, N, K = 19, 23, 40
+    a, b = workloads.make_inputs(M, N, K, dist="intsmall", seed=5)
+    A, B = workloads.as_u16(a), workloads.as_u16(b)
+    s = a.numpy().astype(np.int64) @ b.numpy().astype(np.int64)
+    want = np.maximum(s, 0).astype(np.float16).view(np.uint16)
+    got = oracle.gemm_relu_f16(_stored(A, ta), _stored(B, tb), trans_a=ta, trans_b=tb)
+    assert np.array_equal(got, want)
+    # rows and points of the bias + GELU form read the operands the same way
+    bias = f16_bits(np.linspace(-3, 3, N))
+    full = oracle.gemm_bias_gelu_f16(A, B, bias)
+    part = oracle.gemm_bias_gelu_f16(_stored(A, ta), _stored(B, tb), bias, rows=(4, 11), trans_a=ta, trans_b=tb)
+    assert np.array_equal(part, full[4:11])
+    ii = np.array([0, 18, 7, 3]); jj = np.array([22, 0, 11, 5])
+    pts = oracle.gemm_bias_gelu_f16_points(_stored(A, ta), _stored(B, tb), bias, ii, jj, trans_a=ta, trans_b=tb)
+    assert np.array_equal(pts, full[ii, jj])
+
+
+def test_transposed_shapes_checked():
+    A = np.zeros((4, 3), dtype=np.uint16)   # stored K x M with trans_a: M = 3, K = 4
+    B = np.zeros((5, 4), dtype=np.uint16)   # stored N x K with trans_b: N = 5
+    assert oracle.gemm_relu_f16(A, B, trans_a=True, trans_b=True).shape == (3, 5)
+    with pytest.raises(ValueError):
+        oracle.gemm_relu_f16(A, B, trans_a=True)   # op(B) would be 5 x 4: K differs
+
+
+TRANS_MUTANTS = {
+    "at_read_as_stored": ("return op_a ? A[k * M + i] : A[i * K + k];", "return op_a ? A[i * K + k] : A[i * K + k];"),
+    "at_wrong_stride": ("return op_a ? A[k * M + i] : A[i * K + k];", "return op_a ? A[(k * K + i) % (M * K)] : A[i * K + k];"),
+    "bt_read_as_stored": ("return op_b ? B[j * K + k] : B[k * N + j];", "return op_b ? B[k * N + j] : B[k * N + j];"),
+    "bt_wrong_stride": ("return op_b ? B[j * K + k] : B[k * N + j];", "return op_b ? B[(j * N + k) % (N * K)] : B[k * N + j];"),
+}
+
+
+def _trans_pin_suite(mod) -> list[str]:
+    fails = []
+    for ta, tb in LAYOUTS:
+        for M, N, K in ((3, 5, 7), (6, 4, 9)):
+            a, b = workloads.make_inputs(M, N, K, dist="intsmall", seed=M + N + K + 2 * ta + tb)
+            A, B = workloads.as_u16(a), workloads.as_u16(b)
+            s = a.numpy().astype(np.int64) @ b.numpy().astype(np.int64)
+            want = np.maximum(s, 0).astype(np.float16).view(np.uint16)
+            try:
+                got = mod.gemm_relu_f16(_stored(A, ta), _stored(B, tb), trans_a=ta, trans_b=tb)
+            except Exception as e:  # a crash counts as caught
+                fails.append(f"{ta}{tb}:{e}")
+                continue
+            if not np.array_equal(got, want):
+                fails.append(f"{ta}{tb}{(M, N, K)}")
+    return fails
+
+
+def test_transposed_pins_pass_on_real_oracle():
+    assert _trans_pin_suite(oracle) == []
+
+
+@pytest.mark.parametrize("mutant", sorted(TRANS_MUTANTS))
+def test_planted_transpose_mistake_is_caught(mutant, tmp_path):
+    import importlib.util
+    src_dir = os.path.join(os.path.dirname(HERE), "oracle")
+    old, new = TRANS_MUTANTS[mutant]
+    text = open(os.path.join(src_dir, "gemm_relu_oracle.c")).read()
+    assert text.count(old) == 1, f"mutation anchor for {mutant} not found"
+    dst = tmp_path / "oracle_mut"
+    dst.mkdir()
+    (dst / "gemm_relu_oracle.c").write_text(text.replace(old, new, 1))
+    shutil.copy(os.path.join(src_dir, "__init__.py"), dst / "__init__.py")
+    spec = importlib.util.spec_from_file_location(f"oracle_tmut_{mutant}", dst / "__init__.py")
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert _trans_pin_suite(mod) != [], f"planted mistake {mutant} went unnoticed"
+
