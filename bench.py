@@ -50,10 +50,11 @@ def source_hash(tile: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, tile: str) -> float | None:
+def measured_traffic(workload: str, tile: str, layout: str = "nn", epilogue: str = "relu") -> float | None:
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current source of the kernel that runs `tile`;
-    otherwise None."""
+    was taken on the current source of the kernel that runs `tile`, with the
+    same operand layout and epilogue (entries without those keys are "nn" and
+    "relu"); otherwise None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     cur = source_hash(tile)
@@ -71,7 +72,8 @@ def measured_traffic(workload: str, tile: str) -> float | None:
     if entry:
         entries.append(entry)
     for e in entries:
-        if e.get("workload") == workload and e.get("tile") == tile and e.get("kernel_source_sha256") == cur:
+        if (e.get("workload") == workload and e.get("tile") == tile and e.get("kernel_source_sha256") == cur
+                and e.get("layout", "nn") == layout and e.get("epilogue", "relu") == epilogue):
             try:
                 return float(e["traffic_bytes_per_launch"])
             except (KeyError, ValueError):
@@ -82,7 +84,8 @@ def measured_traffic(workload: str, tile: str) -> float | None:
 ROTATE_BYTES = 768 << 20  # well above the 256 MB last-level (MALL) cache
 
 
-def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0, epilogue: str = "relu"):
+def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0, epilogue: str = "relu",
+             layout: str = "nn"):
     """Times `steps` back-to-back launches on one stream, bracketed by two
     events on that stream. Successive launches cycle through R copies of
     (A, B) with R * (|A| + |B|) >= 768 MiB (at most 8), so the inputs of a
@@ -96,15 +99,22 @@ def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0, epilog
     launch cost, which otherwise dominates for kernels of a few microseconds.
 
     Also times 200 single launches, each between its own pair of events, for
-    the duration of one launch."""
+    the duration of one launch.
+
+    `layout` ("nn", "nt", "tn", "tt") stores A as K x M (t in first place)
+    and/or B as N x K (t in second place) and calls the transposed-operand
+    entry points; the product is the same."""
     import torch
     import tiled_dense_gemm_f16_amd as gr
 
     a, b = workloads.workload_inputs(w)
+    ta, tb = layout[0] == "t", layout[1] == "t"
+    a_st = a.t().contiguous() if ta else a
+    b_st = b.t().contiguous() if tb else b
     in_bytes = 2 * (w.M * w.K + w.K * w.N)
     rot = max(1, min(8, -(-ROTATE_BYTES // max(in_bytes, 1))))
-    ads = [a.cuda() for _ in range(rot)]
-    bds = [b.cuda() for _ in range(rot)]
+    ads = [a_st.cuda() for _ in range(rot)]
+    bds = [b_st.cuda() for _ in range(rot)]
     c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
     stream = torch.cuda.Stream()
     opts = gr.make_opts(tile)
@@ -113,13 +123,13 @@ def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0, epilog
         gen = torch.Generator(device="cpu")
         gen.manual_seed(w.seed + 1)
         bias = (torch.randn(w.N, generator=gen) * (w.K ** 0.5) * w.scale * w.scale).half().cuda()
-        call = gr.gemm_bias_gelu_f16_ex
-        args = [(w.M, w.N, w.K, ads[i].data_ptr(), bds[i].data_ptr(), bias.data_ptr(), c.data_ptr(),
-                 stream.cuda_stream, opts) for i in range(rot)]
+        call = gr.gemm_bias_gelu_f16_op
+        args = [(w.M, w.N, w.K, ads[i].data_ptr(), int(ta), bds[i].data_ptr(), int(tb), bias.data_ptr(),
+                 c.data_ptr(), stream.cuda_stream, opts) for i in range(rot)]
     else:
-        call = gr.gemm_relu_f16_ex
-        args = [(w.M, w.N, w.K, ads[i].data_ptr(), bds[i].data_ptr(), c.data_ptr(), stream.cuda_stream, opts)
-                for i in range(rot)]
+        call = gr.gemm_relu_f16_op
+        args = [(w.M, w.N, w.K, ads[i].data_ptr(), int(ta), bds[i].data_ptr(), int(tb), c.data_ptr(),
+                 stream.cuda_stream, opts) for i in range(rot)]
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for i in range(warmup):
@@ -158,11 +168,13 @@ def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0, epilog
             e1.record(stream)
         torch.cuda.synchronize()
     per = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
-    tile_id = gr.select_tile(w.M, w.N, w.K, ads[0].data_ptr(), bds[0].data_ptr(), c.data_ptr()) if tile is None else tile
+    tile_id = (gr.select_tile(w.M, w.N, w.K, ads[0].data_ptr(), bds[0].data_ptr(), c.data_ptr(), trans_a=ta,
+                              trans_b=tb) if tile is None else tile)
     return {"total_ms": total_ms, "steps": steps, "ms_per_step": total_ms / steps,
             "launch_ms_mean": float(per.mean()), "launch_ms_median": float(np.median(per)),
             "launch_ms_min": float(per.min()), "tile": gr.tile_name(tile_id) if tile_id >= 0 else "generic",
-            "rotation": rot, "graph_batch": graph_batch, "epilogue": epilogue, "c": c, "a": a, "b": b}
+            "rotation": rot, "graph_batch": graph_batch, "epilogue": epilogue, "layout": layout,
+            "c": c, "a": a, "b": b}
 
 
 def cpu_baseline(w, gpu_c, target_s: float = 12.0):
@@ -208,13 +220,14 @@ def result_line(w, r, steps, warmup, cpu=None):
         achieved = w.min_bytes / launch_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = measured_traffic(w.name, r["tile"])
+    roof["traffic"] = measured_traffic(w.name, r["tile"], r["layout"], r["epilogue"])
     line = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": r["steps"],
             "warmup": warmup, "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f16", "accum_dtype": "f32", "data": "synthetic",
             "pct_of_fp16_peak": round(100 * value / PEAK_FP16_TFLOPS, 2),
             "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dist": w.dist,
                        "scale": w.scale, "seed": w.seed, "tile": r["tile"], "epilogue": r["epilogue"],
+                       "layout": r["layout"],
                        "input_copies_rotated": r["rotation"],
                        "parallelism": "single GPU"},
             "roofline": roof,
@@ -241,6 +254,8 @@ def main(argv=None) -> int:
     ap.add_argument("--all", action="store_true", help="also time every workload (lines on stderr)")
     ap.add_argument("--epilogue", choices=("relu", "bias_gelu"), default="relu",
                     help="relu: C = ReLU(A @ B) (the headline); bias_gelu: C = GELU(A @ B + bias)")
+    ap.add_argument("--layout", choices=("nn", "nt", "tn", "tt"), default="nn",
+                    help="operand layouts: A stored K x M (t first) and/or B stored N x K (t second)")
     ap.add_argument("--graph", type=int, default=50, metavar="G",
                     help="capture G launches per HIP graph and replay it (0: launch one by one from the host)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -272,18 +287,19 @@ def main(argv=None) -> int:
     gr.load()
 
     w = workloads.BY_NAME[args.workload]
-    r = time_gpu(w, args.steps, args.warmup, args.tile, args.graph, args.epilogue)
+    r = time_gpu(w, args.steps, args.warmup, args.tile, args.graph, args.epilogue, args.layout)
     print(f"[bench] {w.name}: {r['ms_per_step'] * 1e3:.2f} us/step (graph batch {r['graph_batch']}), "
           f"single launches {r['launch_ms_mean'] * 1e3:.2f} us, tile {r['tile']}", file=sys.stderr, flush=True)
     if args.all:
         for ow in workloads.ALL:
             if ow is w:
                 continue
-            orr = time_gpu(ow, max(args.steps // 4, 50), max(args.warmup // 4, 10), None, args.graph, args.epilogue)
+            orr = time_gpu(ow, max(args.steps // 4, 50), max(args.warmup // 4, 10), None, args.graph, args.epilogue,
+                           args.layout)
             print(json.dumps(result_line(ow, orr, max(args.steps // 4, 50), max(args.warmup // 4, 10))),
                   file=sys.stderr, flush=True)
     cpu = None
-    if not args.no_cpu_baseline and args.epilogue == "relu":
+    if not args.no_cpu_baseline and args.epilogue == "relu" and args.layout == "nn":
         cpu = cpu_baseline(w, r, args.cpu_seconds)
     print(json.dumps(result_line(w, r, args.steps, args.warmup, cpu)), flush=True)
     return 0

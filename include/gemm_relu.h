@@ -172,6 +172,34 @@ typedef struct gemm_relu_tile_desc {
 int gemm_relu_tile_info(int tile, gemm_relu_tile_desc* desc);
 
 /*
+ * Transposed operands: the transpose_A / transpose_B flags of the tile-level
+ * product in the same TileLang example (the notes under the program in
+ * "Escribamos un GEMM"). C = epilogue(op(A) @ op(B)), where
+ *   op_a = GEMM_RELU_OP_N: A is M x K as stored (row-major, leading dim K);
+ *   op_a = GEMM_RELU_OP_T: A is stored K x M (leading dim M) and op(A) is its
+ *                          transpose;
+ *   op_b = GEMM_RELU_OP_N: B is K x N as stored (leading dim N);
+ *   op_b = GEMM_RELU_OP_T: B is stored N x K (leading dim K) and op(B) is its
+ *                          transpose.
+ * C is always M x N row-major (leading dim N). Everything else -- sizes,
+ * accumulation, epilogue, rounding, ownership, errors -- is as for the
+ * untransposed calls; an op value other than N or T gives GEMM_RELU_EINVAL.
+ * The vector kernels need the leading dimensions of A (K or M), B (N or K)
+ * and C (N) to be multiples of 8 and 16-byte aligned pointers; other shapes
+ * take the element-wise path.
+ */
+#define GEMM_RELU_OP_N 0
+#define GEMM_RELU_OP_T 1
+
+/* C = ReLU(op(A) @ op(B)); opts as for gemm_relu_f16_ex (may be NULL). */
+int gemm_relu_f16_op(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B, int op_b,
+                     void* C, void* stream, const gemm_relu_opts* opts);
+
+/* C = GELU(op(A) @ op(B) + bias); bias and opts as for gemm_bias_gelu_f16_ex. */
+int gemm_bias_gelu_f16_op(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B, int op_b,
+                          const void* bias, void* C, void* stream, const gemm_relu_opts* opts);
+
+/*
  * The tile the library would use for this problem without opts, or -1 for the
  * generic element-wise path that serves shapes whose K or N is not a multiple
  * of 8 or whose pointers are not 16-byte aligned (pass NULL pointers to ask
@@ -179,6 +207,10 @@ int gemm_relu_tile_info(int tile, gemm_relu_tile_desc* desc);
  */
 int gemm_relu_select_tile(int64_t M, int64_t N, int64_t K,
                           const void* A, const void* B, const void* C);
+
+/* Same, for operand layouts op_a and op_b (-1 also for an invalid op). */
+int gemm_relu_select_tile_op(int64_t M, int64_t N, int64_t K, int op_a, int op_b,
+                             const void* A, const void* B, const void* C);
 
 #ifdef __cplusplus
 }

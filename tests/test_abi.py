@@ -195,6 +195,42 @@ def test_bias_gelu_arguments_rejected():
     assert gr.gemm_bias_gelu_f16(0, 5, 5, 0, FAKE, FAKE * 4, 0) == gr.OK
 
 
+def test_transposed_operand_arguments():
+    # op values other than N (0) and T (1) are rejected before any HIP call
+    for op_a, op_b in ((2, 0), (0, -1), (7, 7)):
+        assert gr.gemm_relu_f16_op(4, 4, 4, FAKE, op_a, FAKE * 2, op_b, FAKE * 3) == gr.EINVAL
+        assert gr.gemm_bias_gelu_f16_op(4, 4, 4, FAKE, op_a, FAKE * 2, op_b, FAKE * 4, FAKE * 3) == gr.EINVAL
+    # the usual checks apply to every layout
+    for op_a in (gr.OP_N, gr.OP_T):
+        for op_b in (gr.OP_N, gr.OP_T):
+            assert gr.gemm_relu_f16_op(-1, 4, 4, FAKE, op_a, FAKE * 2, op_b, FAKE * 3) == gr.EINVAL
+            assert gr.gemm_relu_f16_op(4, 4, 4, 0, op_a, FAKE * 2, op_b, FAKE * 3) == gr.EINVAL
+            assert gr.gemm_relu_f16_op(4, 4, 4, FAKE, op_a, FAKE * 2, op_b, FAKE * 3 + 1) == gr.EUNSUPPORTED
+            assert gr.gemm_relu_f16_op(0, 4, 4, 0, op_a, FAKE, op_b, 0) == gr.OK
+    # the vector kernels need the stored leading dimensions to be multiples of
+    # 8: K or M for A, N or K for B, and N for C
+    assert gr.select_tile(60, 64, 64) >= 0
+    assert gr.select_tile(60, 64, 64, trans_a=True) == -1
+    assert gr.select_tile(64, 64, 60) == -1  # A's leading dimension is K
+    assert gr.select_tile(64, 64, 60, trans_a=True) >= 0  # neither stored operand has K as leading dimension
+    assert gr.select_tile(64, 64, 60, trans_a=True, trans_b=True) == -1  # B's is
+    assert gr.select_tile(64, 60, 64, trans_b=True) == -1
+    assert gr.select_tile(64, 64, 64, trans_a=True, trans_b=True) >= 0
+    assert gr.load().gemm_relu_select_tile_op(64, 64, 64, 3, 0, None, None, None) == -1
+
+
+def test_python_wrapper_shapes_with_transposes():
+    import torch
+    a = torch.zeros(6, 4, dtype=torch.float16)   # stored K x M with trans_a: M = 4, K = 6
+    b = torch.zeros(5, 6, dtype=torch.float16)   # stored N x K with trans_b: K = 6
+    with pytest.raises(ValueError, match="do not chain"):
+        gr.gemm_relu(a, b)
+    with pytest.raises(ValueError, match="do not chain"):
+        gr.gemm_relu(a, b, trans_a=True)
+    with pytest.raises(ValueError, match="same GPU"):  # shapes chain; CPU tensors are not device memory
+        gr.gemm_relu(a, b, trans_a=True, trans_b=True)
+
+
 def test_empty_output_is_a_no_op():
     # M == 0 or N == 0: success without touching the device (NULL is fine then)
     assert gr.gemm_relu_f16(0, 5, 5, 0, FAKE, 0) == gr.OK

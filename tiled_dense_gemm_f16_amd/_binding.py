@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(PKG, "libgemm_relu.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, 1, 2, 3, 4
 TILE_AUTO = -1
+OP_N, OP_T = 0, 1  # operand as stored / stored transposed
 ORDER_DEFAULT, ORDER_ROW_MAJOR = 0, 1
 
 
@@ -46,9 +47,9 @@ class TileDesc(ctypes.Structure):
 _lock = threading.Lock()
 _lib = None
 
-EXPORTED = ("gemm_relu_f16", "gemm_relu_f16_ex", "gemm_bias_gelu_f16", "gemm_bias_gelu_f16_ex",
-            "gemm_relu_strerror", "gemm_relu_tile_count", "gemm_relu_tile_name", "gemm_relu_tile_info",
-            "gemm_relu_select_tile")
+EXPORTED = ("gemm_relu_f16", "gemm_relu_f16_ex", "gemm_relu_f16_op", "gemm_bias_gelu_f16",
+            "gemm_bias_gelu_f16_ex", "gemm_bias_gelu_f16_op", "gemm_relu_strerror", "gemm_relu_tile_count",
+            "gemm_relu_tile_name", "gemm_relu_tile_info", "gemm_relu_select_tile", "gemm_relu_select_tile_op")
 
 
 def load():
@@ -70,6 +71,12 @@ def load():
         lib.gemm_bias_gelu_f16.restype = i32
         lib.gemm_bias_gelu_f16_ex.argtypes = [i64, i64, i64, p, p, p, p, p, ctypes.POINTER(Opts)]
         lib.gemm_bias_gelu_f16_ex.restype = i32
+        lib.gemm_relu_f16_op.argtypes = [i64, i64, i64, p, i32, p, i32, p, p, ctypes.POINTER(Opts)]
+        lib.gemm_relu_f16_op.restype = i32
+        lib.gemm_bias_gelu_f16_op.argtypes = [i64, i64, i64, p, i32, p, i32, p, p, p, ctypes.POINTER(Opts)]
+        lib.gemm_bias_gelu_f16_op.restype = i32
+        lib.gemm_relu_select_tile_op.argtypes = [i64, i64, i64, i32, i32, p, p, p]
+        lib.gemm_relu_select_tile_op.restype = i32
         lib.gemm_relu_strerror.argtypes = [i32]
         lib.gemm_relu_strerror.restype = ctypes.c_char_p
         lib.gemm_relu_tile_count.argtypes = []
@@ -125,6 +132,20 @@ def gemm_bias_gelu_f16_ex(M: int, N: int, K: int, A: int, B: int, bias: int, C: 
                                         ctypes.byref(opts) if opts is not None else None)
 
 
+def gemm_relu_f16_op(M: int, N: int, K: int, A: int, op_a: int, B: int, op_b: int, C: int, stream: int = 0,
+                     opts: Opts | None = None) -> int:
+    """Raw C-ABI call of C = ReLU(op(A) @ op(B)); returns the status code."""
+    return load().gemm_relu_f16_op(M, N, K, A or None, int(op_a), B or None, int(op_b), C or None, stream or None,
+                                   ctypes.byref(opts) if opts is not None else None)
+
+
+def gemm_bias_gelu_f16_op(M: int, N: int, K: int, A: int, op_a: int, B: int, op_b: int, bias: int, C: int,
+                          stream: int = 0, opts: Opts | None = None) -> int:
+    """Raw C-ABI call of C = GELU(op(A) @ op(B) + bias); returns the status code."""
+    return load().gemm_bias_gelu_f16_op(M, N, K, A or None, int(op_a), B or None, int(op_b), bias or None,
+                                        C or None, stream or None, ctypes.byref(opts) if opts is not None else None)
+
+
 def tile_count() -> int:
     return int(load().gemm_relu_tile_count())
 
@@ -140,23 +161,30 @@ def tile_info(tile: int) -> dict:
     return d.as_dict()
 
 
-def select_tile(M: int, N: int, K: int, A: int = 0, B: int = 0, C: int = 0) -> int:
-    return int(load().gemm_relu_select_tile(M, N, K, A or None, B or None, C or None))
+def select_tile(M: int, N: int, K: int, A: int = 0, B: int = 0, C: int = 0, *, trans_a: bool = False,
+                trans_b: bool = False) -> int:
+    return int(load().gemm_relu_select_tile_op(M, N, K, int(trans_a), int(trans_b), A or None, B or None,
+                                               C or None))
 
 
-def _check_operands(a, b, out):
+def _check_operands(a, b, out, trans_a=False, trans_b=False):
+    """a is the stored A ([M, K], or [K, M] with trans_a); b the stored B ([K, N],
+    or [N, K] with trans_b)."""
     import torch
 
     if a.dtype != torch.float16 or b.dtype != torch.float16:
         raise TypeError("a and b must be float16")
-    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
-        raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not chain")
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be matrices")
+    M, K = (a.shape[1], a.shape[0]) if trans_a else (a.shape[0], a.shape[1])
+    K2, N = (b.shape[1], b.shape[0]) if trans_b else (b.shape[0], b.shape[1])
+    if K != K2:
+        raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not chain "
+                         f"(trans_a={trans_a}, trans_b={trans_b})")
     if not (a.is_cuda and b.is_cuda) or a.device != b.device:
         raise ValueError("a and b must be on the same GPU")
     if not (a.is_contiguous() and b.is_contiguous()):
         raise ValueError("a and b must be contiguous row-major")
-    M, K = a.shape
-    N = b.shape[1]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=a.device)
     else:
@@ -167,31 +195,34 @@ def _check_operands(a, b, out):
     return M, N, K, out
 
 
-def gemm_relu(a, b, out=None, *, tile: int | None = None, block_order: int = ORDER_DEFAULT,
-              group_m: int = 0, stream=None):
-    """C = ReLU(a @ b) for fp16 CUDA(HIP) tensors a[M,K], b[K,N]; returns out[M,N].
+def gemm_relu(a, b, out=None, *, trans_a: bool = False, trans_b: bool = False, tile: int | None = None,
+              block_order: int = ORDER_DEFAULT, group_m: int = 0, stream=None):
+    """C = ReLU(op(a) @ op(b)) for fp16 CUDA(HIP) tensors; returns out[M,N].
 
-    Enqueued on torch's current stream (or ``stream``); does not synchronise.
+    a is [M, K] (or [K, M] with trans_a, op(a) = a.T), b is [K, N] (or [N, K]
+    with trans_b). Enqueued on torch's current stream (or ``stream``); does not
+    synchronise.
     """
     import torch
 
-    M, N, K, out = _check_operands(a, b, out)
+    M, N, K, out = _check_operands(a, b, out, trans_a, trans_b)
     s = stream if stream is not None else torch.cuda.current_stream(a.device)
     opts = make_opts(tile, block_order, group_m)
     with torch.cuda.device(a.device):
-        _check(gemm_relu_f16_ex(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), s.cuda_stream, opts))
+        _check(gemm_relu_f16_op(M, N, K, a.data_ptr(), int(trans_a), b.data_ptr(), int(trans_b), out.data_ptr(),
+                                s.cuda_stream, opts))
     return out
 
 
-def gemm_bias_gelu(a, b, bias, out=None, *, tile: int | None = None, block_order: int = ORDER_DEFAULT,
-                   group_m: int = 0, stream=None):
-    """C = GELU(a @ b + bias) for fp16 tensors a[M,K], b[K,N], bias[N]; returns out[M,N].
+def gemm_bias_gelu(a, b, bias, out=None, *, trans_a: bool = False, trans_b: bool = False,
+                   tile: int | None = None, block_order: int = ORDER_DEFAULT, group_m: int = 0, stream=None):
+    """C = GELU(op(a) @ op(b) + bias) for fp16 tensors (layouts as gemm_relu), bias[N]; returns out[M,N].
 
     Enqueued on torch's current stream (or ``stream``); does not synchronise.
     """
     import torch
 
-    M, N, K, out = _check_operands(a, b, out)
+    M, N, K, out = _check_operands(a, b, out, trans_a, trans_b)
     if bias.dtype != torch.float16 or bias.dim() != 1 or bias.shape[0] != N:
         raise ValueError(f"bias must be float16 [{N}]")
     if not bias.is_cuda or bias.device != a.device or not bias.is_contiguous():
@@ -199,6 +230,6 @@ def gemm_bias_gelu(a, b, bias, out=None, *, tile: int | None = None, block_order
     s = stream if stream is not None else torch.cuda.current_stream(a.device)
     opts = make_opts(tile, block_order, group_m)
     with torch.cuda.device(a.device):
-        _check(gemm_bias_gelu_f16_ex(M, N, K, a.data_ptr(), b.data_ptr(), bias.data_ptr(), out.data_ptr(),
-                                     s.cuda_stream, opts))
+        _check(gemm_bias_gelu_f16_op(M, N, K, a.data_ptr(), int(trans_a), b.data_ptr(), int(trans_b),
+                                     bias.data_ptr(), out.data_ptr(), s.cuda_stream, opts))
     return out

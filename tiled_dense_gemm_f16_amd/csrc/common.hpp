@@ -37,6 +37,9 @@ struct Args {
     int tiles_m, tiles_n;
     int group_m;
     int order;  // GEMM_RELU_ORDER_*
+    // operand layouts: 0 = as stored (A: M x K, B: K x N), 1 = the stored
+    // matrix is the transpose (A: K x M, leading dim M; B: N x K, leading dim K)
+    int trans_a, trans_b;
     // epilogue: kActRelu, or kActBiasGelu with bias[N] (fp16, one per column)
     int act;
     const uint16_t* bias;

@@ -58,30 +58,67 @@ using K64 = gemm_relu::splitk::Cfg<4, GR_SPLITK_NW, GR_SPLITK_D>;  // split-K, 6
 
 using LaunchFn = hipError_t (*)(const Args&, hipStream_t);
 
+// Each launcher instantiates its kernel for the four operand layouts
+// (A as stored or transposed) x (B as stored or transposed).
+template <class T, bool VEC, bool TA, bool TB>
+void launch_staged_as(const Args& a, hipStream_t s)
+{
+    hipLaunchKernelGGL((gemm_relu::staged::staged_kernel<T, VEC, TA, TB>), dim3(a.tiles_m * a.tiles_n), dim3(T::NT),
+                       0, s, a);
+}
+
 template <class T, bool VEC>
 hipError_t launch_staged(const Args& a, hipStream_t s)
 {
-    const int blocks = a.tiles_m * a.tiles_n;
-    hipLaunchKernelGGL((gemm_relu::staged::staged_kernel<T, VEC>), dim3(blocks), dim3(T::NT), 0, s, a);
+    switch (2 * a.trans_a + a.trans_b) {
+    case 0: launch_staged_as<T, VEC, false, false>(a, s); break;
+    case 1: launch_staged_as<T, VEC, false, true>(a, s); break;
+    case 2: launch_staged_as<T, VEC, true, false>(a, s); break;
+    default: launch_staged_as<T, VEC, true, true>(a, s); break;
+    }
     return hipGetLastError();
+}
+
+template <class T, bool TA, bool TB>
+void launch_pipelined_as(const Args& a, hipStream_t s)
+{
+    const int blocks = a.tiles_m * a.tiles_n;
+    if (a.K % T::BK == 0)
+        hipLaunchKernelGGL((gemm_relu::pipelined::pipelined_kernel<T, true, TA, TB>), dim3(blocks), dim3(T::NT), 0,
+                           s, a);
+    else
+        hipLaunchKernelGGL((gemm_relu::pipelined::pipelined_kernel<T, false, TA, TB>), dim3(blocks), dim3(T::NT), 0,
+                           s, a);
 }
 
 template <class T>
 hipError_t launch_pipelined(const Args& a, hipStream_t s)
 {
-    const int blocks = a.tiles_m * a.tiles_n;
-    if (a.K % T::BK == 0)
-        hipLaunchKernelGGL((gemm_relu::pipelined::pipelined_kernel<T, true>), dim3(blocks), dim3(T::NT), 0, s, a);
-    else
-        hipLaunchKernelGGL((gemm_relu::pipelined::pipelined_kernel<T, false>), dim3(blocks), dim3(T::NT), 0, s, a);
+    switch (2 * a.trans_a + a.trans_b) {
+    case 0: launch_pipelined_as<T, false, false>(a, s); break;
+    case 1: launch_pipelined_as<T, false, true>(a, s); break;
+    case 2: launch_pipelined_as<T, true, false>(a, s); break;
+    default: launch_pipelined_as<T, true, true>(a, s); break;
+    }
     return hipGetLastError();
+}
+
+template <class T, bool TA, bool TB>
+void launch_splitk_as(const Args& a, hipStream_t s)
+{
+    hipLaunchKernelGGL((gemm_relu::splitk::splitk_kernel<T, TA, TB>), dim3(a.tiles_m * a.tiles_n * a.splits),
+                       dim3(T::NT), 0, s, a);
 }
 
 template <class T>
 hipError_t launch_splitk(const Args& a, hipStream_t s)
 {
-    const int blocks = a.tiles_m * a.tiles_n * a.splits;
-    hipLaunchKernelGGL((gemm_relu::splitk::splitk_kernel<T>), dim3(blocks), dim3(T::NT), 0, s, a);
+    switch (2 * a.trans_a + a.trans_b) {
+    case 0: launch_splitk_as<T, false, false>(a, s); break;
+    case 1: launch_splitk_as<T, false, true>(a, s); break;
+    case 2: launch_splitk_as<T, true, false>(a, s); break;
+    default: launch_splitk_as<T, true, true>(a, s); break;
+    }
     return hipGetLastError();
 }
 
@@ -156,11 +193,16 @@ void choose_splits(int64_t K, int64_t tiles, int& splits, int& kc)
     if (splits < 1) splits = 1;
 }
 
-bool fast_path_ok(int64_t N, int64_t K, const void* A, const void* B, const void* C)
+// The vector kernels: 16-byte aligned pointers and leading dimensions (K or M
+// for A, N or K for B, N for C) that are multiples of 8 halves.
+bool fast_path_ok(int64_t M, int64_t N, int64_t K, bool ta, bool tb, const void* A, const void* B, const void* C)
 {
     const uintptr_t mis = ((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 15u;
-    // 32-bit in-tile buffer offsets: BM*K*2 and BK*N*2 must stay below 2^31
-    return (K % 8 == 0) && (N % 8 == 0) && mis == 0 && K <= (1 << 22) && N <= (1 << 24);
+    const int64_t lda = ta ? M : K, ldb = tb ? K : N;
+    // 32-bit in-tile buffer offsets: 256 rows of K halves, 64 rows of M or N
+    // halves, stay below 2^31 bytes
+    return lda % 8 == 0 && ldb % 8 == 0 && N % 8 == 0 && mis == 0 && K <= (1 << 22) && N <= (1 << 24) &&
+           (!ta || M <= (1 << 24));
 }
 
 // The split-K kernel addresses A with 32-bit offsets.
@@ -344,9 +386,12 @@ int check_device(int& dev)
 
 // Validated call -> tile choice, split-K workspace, launch. `act` selects the
 // epilogue (kActRelu, or kActBiasGelu with `bias`).
-int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, void* stream,
+int run(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B, int op_b, void* C, void* stream,
         const gemm_relu_opts* opts, int act, const void* bias)
 {
+    if ((op_a != GEMM_RELU_OP_N && op_a != GEMM_RELU_OP_T) || (op_b != GEMM_RELU_OP_N && op_b != GEMM_RELU_OP_T))
+        return GEMM_RELU_EINVAL;
+    const bool ta = op_a == GEMM_RELU_OP_T, tb = op_b == GEMM_RELU_OP_T;
     int rc = validate(M, N, K, A, B, C, opts);
     if (rc != GEMM_RELU_OK) return rc;
     if (act == gemm_relu::kActBiasGelu) {
@@ -358,7 +403,7 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, 
     rc = check_device(dev);
     if (rc != GEMM_RELU_OK) return rc;
 
-    const bool vec = fast_path_ok(N, K, A, B, C);
+    const bool vec = fast_path_ok(M, N, K, ta, tb, A, B, C);
     const int tile =
         (opts && opts->tile != GEMM_RELU_TILE_AUTO) ? opts->tile : (vec ? choose_tile(M, N, K) : kGenericTile);
     // the split-K tiles have no element-wise instance: unaligned shapes take
@@ -378,6 +423,8 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, 
     a.tiles_n = (int)((N + te.desc.bn - 1) / te.desc.bn);
     a.group_m = (opts && opts->group_m > 0) ? opts->group_m : te.desc.default_group_m;
     a.order = opts ? opts->block_order : GEMM_RELU_ORDER_DEFAULT;
+    a.trans_a = ta ? 1 : 0;
+    a.trans_b = tb ? 1 : 0;
     a.act = act;
     a.bias = static_cast<const uint16_t*>(bias);
     a.partial = nullptr;
@@ -432,31 +479,51 @@ int gemm_relu_tile_info(int tile, gemm_relu_tile_desc* desc)
 
 int gemm_relu_select_tile(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* C)
 {
-    if (!fast_path_ok(N, K, A, B, C)) return -1;
+    return gemm_relu_select_tile_op(M, N, K, GEMM_RELU_OP_N, GEMM_RELU_OP_N, A, B, C);
+}
+
+int gemm_relu_select_tile_op(int64_t M, int64_t N, int64_t K, int op_a, int op_b, const void* A, const void* B,
+                             const void* C)
+{
+    if ((op_a != GEMM_RELU_OP_N && op_a != GEMM_RELU_OP_T) || (op_b != GEMM_RELU_OP_N && op_b != GEMM_RELU_OP_T))
+        return -1;
+    if (!fast_path_ok(M, N, K, op_a == GEMM_RELU_OP_T, op_b == GEMM_RELU_OP_T, A, B, C)) return -1;
     return choose_tile(M, N, K);
 }
 
 int gemm_relu_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C,
                      void* stream, const gemm_relu_opts* opts)
 {
-    return run(M, N, K, A, B, C, stream, opts, gemm_relu::kActRelu, nullptr);
+    return run(M, N, K, A, GEMM_RELU_OP_N, B, GEMM_RELU_OP_N, C, stream, opts, gemm_relu::kActRelu, nullptr);
 }
 
 int gemm_relu_f16(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, void* stream)
 {
-    return run(M, N, K, A, B, C, stream, nullptr, gemm_relu::kActRelu, nullptr);
+    return run(M, N, K, A, GEMM_RELU_OP_N, B, GEMM_RELU_OP_N, C, stream, nullptr, gemm_relu::kActRelu, nullptr);
+}
+
+int gemm_relu_f16_op(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B, int op_b, void* C,
+                     void* stream, const gemm_relu_opts* opts)
+{
+    return run(M, N, K, A, op_a, B, op_b, C, stream, opts, gemm_relu::kActRelu, nullptr);
 }
 
 int gemm_bias_gelu_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias,
                           void* C, void* stream, const gemm_relu_opts* opts)
 {
-    return run(M, N, K, A, B, C, stream, opts, gemm_relu::kActBiasGelu, bias);
+    return run(M, N, K, A, GEMM_RELU_OP_N, B, GEMM_RELU_OP_N, C, stream, opts, gemm_relu::kActBiasGelu, bias);
 }
 
 int gemm_bias_gelu_f16(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias,
                        void* C, void* stream)
 {
-    return run(M, N, K, A, B, C, stream, nullptr, gemm_relu::kActBiasGelu, bias);
+    return run(M, N, K, A, GEMM_RELU_OP_N, B, GEMM_RELU_OP_N, C, stream, nullptr, gemm_relu::kActBiasGelu, bias);
+}
+
+int gemm_bias_gelu_f16_op(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B, int op_b,
+                          const void* bias, void* C, void* stream, const gemm_relu_opts* opts)
+{
+    return run(M, N, K, A, op_a, B, op_b, C, stream, opts, gemm_relu::kActBiasGelu, bias);
 }
 
 }  // extern "C"

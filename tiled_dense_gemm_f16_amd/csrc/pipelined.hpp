@@ -31,6 +31,12 @@
 //    stored as it lies in memory, n-contiguous ([32][BN]), and read with the
 //    gfx950 transposing LDS load ds_read_b64_tr_b16, which hands each lane
 //    four k-values of one column: no register transpose.
+//  * Transposed operands (the transpose_A / transpose_B of the pages' tile
+//    product): every operand tile keeps the layout it has in memory. A
+//    stored K x M is staged m-contiguous ([32][BM]) and read with the
+//    transposing load; B stored N x K is staged k-contiguous ([BN][32]) and
+//    read with ds_read_b128. Fragments come out in the same lanes either way,
+//    so the matrix ops and the epilogue do not change.
 //  * XOR swizzles of the 16-byte chunk index (applied when choosing which
 //    global chunk each lane fetches) spread the fragment reads over the LDS
 //    banks; the direct loads themselves write 1 KiB linearly.
@@ -41,8 +47,10 @@
 //    fp16 tile; then every lane stores 16 consecutive bytes of a row, so each
 //    store instruction writes two full 512-byte rows of C.
 //
-// Requirements (checked on the host): K % 8 == 0, N % 8 == 0, A, B and C
-// 16-byte aligned, BM * K * 2 and 32 * N * 2 below 2^31.
+// Requirements (checked on the host): the leading dimension of each operand
+// (K or M for A, N or K for B) and N are multiples of 8, A, B and C are
+// 16-byte aligned, and every in-tile offset (BM * K, 32 * M, 32 * N, BN * K
+// halves) stays below 2^30.
 #pragma once
 
 #include <utility>
@@ -98,6 +106,20 @@ __device__ __forceinline__ int a_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; 
 // them over four pairs.
 __device__ __forceinline__ int b_swz(int kr) { return 2 * (kr & 3); }
 
+// Transposed A, staged m-contiguous: row kr of a stage holds BM halves. Its
+// transposing reads take 32-byte column pairs p and p + 1 (two 16-lane groups)
+// from four consecutive rows, so the XOR moves whole pairs by an even amount:
+// with rows of 256 bytes or more, 2 (kr % 4) pairs, which puts the eight
+// (row, pair) reads of 32 lanes on eight pairs of one 256-byte bank window;
+// with 128-byte rows (BM = 64), where rows kr and kr + 2 share a window, 2
+// pairs for kr / 2 odd.
+template <int BM>
+__device__ __forceinline__ int at_swz(int kr)
+{
+    if constexpr (BM >= 128) return 4 * (kr & 3);
+    else return 4 * ((kr >> 1) & 1);
+}
+
 // Epilogue C tile in LDS: row r (BN halves = 32 chunks of 16 B), logical chunk
 // c at physical chunk c ^ (r % 32), so the 32 rows that one store of the
 // accumulator layout touches land on 32 different chunks.
@@ -130,7 +152,7 @@ struct RegionPlan {
     static constexpr bool fits() { return PRE + 1 + NSLOT <= NMMA && NSLOT <= NMMA && LPT <= kPositions - PRE - 1; }
 };
 
-template <class T, bool KALIGNED>
+template <class T, bool KALIGNED, bool TA = false, bool TB = false>
 __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
 {
     // One LDS array per stage (A tile, then B tile): the compiler tracks
@@ -149,6 +171,7 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     };
     auto stage_b = [&]<int S>() -> uint16_t* { return stage_a.template operator()<S>() + T::A_HALVES; };
 
+    static_assert(!TA || (T::BM >= 64 && 512 % T::BM == 0), "a transposed A tile row is 64 to 512 halves");
     int tm, tn;
     tile_coords(p, tm, tn);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
@@ -160,24 +183,44 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
 
     // ---- per-lane global offsets of this wave's direct loads (bytes, relative
     // to the step's descriptor base: A + m0*K + k0 and B + k0*N) ----
+    // (A stored K x M: relative to A + k0*M; B stored N x K: to B + n0*K + k0)
     uint32_t a_off[T::A_LOADS_W];
     int a_kc[T::A_LOADS_W];  // logical k-chunk of the lane, for the K tail
 #pragma unroll
     for (int i = 0; i < T::A_LOADS_W; ++i) {
         const int gi = wave * T::A_LOADS_W + i;
-        const int row = gi * 16 + lane / 4;
-        const int c = (lane % 4) ^ a_swz(row);
-        a_kc[i] = c;
-        a_off[i] = (m0 + row < M) ? (uint32_t)(row * K + c * 8) * 2u : kOOB;
+        if constexpr (!TA) {
+            const int row = gi * 16 + lane / 4;
+            const int c = (lane % 4) ^ a_swz(row);
+            a_kc[i] = c;
+            a_off[i] = (m0 + row < M) ? (uint32_t)(row * K + c * 8) * 2u : kOOB;
+        } else {
+            // one 1 KiB load covers 512 / BM k-rows of BM halves
+            constexpr int LPR = T::BM / 8;
+            const int kr = gi * (64 / LPR) + lane / LPR;
+            const int c = (lane % LPR) ^ at_swz<T::BM>(kr);
+            a_kc[i] = 0;
+            // rows past K are cut off by the descriptor's byte count
+            a_off[i] = (m0 + c * 8 < M) ? (uint32_t)(kr * M + m0 + c * 8) * 2u : kOOB;
+        }
     }
     uint32_t b_off[T::B_LOADS_W];
+    int b_kc[T::B_LOADS_W];
 #pragma unroll
     for (int i = 0; i < T::B_LOADS_W; ++i) {
         const int gi = wave * T::B_LOADS_W + i;
-        const int kr = gi * 2 + lane / 32;
-        const int c = (lane % 32) ^ b_swz(kr);
-        // rows past K are cut off by the descriptor's byte count
-        b_off[i] = (n0 + c * 8 < N) ? (uint32_t)(kr * N + n0 + c * 8) * 2u : kOOB;
+        if constexpr (!TB) {
+            const int kr = gi * 2 + lane / 32;
+            const int c = (lane % 32) ^ b_swz(kr);
+            b_kc[i] = 0;
+            // rows past K are cut off by the descriptor's byte count
+            b_off[i] = (n0 + c * 8 < N) ? (uint32_t)(kr * N + n0 + c * 8) * 2u : kOOB;
+        } else {
+            const int row = gi * 16 + lane / 4;
+            const int c = (lane % 4) ^ a_swz(row);
+            b_kc[i] = c;
+            b_off[i] = (n0 + row < N) ? (uint32_t)(row * K + c * 8) * 2u : kOOB;
+        }
     }
 
     // Buffer descriptors of step kt. Steps past the end of K get empty
@@ -188,12 +231,13 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     auto descriptors = [&](int kt) -> Rsrc {
         const int k0 = kt * T::BK;
         const bool live = kt < nk;
-        int64_t arem = ((int64_t)(M - m0) * K - k0) * 2;
-        int64_t brem = ((int64_t)K - k0) * N * 2;
+        int64_t arem = TA ? ((int64_t)K - k0) * M * 2 : ((int64_t)(M - m0) * K - k0) * 2;
+        int64_t brem = TB ? ((int64_t)(N - n0) * K - k0) * 2 : ((int64_t)K - k0) * N * 2;
         arem = live ? arem : 0;
         brem = live ? brem : 0;
-        return {make_rsrc(p.A + (int64_t)m0 * K + k0, (uint64_t)arem),
-                make_rsrc(p.B + (int64_t)k0 * N, (uint64_t)brem)};
+        const uint16_t* abase = TA ? p.A + (int64_t)k0 * M : p.A + (int64_t)m0 * K + k0;
+        const uint16_t* bbase = TB ? p.B + (int64_t)n0 * K + k0 : p.B + (int64_t)k0 * N;
+        return {make_rsrc(abase, (uint64_t)arem), make_rsrc(bbase, (uint64_t)brem)};
     };
     // Load number i (A loads first, then B loads) of step kt into stage S.
     // (The descriptor is copied into a local first: handing the builtin a
@@ -204,14 +248,17 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         if (i < T::A_LOADS_W) {
             const __amdgpu_buffer_rsrc_t ra = r.a;
             uint32_t off = a_off[i];
-            if constexpr (!KALIGNED) off = (kt * T::BK + a_kc[i] * 8 < K) ? off : kOOB;
+            // a k-contiguous tile masks the K tail per lane
+            if constexpr (!KALIGNED && !TA) off = (kt * T::BK + a_kc[i] * 8 < K) ? off : kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (GR_LDS void*)(sa + (wave * T::A_LOADS_W + i) * 512), 16, (int)off, 0, 0, 0);
         } else {
             const __amdgpu_buffer_rsrc_t rb = r.b;
             const int j = i - T::A_LOADS_W;
+            uint32_t off = b_off[j];
+            if constexpr (!KALIGNED && TB) off = (kt * T::BK + b_kc[j] * 8 < K) ? off : kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (GR_LDS void*)(sb + (wave * T::B_LOADS_W + j) * 512), 16, (int)b_off[j], 0, 0, 0);
+                rb, (GR_LDS void*)(sb + (wave * T::B_LOADS_W + j) * 512), 16, (int)off, 0, 0, 0);
         }
     };
 
@@ -221,6 +268,17 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     uint32_t a_rd[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) a_rd[h] = ar * 64 + (((2 * h + lane / 32) ^ a_swz(lane % 32)) * 16);
+    // Transposed A (m-contiguous [32][BM]) block i: the 16-lane group g reads
+    // rows 8*(g/2) + 4*t + (lane%16)/4 and columns wm*TM + 32i + 16*(g%2) +
+    // 4*(lane%4) .. +3, so the lane receives column wm*TM + 32i + lane%32: the
+    // same rows of C as the k-contiguous read.
+    uint32_t at_rd[T::FM];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+        const int kr = 8 * ((lane / 16) / 2) + (lane % 16) / 4;
+        const int col = wm * T::TM + 32 * i + 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+        at_rd[i] = kr * (T::BM * 2) + (((col / 8) ^ at_swz<T::BM>(kr)) * 16) + 8 * ((col / 4) % 2);
+    }
     // B block j: the 16-lane group g reads rows 8*(g/2) + 4*t + (lane%16)/4
     // (t = 0, 1 for the two transposing reads) and columns
     //   wn*TN + 128*(j/4) + 16*(j%4) + 64*(g%2) + 4*(lane%4) .. +3,
@@ -235,6 +293,17 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         const int c = col / 8;
         b_rd[j] = kr * T::B_ROW_BYTES + ((c ^ b_swz(kr)) * 16) + 8 * ((col / 4) % 2);
     }
+    // Transposed B (k-contiguous [BN][32]) block j, half h: the lane reads
+    // row wn*TN + 128*(j/4) + 16*(j%4) + 64*(d/16) + d%16 (d = lane % 32) at
+    // chunk 2h + lane/32 -- the columns the transposing read gives the lane.
+    uint32_t bt_rd[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int d = lane % 32;
+        const int row = wn * T::TN + 16 * j + 64 * (d / 16) + d % 16;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) bt_rd[j][h] = row * 64 + (((2 * h + lane / 32) ^ a_swz(row)) * 16);
+    }
 
     // fragments of one 16-deep half-step
     struct Frag {
@@ -247,16 +316,20 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     auto read_slot = [&]<int S>(int half, int s, Frag& f) {
         const char* sa = reinterpret_cast<const char*>(stage_a.template operator()<S>());
         const char* sb = reinterpret_cast<const char*>(stage_b.template operator()<S>());
+        auto tr_read = [](const char* base, int row_bytes) -> f16x8 {
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GR_LDS i16x4*)(base));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GR_LDS i16x4*)(base + 4 * row_bytes));
+            return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
         if (s == 0 || s > T::FN) {
             const int i = (s == 0) ? 0 : s - T::FN;
-            f.a[i] = *reinterpret_cast<const f16x8*>(sa + a_rd[half] + i * 32 * 64);
+            if constexpr (!TA) f.a[i] = *reinterpret_cast<const f16x8*>(sa + a_rd[half] + i * 32 * 64);
+            else f.a[i] = tr_read(sa + at_rd[i] + half * 16 * (T::BM * 2), T::BM * 2);
         } else {
             const int j = s - 1;
-            const char* base = sb + b_rd[j % 4] + (j / 4) * 256 + half * 16 * T::B_ROW_BYTES;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GR_LDS i16x4*)(base));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GR_LDS i16x4*)(base + 4 * T::B_ROW_BYTES));
-            const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            f.b[j] = __builtin_bit_cast(f16x8, v);
+            if constexpr (!TB) f.b[j] = tr_read(sb + b_rd[j % 4] + (j / 4) * 256 + half * 16 * T::B_ROW_BYTES,
+                                                T::B_ROW_BYTES);
+            else f.b[j] = *reinterpret_cast<const f16x8*>(sb + bt_rd[j % 4][half] + (j / 4) * 128 * 64);
         }
     };
 

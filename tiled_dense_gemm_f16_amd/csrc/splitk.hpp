@@ -26,6 +26,10 @@
 //  * Rows of B past the wave's range, columns past N and rows of A past M
 //    read as zeros (buffer descriptors and out-of-range offsets); the K tail
 //    of A is masked per lane.
+//  * Transposed operands: B given as N x K is already k-contiguous, so each
+//    lane loads its eight columns' 8 k-values as eight 16-byte loads and
+//    skips the register transpose; A given as K x M is read one 2-byte
+//    element per k (A is the small operand here).
 //  * Reduction: the four waves add their fp32 tiles through LDS in a fixed
 //    order. With one workgroup along K the sum goes straight to the ReLU and
 //    the fp16 store. Otherwise each workgroup writes its fp32 partial tile,
@@ -38,7 +42,7 @@
 //
 // Requirements (checked on the host): N % 8 == 0, K % 8 == 0, 16-byte
 // aligned pointers, kc (the K range of a workgroup) a multiple of 4 * 32,
-// M * K * 2 and 8 * N * 2 below 2^31.
+// M * K * 2, 8 * N * 2 and 128 * K * 2 below 2^31.
 #pragma once
 
 #include "common.hpp"
@@ -59,7 +63,7 @@ struct Cfg {
     static_assert(BM % ROWS_PER_PASS == 0 || ROWS_PER_PASS % BM == 0, "combine rows");
 };
 
-template <class T>
+template <class T, bool TA = false, bool TB = false>
 __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
 {
     __shared__ __attribute__((aligned(16))) float red[T::NW][T::BM][T::RED_ROW];
@@ -82,16 +86,22 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
     const int g = lane / 16, i16 = lane % 16;
     // B: lane reads rows 8g + r (r = 0..7) of a step, columns ncol .. ncol+7
     const int ncol = n0 + 8 * i16;
+    // (B given as N x K: rows k .. k+7 of column ncol + r, relative to
+    // B + n0*K + k0)
     uint32_t boff[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) boff[r] = (ncol < N) ? (uint32_t)((8 * g + r) * N + ncol) * 2u : kOOB;
+    for (int r = 0; r < 8; ++r) {
+        if constexpr (!TB) boff[r] = (ncol < N) ? (uint32_t)((8 * g + r) * N + ncol) * 2u : kOOB;
+        else boff[r] = (ncol + r < N) ? (uint32_t)((8 * i16 + r) * K + 8 * g) * 2u : kOOB;
+    }
     // A: lane reads row m0 + mb*16 + i16, k-chunk 8g of a step
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, (uint64_t)M * K * 2);
     uint32_t arow[T::MB];
 #pragma unroll
     for (int mb = 0; mb < T::MB; ++mb) {
         const int m = m0 + mb * 16 + i16;
-        arow[mb] = (m < M) ? (uint32_t)m * (uint32_t)K * 2u : kOOB;
+        // A given as K x M: the element offset of column m (k added per step)
+        arow[mb] = (m < M) ? (TA ? (uint32_t)m * 2u : (uint32_t)m * (uint32_t)K * 2u) : kOOB;
     }
 
     u32x4 bst[T::D][8];
@@ -101,15 +111,38 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
     auto issue = [&](int d, int s) {
         const int k0 = kbeg + s * T::BK;
         const int64_t rows = (int64_t)kend - k0;
-        const int64_t brem = (rows > 0 ? rows : 0) * N * 2;
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)min(k0, K) * N, (uint64_t)brem);
+        if constexpr (!TB) {
+            const int64_t brem = (rows > 0 ? rows : 0) * N * 2;
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)min(k0, K) * N, (uint64_t)brem);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) bst[d][r] = load16(rb, boff[r]);
+            for (int r = 0; r < 8; ++r) bst[d][r] = load16(rb, boff[r]);
+        } else {
+            // columns of this tile, k from k0: a row's 16 bytes lie past the
+            // range's end only when the whole step does (kend - k0 is a
+            // multiple of 8), so a step past the end loads zeros
+            const int kk = min(k0, K);
+            const int64_t brem = rows > 0 ? ((int64_t)(N - n0) * K - kk) * 2 : 0;
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)n0 * K + kk, (uint64_t)brem);
+            const bool live = 8 * g < rows;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) bst[d][r] = load16(rb, live ? boff[r] : kOOB);
+        }
         const int ka = k0 + 8 * g;
 #pragma unroll
         for (int mb = 0; mb < T::MB; ++mb) {
-            const uint32_t off = (ka < kend && arow[mb] != kOOB) ? arow[mb] + (uint32_t)ka * 2u : kOOB;
-            ast[d][mb] = load16(ra, off);
+            if constexpr (!TA) {
+                const uint32_t off = (ka < kend && arow[mb] != kOOB) ? arow[mb] + (uint32_t)ka * 2u : kOOB;
+                ast[d][mb] = load16(ra, off);
+            } else {
+                uint16_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const bool ok = ka + e < kend && arow[mb] != kOOB;
+                    h[e] = ok ? p.A[(int64_t)(ka + e) * M + (arow[mb] >> 1)] : (uint16_t)0;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ast[d][mb][j] = (uint32_t)h[2 * j] | ((uint32_t)h[2 * j + 1] << 16);
+            }
         }
     };
 
@@ -121,7 +154,11 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
 
     auto compute = [&](int d) {
         u32x4 cols[8];
-        transpose8x8(bst[d], cols);
+        if constexpr (!TB) transpose8x8(bst[d], cols);
+        else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cols[e] = bst[d][e];
+        }
 #pragma unroll
         for (int mb = 0; mb < T::MB; ++mb) {
             const f16x8 a = __builtin_bit_cast(f16x8, ast[d][mb]);

@@ -7,7 +7,9 @@
 //  * A is stored k-contiguous ([BM][BK]); B arrives n-contiguous and is
 //    transposed in registers (8x8 blocks of halves) so it is also stored
 //    k-contiguous ([BN][BK]); both use an XOR swizzle of the 16-byte chunk
-//    index, so fragment reads hit distinct LDS banks;
+//    index, so fragment reads hit distinct LDS banks. Transposed operands
+//    (A given as K x M, B as N x K) swap which of the two load paths each
+//    operand takes; the LDS tiles and everything after them are the same;
 //  * two LDS stages plus the register prefetch form a three-deep pipeline;
 //  * tile products run on v_mfma_f32_16x16x32_f16 with the B fragment as the
 //    first operand, so the result block is C^T and each lane holds four
@@ -15,6 +17,8 @@
 // With VEC = false every global access is an element-wise, bounds-checked
 // load or store: any K, N and pointer alignment.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -34,10 +38,6 @@ struct Tile {
     static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;  // per-wave sub-tile
     static constexpr int FM = TM / 16, FN = TN / 16;              // 16x16 MFMA blocks
     static constexpr int KC = BK / 8;                             // 16-byte chunks per row
-    static constexpr int A_CHUNKS = BM * KC;                      // per stage
-    static constexpr int B_UNITS = KC * (BN / 8);                 // 8x8 blocks per stage
-    static constexpr int A_PER_T = (A_CHUNKS + NT - 1) / NT;
-    static constexpr int B_PER_T = (B_UNITS + NT - 1) / NT;
     static constexpr int STAGE_HALVES = (BM + BN) * BK;
     static constexpr int LDS_BYTES = 2 * STAGE_HALVES * 2;
     static constexpr int MIN_WAVES = MIN_WAVES_;
@@ -49,113 +49,167 @@ struct Tile {
     static_assert(BM % WAVES_M == 0 && BN % WAVES_N == 0, "waves must divide the tile");
 };
 
-// Registers holding one k-step of the block's operands on their way to LDS.
-template <class T>
-struct Staging {
-    u32x4 a[T::A_PER_T];
-    u32x4 b[T::B_PER_T][8];
+// Registers holding one k-step of one operand on its way to LDS. An operand
+// stored k-contiguous (A as given, or B given as N x K) arrives as 16-byte
+// chunks of 8 consecutive k; one stored mn-contiguous (B as given, or A given
+// as K x M) arrives as 8 x 8 blocks (8 k-rows of 8 columns), transposed in
+// registers before the LDS write. Either way the LDS tile is [ROWS][BK].
+template <class T, int ROWS>
+struct KChunks {
+    static constexpr int COUNT = ROWS * T::KC;
+    static constexpr int PER_T = (COUNT + T::NT - 1) / T::NT;
+    u32x4 v[PER_T];
 };
 
-template <class T, bool VEC>
-__device__ __forceinline__ void load_tile(const Args& p, int m0, int n0, int k0, Staging<T>& st)
+template <class T, int ROWS>
+struct MNUnits {
+    static constexpr int COUNT = T::KC * (ROWS / 8);
+    static constexpr int PER_T = (COUNT + T::NT - 1) / T::NT;
+    u32x4 v[PER_T][8];
+};
+
+template <class T, bool TA, bool TB>
+struct Staging {
+    std::conditional_t<TA, MNUnits<T, T::BM>, KChunks<T, T::BM>> a;
+    std::conditional_t<TB, KChunks<T, T::BN>, MNUnits<T, T::BN>> b;
+};
+
+// Rows [row0, row0 + ROWS) and k-columns [k0, k0 + BK) of a k-contiguous
+// operand X[rows_total][K]. Chunk c of the tile is row c / KC, k-chunk c % KC.
+template <class T, int ROWS, bool VEC>
+__device__ __forceinline__ void load_k(const uint16_t* X, int rows_total, int row0, int k0, int K,
+                                       KChunks<T, ROWS>& st)
 {
+    using S = KChunks<T, ROWS>;
     const int t = threadIdx.x;
-    const int K = p.K, N = p.N, M = p.M;
     if constexpr (VEC) {
-        // A: BM rows x KC chunks, block base at row m0, column k0
-        // (a step past the end of K gets an empty descriptor: zeros)
-        const int64_t arem = ((int64_t)(M - m0) * K - k0) * 2;
-        const uint16_t* abase = p.A + (int64_t)m0 * K + (k0 < K ? k0 : K);
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, (uint64_t)(k0 < K && arem > 0 ? arem : 0));
+        // a step past the end of K gets an empty descriptor: zeros
+        const int64_t rem = ((int64_t)(rows_total - row0) * K - k0) * 2;
+        const uint16_t* base = X + (int64_t)row0 * K + (k0 < K ? k0 : K);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (uint64_t)(k0 < K && rem > 0 ? rem : 0));
         const bool ktail = (k0 + T::BK > K);
 #pragma unroll
-        for (int i = 0; i < T::A_PER_T; ++i) {
+        for (int i = 0; i < S::PER_T; ++i) {
             const int c = t + i * T::NT;
             const int row = c / T::KC, kc = c % T::KC;
-            bool ok = (c < T::A_CHUNKS) && (m0 + row < M);
+            bool ok = (c < S::COUNT) && (row0 + row < rows_total);
             if (ktail) ok = ok && (k0 + kc * 8 < K);
-            const uint32_t off = ok ? (uint32_t)(row * K + kc * 8) * 2u : kOOB;
-            st.a[i] = load16(ra, off);
-        }
-        // B: BK rows x BN columns as 8x8 units; unit u -> k-block u % KC,
-        // n-block u / KC (8 consecutive lanes cover one n-block's 8 k-blocks,
-        // so the transposed LDS writes below hit 8 different chunks)
-        const int64_t brem = ((int64_t)K - k0) * N * 2;
-        const uint16_t* bbase = p.B + (int64_t)(k0 < K ? k0 : K) * N;
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bbase, (uint64_t)(brem > 0 ? brem : 0));
-#pragma unroll
-        for (int i = 0; i < T::B_PER_T; ++i) {
-            const int u = t + i * T::NT;
-            const int kb = u % T::KC, nb = u / T::KC;
-            const bool uok = (u < T::B_UNITS) && (n0 + nb * 8 < N);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int kr = kb * 8 + r;
-                const bool ok = uok && (!ktail || k0 + kr < K);
-                const uint32_t off = ok ? (uint32_t)(kr * N + n0 + nb * 8) * 2u : kOOB;
-                st.b[i][r] = load16(rb, off);
-            }
+            st.v[i] = load16(r, ok ? (uint32_t)(row * K + kc * 8) * 2u : kOOB);
         }
     } else {
         // element-wise loads with full bounds checks (any K, N, alignment)
 #pragma unroll
-        for (int i = 0; i < T::A_PER_T; ++i) {
+        for (int i = 0; i < S::PER_T; ++i) {
             const int c = t + i * T::NT;
             const int row = c / T::KC, kc = c % T::KC;
             uint16_t h[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int gm = m0 + row, gk = k0 + kc * 8 + e;
-                h[e] = (c < T::A_CHUNKS && gm < M && gk < K) ? p.A[(int64_t)gm * K + gk] : (uint16_t)0;
+                const int gr = row0 + row, gk = k0 + kc * 8 + e;
+                h[e] = (c < S::COUNT && gr < rows_total && gk < K) ? X[(int64_t)gr * K + gk] : (uint16_t)0;
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) st.a[i][j] = (uint32_t)h[2 * j] | ((uint32_t)h[2 * j + 1] << 16);
+            for (int j = 0; j < 4; ++j) st.v[i][j] = (uint32_t)h[2 * j] | ((uint32_t)h[2 * j + 1] << 16);
         }
+    }
+}
+
+// k-rows [k0, k0 + BK) and columns [row0, row0 + ROWS) of an mn-contiguous
+// operand X[K][ld]. Unit u is k-block u % KC, column block u / KC (8
+// consecutive threads cover one column block's k-blocks, so the transposed
+// LDS writes hit 8 different chunks).
+template <class T, int ROWS, bool VEC>
+__device__ __forceinline__ void load_mn(const uint16_t* X, int ld, int row0, int k0, int K, MNUnits<T, ROWS>& st)
+{
+    using S = MNUnits<T, ROWS>;
+    const int t = threadIdx.x;
+    const bool ktail = (k0 + T::BK > K);
+    if constexpr (VEC) {
+        const int64_t rem = ((int64_t)K - k0) * ld * 2;
+        const uint16_t* base = X + (int64_t)(k0 < K ? k0 : K) * ld;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (uint64_t)(rem > 0 ? rem : 0));
 #pragma unroll
-        for (int i = 0; i < T::B_PER_T; ++i) {
+        for (int i = 0; i < S::PER_T; ++i) {
+            const int u = t + i * T::NT;
+            const int kb = u % T::KC, nb = u / T::KC;
+            const bool uok = (u < S::COUNT) && (row0 + nb * 8 < ld);
+#pragma unroll
+            for (int r8 = 0; r8 < 8; ++r8) {
+                const int kr = kb * 8 + r8;
+                const bool ok = uok && (!ktail || k0 + kr < K);
+                st.v[i][r8] = load16(r, ok ? (uint32_t)(kr * ld + row0 + nb * 8) * 2u : kOOB);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < S::PER_T; ++i) {
             const int u = t + i * T::NT;
             const int kb = u % T::KC, nb = u / T::KC;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
+            for (int r8 = 0; r8 < 8; ++r8) {
                 uint16_t h[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int gk = k0 + kb * 8 + r, gn = n0 + nb * 8 + e;
-                    h[e] = (u < T::B_UNITS && gk < K && gn < N) ? p.B[(int64_t)gk * N + gn] : (uint16_t)0;
+                    const int gk = k0 + kb * 8 + r8, gc = row0 + nb * 8 + e;
+                    h[e] = (u < S::COUNT && gk < K && gc < ld) ? X[(int64_t)gk * ld + gc] : (uint16_t)0;
                 }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) st.b[i][r][j] = (uint32_t)h[2 * j] | ((uint32_t)h[2 * j + 1] << 16);
+                for (int j = 0; j < 4; ++j) st.v[i][r8][j] = (uint32_t)h[2 * j] | ((uint32_t)h[2 * j + 1] << 16);
             }
         }
     }
 }
 
-template <class T>
-__device__ __forceinline__ void store_tile(uint16_t* As, uint16_t* Bs, const Staging<T>& st)
+template <class T, bool VEC, bool TA, bool TB>
+__device__ __forceinline__ void load_tile(const Args& p, int m0, int n0, int k0, Staging<T, TA, TB>& st)
 {
+    if constexpr (TA) load_mn<T, T::BM, VEC>(p.A, p.M, m0, k0, p.K, st.a);
+    else load_k<T, T::BM, VEC>(p.A, p.M, m0, k0, p.K, st.a);
+    if constexpr (TB) load_k<T, T::BN, VEC>(p.B, p.N, n0, k0, p.K, st.b);
+    else load_mn<T, T::BN, VEC>(p.B, p.N, n0, k0, p.K, st.b);
+}
+
+template <class T, int ROWS>
+__device__ __forceinline__ void store_op(uint16_t* Xs, const KChunks<T, ROWS>& st)
+{
+    using S = KChunks<T, ROWS>;
     const int t = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < T::A_PER_T; ++i) {
+    for (int i = 0; i < S::PER_T; ++i) {
         const int c = t + i * T::NT;
-        if (c < T::A_CHUNKS) {
+        if (c < S::COUNT) {
             const int row = c / T::KC, kc = c % T::KC;
-            *reinterpret_cast<u32x4*>(As + row * T::BK + ((kc ^ swz(row)) * 8)) = st.a[i];
+            *reinterpret_cast<u32x4*>(Xs + row * T::BK + ((kc ^ swz(row)) * 8)) = st.v[i];
         }
     }
+}
+
+template <class T, int ROWS>
+__device__ __forceinline__ void store_op(uint16_t* Xs, const MNUnits<T, ROWS>& st)
+{
+    using S = MNUnits<T, ROWS>;
+    const int t = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < T::B_PER_T; ++i) {
+    for (int i = 0; i < S::PER_T; ++i) {
         const int u = t + i * T::NT;
-        if (u < T::B_UNITS) {
+        if (u < S::COUNT) {
             const int kb = u % T::KC, nb = u / T::KC;
             u32x4 cols[8];
-            transpose8x8(st.b[i], cols);
+            transpose8x8(st.v[i], cols);
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const int n = nb * 8 + c;
-                *reinterpret_cast<u32x4*>(Bs + n * T::BK + ((kb ^ swz(n)) * 8)) = cols[c];
+                *reinterpret_cast<u32x4*>(Xs + n * T::BK + ((kb ^ swz(n)) * 8)) = cols[c];
             }
         }
     }
+}
+
+template <class T, bool TA, bool TB>
+__device__ __forceinline__ void store_tile(uint16_t* As, uint16_t* Bs, const Staging<T, TA, TB>& st)
+{
+    store_op<T, T::BM>(As, st.a);
+    store_op<T, T::BN>(Bs, st.b);
 }
 
 template <class T>
@@ -188,7 +242,7 @@ __device__ __forceinline__ void compute_tile(const uint16_t* As, const uint16_t*
     }
 }
 
-template <class T, bool VEC>
+template <class T, bool VEC, bool TA = false, bool TB = false>
 __global__ void __launch_bounds__(T::NT, T::MIN_WAVES) staged_kernel(Args p)
 {
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE_HALVES];
@@ -208,19 +262,19 @@ __global__ void __launch_bounds__(T::NT, T::MIN_WAVES) staged_kernel(Args p)
 
     const int nk = (p.K + T::BK - 1) / T::BK;
     if constexpr (!VEC || T::PREFETCH == 1) {
-        Staging<T> st;
+        Staging<T, TA, TB> st;
         if (nk > 0) {
-            load_tile<T, VEC>(p, m0, n0, 0, st);
-            store_tile<T>(smem, smem + T::BM * T::BK, st);
+            load_tile<T, VEC, TA, TB>(p, m0, n0, 0, st);
+            store_tile<T, TA, TB>(smem, smem + T::BM * T::BK, st);
             __syncthreads();
         }
         for (int kt = 0; kt < nk; ++kt) {
             uint16_t* cur = smem + (kt & 1) * T::STAGE_HALVES;
             uint16_t* nxt = smem + ((kt + 1) & 1) * T::STAGE_HALVES;
             const bool more = kt + 1 < nk;
-            if (more) load_tile<T, VEC>(p, m0, n0, (kt + 1) * T::BK, st);
+            if (more) load_tile<T, VEC, TA, TB>(p, m0, n0, (kt + 1) * T::BK, st);
             compute_tile<T>(cur, cur + T::BM * T::BK, acc, wm, wn, lane);
-            if (more) store_tile<T>(nxt, nxt + T::BM * T::BK, st);
+            if (more) store_tile<T, TA, TB>(nxt, nxt + T::BM * T::BK, st);
             __syncthreads();
         }
     } else {
@@ -234,8 +288,8 @@ __global__ void __launch_bounds__(T::NT, T::MIN_WAVES) staged_kernel(Args p)
         // to a multiple of D, and steps past the end of K load and multiply
         // zeros.
         constexpr int D = T::PREFETCH;
-        Staging<T> st[D];
-        auto issue = [&](int slot, int s) { load_tile<T, true>(p, m0, n0, s * T::BK, st[slot]); };
+        Staging<T, TA, TB> st[D];
+        auto issue = [&](int slot, int s) { load_tile<T, true, TA, TB>(p, m0, n0, s * T::BK, st[slot]); };
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             issue(d, d);
@@ -243,7 +297,7 @@ __global__ void __launch_bounds__(T::NT, T::MIN_WAVES) staged_kernel(Args p)
         }
         const int nkd = (nk + D - 1) / D * D;
         if (nk > 0) {
-            store_tile<T>(smem, smem + T::BM * T::BK, st[0]);
+            store_tile<T, TA, TB>(smem, smem + T::BM * T::BK, st[0]);
             __syncthreads();
             issue(0, D);
             __builtin_amdgcn_sched_barrier(0);
@@ -256,7 +310,7 @@ __global__ void __launch_bounds__(T::NT, T::MIN_WAVES) staged_kernel(Args p)
                 uint16_t* nxt = smem + ((kt + 1) & 1) * T::STAGE_HALVES;
                 compute_tile<T>(cur, cur + T::BM * T::BK, acc, wm, wn, lane);
                 __builtin_amdgcn_sched_barrier(0);
-                store_tile<T>(nxt, nxt + T::BM * T::BK, st[(d + 1) % D]);
+                store_tile<T, TA, TB>(nxt, nxt + T::BM * T::BK, st[(d + 1) % D]);
                 __syncthreads();
                 issue((d + 1) % D, kt + 1 + D);
                 __builtin_amdgcn_sched_barrier(0);
