@@ -1,12 +1,14 @@
 """CPU oracle for C = ReLU(A @ B) and C = GELU(A @ B + bias) (fp16 in, fp16
-out) -- TEST INFRASTRUCTURE.
+out), and for row softmax and the attention forward pass -- TEST
+INFRASTRUCTURE.
 
 Only ``tests/``, the package smoke check in ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package. The product path
 (the HIP library and its Python binding) never imports it and shares no code
 with it.
 
-The arithmetic lives in ``gemm_relu_oracle.c`` (plain C, built with gcc); this
+The arithmetic lives in ``gemm_relu_oracle.c`` and ``attention_oracle.c``
+(plain C, built with gcc); this
 module builds it on demand and marshals numpy arrays of fp16 bit patterns
 (``uint16``) through ctypes. What each function computes, and the passage of
 the TileLang pages it follows, is stated in the C source.
@@ -26,6 +28,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gemm_relu_oracle.c")
+_SRCS = [_SRC, os.path.join(_HERE, "attention_oracle.c")]
 _LIB = os.path.join(_HERE, "liboracle_gemm_relu.so")
 _lock = threading.Lock()
 _lib = None
@@ -33,11 +36,11 @@ _lib = None
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (-O2, OpenMP, no fast-math). Returns the .so path."""
-    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+    if not force and os.path.exists(_LIB) and all(os.path.getmtime(_LIB) >= os.path.getmtime(f) for f in _SRCS):
         return _LIB
     tmp = _LIB + f".tmp{os.getpid()}"
     cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+           "-fno-fast-math", "-ffp-contract=off", *_SRCS, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB
@@ -78,6 +81,11 @@ def _load():
         lib.oracle_gemm_f16_rows_t.restype = ctypes.c_int
         lib.oracle_gemm_f16_points_t.argtypes = [i64, i64, i64, p, i32, p, i32, p, i64, p, p, p, p, p]
         lib.oracle_gemm_f16_points_t.restype = ctypes.c_int
+        lib.oracle_softmax_rows_f16.argtypes = [i64, i64, p, p, p]
+        lib.oracle_softmax_rows_f16.restype = ctypes.c_int
+        lib.oracle_attention_rows_f16.argtypes = [i64, i64, i64, i64, p, p, p, ctypes.c_double, i32, i64, p, p,
+                                                  p, p, p, p]
+        lib.oracle_attention_rows_f16.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -237,3 +245,76 @@ def gemm_bias_gelu_f16_points(A: np.ndarray, B: np.ndarray, bias: np.ndarray, ii
                               trans_a: bool = False, trans_b: bool = False):
     """Elements C[ii[t], jj[t]] of GELU(op(A) @ op(B) + bias) as fp16 bit patterns."""
     return _points(A, B, bias, ii, jj, want_pre, want_absdot, trans_a, trans_b)
+
+
+def softmax_rows_f16(X: np.ndarray, *, want_double: bool = False):
+    """Row softmax of fp16 bit patterns X [rows, cols]: fp16 bit patterns, and
+    optionally the float64 values before the rounding."""
+    X = np.ascontiguousarray(X)
+    if X.dtype != np.uint16 or X.ndim != 2:
+        raise ValueError("X must be a 2-D uint16 array of fp16 bit patterns")
+    rows, cols = X.shape
+    Y = np.zeros((rows, cols), dtype=np.uint16)
+    yd = np.zeros((rows, cols), dtype=np.float64) if want_double else None
+    if _load().oracle_softmax_rows_f16(rows, cols, _ptr(X), _ptr(Y), _ptr(yd)) != 0:
+        raise RuntimeError("oracle softmax failed")
+    return (Y, yd) if want_double else Y
+
+
+def _bhsd(x, name):
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint16 or x.ndim != 4:
+        raise ValueError(f"{name} must be a [B, H, S, D] uint16 array of fp16 bit patterns")
+    return x
+
+
+def attention_rows_f16(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, causal: bool, bh, qi, *,
+                       want_double: bool = False, want_lse: bool = False, want_pv: bool = False):
+    """Selected query rows of the attention forward pass.
+
+    Q: [B, H, Sq, D], K and V: [B, H, Skv, D] (fp16 bit patterns). Row t is
+    query qi[t] of batch-head bh[t] = b * H + h. Returns O rows [n, D] (fp16
+    bit patterns) and, as asked for, their float64 values, the log-sum-exp per
+    row and sum_j p_j |V[j][d]| per element.
+    """
+    Q, K, V = _bhsd(Q, "Q"), _bhsd(K, "K"), _bhsd(V, "V")
+    B, H, Sq, D = Q.shape
+    if K.shape[:2] != (B, H) or K.shape[3] != D or V.shape != K.shape:
+        raise ValueError(f"shapes {Q.shape}, {K.shape}, {V.shape} do not match")
+    Skv = K.shape[2]
+    bh = np.ascontiguousarray(bh, dtype=np.int64)
+    qi = np.ascontiguousarray(qi, dtype=np.int64)
+    if bh.shape != qi.shape or bh.ndim != 1:
+        raise ValueError("bh and qi must be 1-D of equal length")
+    n = bh.size
+    out = np.zeros((n, D), dtype=np.uint16)
+    od = np.zeros((n, D), dtype=np.float64) if want_double else None
+    lse = np.zeros(n, dtype=np.float64) if want_lse else None
+    pv = np.zeros((n, D), dtype=np.float64) if want_pv else None
+    rc = _load().oracle_attention_rows_f16(B * H, Sq, Skv, D, _ptr(Q), _ptr(K), _ptr(V), float(scale), int(causal), n,
+                                           _ptr(bh), _ptr(qi), _ptr(out), _ptr(od), _ptr(lse), _ptr(pv))
+    if rc != 0:
+        raise RuntimeError("oracle attention failed")
+    res = [out]
+    if want_double:
+        res.append(od)
+    if want_lse:
+        res.append(lse)
+    if want_pv:
+        res.append(pv)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def attention_f16(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, causal: bool, **kw):
+    """Every query row of the attention forward pass: O [B, H, Sq, D] (and the
+    extras of attention_rows_f16, reshaped likewise)."""
+    B, H, Sq, D = np.shape(Q)
+    bh, qi = np.divmod(np.arange(B * H * Sq, dtype=np.int64), Sq)
+    res = attention_rows_f16(Q, K, V, scale, causal, bh, qi, **kw)
+    if not isinstance(res, tuple):
+        return res.reshape(B, H, Sq, D)
+    out = []
+    for r in res:
+        out.append(r.reshape(B, H, Sq) if r.ndim == 1 else r.reshape(B, H, Sq, D))
+    return tuple(out)
+

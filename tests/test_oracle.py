@@ -466,6 +466,7 @@ def test_planted_mistake_is_caught(mutant, tmp_path):
     dst.mkdir()
     (dst / "gemm_relu_oracle.c").write_text(text.replace(old, new, 1))
     shutil.copy(os.path.join(src_dir, "__init__.py"), dst / "__init__.py")
+    shutil.copy(os.path.join(src_dir, "attention_oracle.c"), dst / "attention_oracle.c")
     spec = importlib.util.spec_from_file_location(f"oracle_mut_{mutant}", dst / "__init__.py")
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
@@ -644,6 +645,7 @@ def test_planted_bias_gelu_mistake_is_caught(mutant, tmp_path):
     dst.mkdir()
     (dst / "gemm_relu_oracle.c").write_text(text.replace(old, new, 1))
     shutil.copy(os.path.join(src_dir, "__init__.py"), dst / "__init__.py")
+    shutil.copy(os.path.join(src_dir, "attention_oracle.c"), dst / "attention_oracle.c")
     spec = importlib.util.spec_from_file_location(f"oracle_bmut_{mutant}", dst / "__init__.py")
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
@@ -760,6 +762,7 @@ def test_planted_transpose_mistake_is_caught(mutant, tmp_path):
     dst.mkdir()
     (dst / "gemm_relu_oracle.c").write_text(text.replace(old, new, 1))
     shutil.copy(os.path.join(src_dir, "__init__.py"), dst / "__init__.py")
+    shutil.copy(os.path.join(src_dir, "attention_oracle.c"), dst / "attention_oracle.c")
     spec = importlib.util.spec_from_file_location(f"oracle_tmut_{mutant}", dst / "__init__.py")
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
