@@ -15,19 +15,22 @@ import pytest
 import tiled_dense_gemm_f16_amd as gr
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gemm_relu.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gemm_relu.h", "attention.h")]
 
 
 def declared_functions() -> list[str]:
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gemm_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert "gemm_relu_f16" in names and "gemm_relu_f16_ex" in names
     assert "gemm_bias_gelu_f16" in names and "gemm_bias_gelu_f16_ex" in names
+    assert "softmax_rows_f16" in names and "flash_attn_fwd_f16" in names
     assert set(names) == set(gr.EXPORTED)
 
 
@@ -229,6 +232,29 @@ def test_python_wrapper_shapes_with_transposes():
         gr.gemm_relu(a, b, trans_a=True)
     with pytest.raises(ValueError, match="same GPU"):  # shapes chain; CPU tensors are not device memory
         gr.gemm_relu(a, b, trans_a=True, trans_b=True)
+
+
+def test_softmax_arguments_rejected():
+    assert gr.softmax_rows_f16(-1, 4, FAKE, FAKE * 2) == gr.EINVAL
+    assert gr.softmax_rows_f16(4, 4, 0, FAKE * 2) == gr.EINVAL
+    assert gr.softmax_rows_f16(4, 4, FAKE + 1, FAKE * 2) == gr.EUNSUPPORTED
+    assert gr.softmax_rows_f16(4, 4, FAKE, FAKE + 8) == gr.EINVAL  # partial overlap
+    assert gr.softmax_rows_f16(2 ** 31, 4, FAKE, FAKE * 2) == gr.EUNSUPPORTED
+    assert gr.softmax_rows_f16(0, 4, 0, 0) == gr.OK
+
+
+def test_attention_arguments_rejected():
+    f = gr.flash_attn_fwd_f16
+    Q, K, V, O = FAKE, FAKE * 4, FAKE * 8, FAKE * 12
+    assert f(-1, 1, 4, 4, 64, Q, K, V, O, 0, 0.1, 0) == gr.EINVAL
+    assert f(1, 1, 4, 4, 64, Q, K, V, O, 0, 0.1, 2) == gr.EINVAL      # causal must be 0 or 1
+    assert f(1, 1, 4, 4, 96, Q, K, V, O, 0, 0.1, 0) == gr.EUNSUPPORTED  # head dimension
+    assert f(1, 1, 4, 4, 64, 0, K, V, O, 0, 0.1, 0) == gr.EINVAL
+    assert f(1, 1, 4, 4, 64, Q + 8, K, V, O, 0, 0.1, 0) == gr.EUNSUPPORTED  # 16-byte alignment
+    assert f(1, 1, 4, 4, 64, Q, K, V, O, FAKE * 16 + 2, 0.1, 0) == gr.EUNSUPPORTED  # lse alignment
+    assert f(1, 1, 4, 4, 64, Q, K, V, Q, 0, 0.1, 0) == gr.EINVAL       # O overlaps Q
+    assert f(1, 1, 2 ** 24, 4, 64, Q, K, V, O, 0, 0.1, 0) == gr.EUNSUPPORTED  # in-head offsets
+    assert f(1, 1, 0, 4, 64, 0, K, V, 0, 0, 0.1, 0) == gr.OK            # nothing to write
 
 
 def test_empty_output_is_a_no_op():

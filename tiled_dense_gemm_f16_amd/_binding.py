@@ -49,7 +49,8 @@ _lib = None
 
 EXPORTED = ("gemm_relu_f16", "gemm_relu_f16_ex", "gemm_relu_f16_op", "gemm_bias_gelu_f16",
             "gemm_bias_gelu_f16_ex", "gemm_bias_gelu_f16_op", "gemm_relu_strerror", "gemm_relu_tile_count",
-            "gemm_relu_tile_name", "gemm_relu_tile_info", "gemm_relu_select_tile", "gemm_relu_select_tile_op")
+            "gemm_relu_tile_name", "gemm_relu_tile_info", "gemm_relu_select_tile", "gemm_relu_select_tile_op",
+            "softmax_rows_f16", "flash_attn_fwd_f16")
 
 
 def load():
@@ -77,6 +78,10 @@ def load():
         lib.gemm_bias_gelu_f16_op.restype = i32
         lib.gemm_relu_select_tile_op.argtypes = [i64, i64, i64, i32, i32, p, p, p]
         lib.gemm_relu_select_tile_op.restype = i32
+        lib.softmax_rows_f16.argtypes = [i64, i64, p, p, p]
+        lib.softmax_rows_f16.restype = i32
+        lib.flash_attn_fwd_f16.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, ctypes.c_float, i32, p]
+        lib.flash_attn_fwd_f16.restype = i32
         lib.gemm_relu_strerror.argtypes = [i32]
         lib.gemm_relu_strerror.restype = ctypes.c_char_p
         lib.gemm_relu_tile_count.argtypes = []
@@ -233,3 +238,59 @@ def gemm_bias_gelu(a, b, bias, out=None, *, trans_a: bool = False, trans_b: bool
         _check(gemm_bias_gelu_f16_op(M, N, K, a.data_ptr(), int(trans_a), b.data_ptr(), int(trans_b),
                                      bias.data_ptr(), out.data_ptr(), s.cuda_stream, opts))
     return out
+
+
+def softmax_rows_f16(rows: int, cols: int, X: int, Y: int, stream: int = 0) -> int:
+    """Raw C-ABI call of the row softmax; returns the status code."""
+    return load().softmax_rows_f16(rows, cols, X or None, Y or None, stream or None)
+
+
+def flash_attn_fwd_f16(B: int, H: int, Sq: int, Skv: int, D: int, Q: int, K: int, V: int, O: int, lse: int,
+                       scale: float, causal: int, stream: int = 0) -> int:
+    """Raw C-ABI call of the attention forward pass; returns the status code."""
+    return load().flash_attn_fwd_f16(B, H, Sq, Skv, D, Q or None, K or None, V or None, O or None, lse or None,
+                                     float(scale), int(causal), stream or None)
+
+
+def softmax_rows(x, out=None, *, stream=None):
+    """Row softmax of a 2-D fp16 CUDA(HIP) tensor; returns out (may be x itself)."""
+    import torch
+
+    if x.dtype != torch.float16 or x.dim() != 2 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D float16 GPU tensor")
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or out.device != x.device or not out.is_contiguous():
+        raise ValueError("out must match x")
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        _check(softmax_rows_f16(x.shape[0], x.shape[1], x.data_ptr(), out.data_ptr(), s.cuda_stream))
+    return out
+
+
+def flash_attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, return_lse: bool = False,
+                   stream=None):
+    """Attention forward for fp16 tensors q [B, H, Sq, D], k and v [B, H, Skv, D]
+    (contiguous, D = 64 or 128); scale defaults to 1/sqrt(D). Returns out
+    [B, H, Sq, D] (and the fp32 log-sum-exp [B, H, Sq] with return_lse)."""
+    import torch
+
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.float16 or t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D float16 GPU tensor")
+    B, H, Sq, D = q.shape
+    if k.shape[:2] != (B, H) or k.shape[3] != D or v.shape != k.shape or k.device != q.device or v.device != q.device:
+        raise ValueError(f"shapes {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)} do not match")
+    Skv = k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must match q")
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    sc = (1.0 / D ** 0.5) if scale is None else float(scale)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        _check(flash_attn_fwd_f16(B, H, Sq, Skv, D, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse.data_ptr() if lse is not None else 0, sc, int(causal), s.cuda_stream))
+    return (out, lse) if return_lse else out
+

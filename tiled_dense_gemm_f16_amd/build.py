@@ -1,4 +1,6 @@
-"""Builds libgemm_relu.so (gfx950 only) in-tree with hipcc.
+"""Builds libgemm_relu.so (gfx950 only) in-tree with hipcc: the GEMM
+(csrc/gemm_relu.hip) and the softmax / attention kernels (csrc/attention.hip)
+compiled in parallel and linked into one shared library.
 
 Usage: ``python -m tiled_dense_gemm_f16_amd.build`` or ``build()`` from Python.
 """
@@ -11,6 +13,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "gemm_relu.hip")
+SRCS = [SRC, os.path.join(PKG, "csrc", "attention.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgemm_relu.so")
 ARCH = "gfx950"
@@ -20,7 +23,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++20",
     "-fPIC",
-    "-shared",
     "-Wall",
     # no packed fp32 arithmetic in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -34,16 +36,36 @@ def hipcc() -> str:
 
 def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str | None = None) -> str:
     """Compile the HIP library. Always compiles (no staleness shortcut)."""
+    import concurrent.futures
+
     out = out or LIB
-    tmp = out + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", SRC, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed ({res.returncode}) building {out}")
-    os.replace(tmp, out)
+    tag = f".tmp{os.getpid()}"
+    objs = [out + f".{os.path.splitext(os.path.basename(src))[0]}{tag}.o" for src in SRCS]
+
+    def run(cmd):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        return subprocess.run(cmd, capture_output=True, text=True)
+
+    cmds = [[hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", "-c", src, "-o", obj]
+            for src, obj in zip(SRCS, objs)]
+    try:
+        with concurrent.futures.ThreadPoolExecutor(len(cmds)) as ex:
+            results = list(ex.map(run, cmds))
+        for res, src in zip(results, SRCS):
+            if res.returncode != 0:
+                sys.stderr.write(res.stdout + res.stderr)
+                raise RuntimeError(f"hipcc failed ({res.returncode}) compiling {src}")
+        tmp = out + tag
+        res = run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc failed ({res.returncode}) linking {out}")
+        os.replace(tmp, out)
+    finally:
+        for obj in objs:
+            if os.path.exists(obj):
+                os.remove(obj)
     return out
 
 
