@@ -12,6 +12,14 @@ stderr.
 
 The CPU baseline leg times the oracle (plain C, all host threads) on a bounded
 slice of the same workload -- leading rows of C -- and scales it to TFLOP/s.
+
+    python bench.py --op attention [--batch B --heads H --seq S --head-dim D --causal]
+    python bench.py --op softmax [--rows R --cols C]
+
+time the second workload the same way (graph replay, rotated inputs): the
+attention forward pass against the fp16 MFMA roofline, the row softmax
+against HBM bandwidth; each prints its own JSON line, with the oracle on
+sampled rows as its CPU baseline.
 """
 from __future__ import annotations
 
@@ -242,6 +250,165 @@ def result_line(w, r, steps, warmup, cpu=None):
     return line
 
 
+def time_calls(calls, steps: int, warmup: int, graph_batch: int, stream) -> dict:
+    """Warm-up, then `steps` launches replayed from HIP graphs of `graph_batch`
+    (cycling through `calls`, one per input copy) between two events on
+    `stream`; then 50 single launches between their own events."""
+    import torch
+
+    rot = len(calls)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            calls[i % rot]()
+        torch.cuda.synchronize()
+        steps = max(graph_batch, steps // graph_batch * graph_batch)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(graph_batch):
+                calls[i % rot]()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps // graph_batch):
+            graph.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        total_ms = t0.elapsed_time(t1)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+        for i, (e0, e1) in enumerate(evs):
+            e0.record(stream)
+            calls[i % rot]()
+            e1.record(stream)
+        torch.cuda.synchronize()
+    per = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    return {"ms_per_step": total_ms / steps, "steps": steps, "launch_ms_mean": float(per.mean()),
+            "launch_ms_min": float(per.min()), "rotation": rot, "graph_batch": graph_batch}
+
+
+def cpu_sample(fn, total_rows: int, target_s: float) -> tuple[int, float]:
+    """Times fn(n) (the oracle on n rows) on a growing n, then on about
+    target_s seconds' worth; returns (rows, seconds)."""
+    n = 8
+    while True:
+        t = time.perf_counter()
+        fn(n)
+        dt = time.perf_counter() - t
+        if dt >= 0.5 or n >= total_rows:
+            break
+        n = min(total_rows, n * 4)
+    rows = int(min(total_rows, max(1, round(n * target_s / max(dt, 1e-6)))))
+    t = time.perf_counter()
+    fn(rows)
+    return rows, time.perf_counter() - t
+
+
+def bench_attention(args) -> dict:
+    import torch
+    import tiled_dense_gemm_f16_amd as gr
+
+    B, H, S, D = args.batch, args.heads, args.seq, args.head_dim
+    Skv = args.seq_kv or S
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    mk = lambda s_: torch.randn((B, H, s_, D), generator=gen, device="cuda", dtype=torch.float32).half()  # noqa: E731
+    rot = 2
+    qs = [mk(S) for _ in range(rot)]
+    ks = [mk(Skv) for _ in range(rot)]
+    vs = [mk(Skv) for _ in range(rot)]
+    o = torch.empty_like(qs[0])
+    stream = torch.cuda.Stream()
+    scale = 1.0 / D ** 0.5
+    calls = [lambda i=i: gr.flash_attn_fwd_f16(B, H, S, Skv, D, qs[i].data_ptr(), ks[i].data_ptr(),
+                                               vs[i].data_ptr(), o.data_ptr(), 0, scale, int(args.causal),
+                                               stream.cuda_stream) for i in range(rot)]
+    st = calls[0]()
+    if st != gr.OK:
+        raise RuntimeError(gr.strerror(st))
+    r = time_calls(calls, args.steps, args.warmup, args.graph or 10, stream)
+    # multiply-adds of Q K^T and P V over the visible (query, key) pairs
+    pairs = sum(min(i + 1, Skv) for i in range(S)) if args.causal else S * Skv
+    flops = 4.0 * B * H * D * pairs
+    achieved = flops / (r["ms_per_step"] * 1e-3) / 1e12
+    name = f"attention_fwd_f16_b{B}_h{H}_s{S}" + (f"_skv{Skv}" if Skv != S else "") + f"_d{D}" + \
+        ("_causal" if args.causal else "")
+    line = {"metric": "TFLOP/s of the attention forward pass (fp16 in, fp32 accumulate, fp16 out)",
+            "value": round(achieved, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": r["steps"],
+            "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16", "accum_dtype": "f32", "data": "synthetic",
+            "config": {"workload": name, "batch": B, "heads": H, "seq_q": S, "seq_kv": Skv, "head_dim": D,
+                       "causal": bool(args.causal), "dist": "normal", "input_copies_rotated": rot,
+                       "parallelism": "single GPU"},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None},
+            "kernel_ms_timed_region_mean": round(r["ms_per_step"], 5), "graph_batch": r["graph_batch"],
+            "single_launch_event_ms": {"mean": round(r["launch_ms_mean"], 5), "min": round(r["launch_ms_min"], 5)},
+            "flops_per_launch": flops}
+    if not args.no_cpu_baseline:
+        import oracle
+        Q = workloads.as_u16(qs[0].cpu())
+        Kc = workloads.as_u16(ks[0].cpu())
+        Vc = workloads.as_u16(vs[0].cpu())
+        rng = np.random.default_rng(0)
+        total = B * H * S
+        bh_all = rng.integers(0, B * H, total)
+        qi_all = rng.integers(0, S, total)
+
+        def run(n):
+            oracle.attention_rows_f16(Q, Kc, Vc, scale, bool(args.causal), bh_all[:n], qi_all[:n])
+
+        rows, secs = cpu_sample(run, total, args.cpu_seconds)
+        qi = qi_all[:rows]
+        row_pairs = np.minimum(qi + 1, Skv).sum() if args.causal else rows * Skv
+        line["cpu_baseline"] = {"value": 4.0 * D * float(row_pairs) / secs / 1e12, "unit": "TFLOP/s",
+                                "cores": oracle.num_threads(), "kind": "oracle",
+                                "sample": f"{rows} random query rows of {name} ({secs:.1f} s)"}
+    return line
+
+
+def bench_softmax(args) -> dict:
+    import torch
+    import tiled_dense_gemm_f16_amd as gr
+
+    R, C = args.rows, args.cols
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    nbytes = 2 * R * C
+    rot = max(1, min(8, -(-ROTATE_BYTES // max(nbytes, 1))))
+    xs = [torch.randn((R, C), generator=gen, device="cuda", dtype=torch.float32).half() for _ in range(rot)]
+    y = torch.empty_like(xs[0])
+    stream = torch.cuda.Stream()
+    calls = [lambda i=i: gr.softmax_rows_f16(R, C, xs[i].data_ptr(), y.data_ptr(), stream.cuda_stream)
+             for i in range(rot)]
+    st = calls[0]()
+    if st != gr.OK:
+        raise RuntimeError(gr.strerror(st))
+    r = time_calls(calls, args.steps, args.warmup, args.graph or 10, stream)
+    moved = 2 * nbytes  # each element read once and written once
+    gbs = moved / (r["ms_per_step"] * 1e-3) / 1e9
+    name = f"softmax_rows_f16_{R}x{C}"
+    line = {"metric": "GB/s of the row softmax (fp16 in and out, fp32 arithmetic)", "value": round(gbs, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": r["steps"], "warmup": args.warmup,
+            "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f16", "accum_dtype": "f32", "data": "synthetic",
+            "config": {"workload": name, "rows": R, "cols": C, "dist": "normal", "input_copies_rotated": rot,
+                       "parallelism": "single GPU"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+            "kernel_ms_timed_region_mean": round(r["ms_per_step"], 5), "graph_batch": r["graph_batch"],
+            "single_launch_event_ms": {"mean": round(r["launch_ms_mean"], 5), "min": round(r["launch_ms_min"], 5)},
+            "bytes_per_launch": moved}
+    if not args.no_cpu_baseline:
+        import oracle
+        X = workloads.as_u16(xs[0].cpu())
+        rows, secs = cpu_sample(lambda n: oracle.softmax_rows_f16(X[:n]), R, args.cpu_seconds)
+        line["cpu_baseline"] = {"value": 4.0 * rows * C / secs / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+                                "kind": "oracle", "sample": f"rows 0..{rows - 1} of {name} ({secs:.1f} s)"}
+    return line
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,6 +425,16 @@ def main(argv=None) -> int:
                     help="operand layouts: A stored K x M (t first) and/or B stored N x K (t second)")
     ap.add_argument("--graph", type=int, default=50, metavar="G",
                     help="capture G launches per HIP graph and replay it (0: launch one by one from the host)")
+    ap.add_argument("--op", choices=("gemm", "attention", "softmax"), default="gemm",
+                    help="gemm (the headline), or the second workload: attention forward / row softmax")
+    ap.add_argument("--batch", type=int, default=4)
+    ap.add_argument("--heads", type=int, default=32)
+    ap.add_argument("--seq", type=int, default=4096)
+    ap.add_argument("--seq-kv", type=int, default=0, help="key/value length (default: --seq)")
+    ap.add_argument("--head-dim", type=int, default=128, choices=(64, 128))
+    ap.add_argument("--causal", action="store_true")
+    ap.add_argument("--rows", type=int, default=16384)
+    ap.add_argument("--cols", type=int, default=8192)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run an element-wise copy (negation) of MIB MiB, 20 times: a kernel of known "
                          "traffic, used to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -285,6 +462,16 @@ def main(argv=None) -> int:
         return 0
     import tiled_dense_gemm_f16_amd as gr
     gr.load()
+    if args.op != "gemm":
+        if args.graph == 50:
+            args.graph = 10
+        if args.steps == 2000 and args.warmup == 200:  # defaults sized for the GEMM
+            args.steps, args.warmup = (40, 5) if args.op == "attention" else (200, 20)
+        line = bench_attention(args) if args.op == "attention" else bench_softmax(args)
+        print(f"[bench] {line['config']['workload']}: {line['ms_per_step'] * 1e3:.2f} us/step, "
+              f"{line['value']} {line['unit']}", file=sys.stderr, flush=True)
+        print(json.dumps(line), flush=True)
+        return 0
 
     w = workloads.BY_NAME[args.workload]
     r = time_gpu(w, args.steps, args.warmup, args.tile, args.graph, args.epilogue, args.layout)
