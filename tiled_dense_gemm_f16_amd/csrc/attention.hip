@@ -50,10 +50,14 @@ void launch_softmax_vec(const SoftmaxArgs& a, hipStream_t s)
     hipLaunchKernelGGL((gemm_relu::attn::softmax_rows_vec<V>), dim3((a.rows + 3) / 4), dim3(256), 0, s, a);
 }
 
+#ifndef GR_ATTN_NW
+#define GR_ATTN_NW 4
+#endif
+
 template <int D>
 void launch_attn(const AttnArgs& a, hipStream_t s)
 {
-    using T = AttnCfg<D>;
+    using T = AttnCfg<D, GR_ATTN_NW>;
     hipLaunchKernelGGL((gemm_relu::attn::attn_fwd_kernel<T>), dim3(a.BH * a.nqb), dim3(T::NT), 0, s, a);
 }
 
@@ -107,7 +111,8 @@ int flash_attn_fwd_f16(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
         (lse && overlaps(O, 2 * nq, lse, 4 * BH * Sq)))
         return GEMM_RELU_EINVAL;
     if (BH == 0 || Sq == 0) return GEMM_RELU_OK;
-    const int64_t nqb = (Sq + 255) / 256;
+    constexpr int64_t kBM = AttnCfg<128, GR_ATTN_NW>::BM;  // query rows per workgroup
+    const int64_t nqb = (Sq + kBM - 1) / kBM;
     if (BH * nqb > INT32_MAX) return GEMM_RELU_EUNSUPPORTED;
     const int rc = check_device();
     if (rc != GEMM_RELU_OK) return rc;

@@ -148,9 +148,10 @@ __global__ void __launch_bounds__(256) softmax_rows_any(SoftmaxArgs a)
 // value tiles with a running maximum and sum, and the score matrix never goes
 // to memory).
 //
-//  * A workgroup owns BM = 256 query rows of one (batch, head): 8 waves, two
-//    per SIMD, 32 rows each, so one wave's softmax arithmetic overlaps the
-//    other's matrix ops.
+//  * A workgroup owns BM = 128 query rows of one (batch, head): 4 waves of 32
+//    rows. Two workgroups share a CU (two waves per SIMD) and run out of step
+//    with each other, so one's softmax arithmetic overlaps the other's
+//    matrix ops; the small workgroup also evens out causal work.
 //  * Key and value tiles of BN = 64 rows go global -> LDS with direct 1 KiB
 //    buffer loads into two LDS stages (one array per stage and operand), the
 //    next tile in flight while the current one is used; rows past the
@@ -159,9 +160,13 @@ __global__ void __launch_bounds__(256) softmax_rows_any(SoftmaxArgs a)
 //    ends up with one query row (lane % 32) and 16 of the tile's keys. Q's
 //    fragments stay in registers for the whole pass.
 //  * Online softmax per row in the log2 domain: t = s * scale * log2(e),
-//    m' = max(m, max t), p = 2^(t - m'), l' = l 2^(m - m') + sum p, O *= 2^(m - m').
-//    The row's two lanes (lane, lane ^ 32) meet with one swap for the maximum;
-//    the sums stay per lane until the end.
+//    p = 2^(t - m), l += sum p, O += P V, with the reference m of each row
+//    moved to the running maximum (and O, l rescaled by 2^(m - m')) only when
+//    a score exceeds it by more than 2^8 -- exact in real arithmetic, and it
+//    spares most tiles the rescaling. The row's two lanes (lane, lane ^ 32)
+//    meet with one swap for the maximum; the sums stay per lane until the
+//    end. Interior tiles fold the scaling into the exponent (one FMA per
+//    score); only tiles at the sequence end or the causal diagonal mask.
 //  * O += P V with P as the second operand straight from the S registers
 //    (converted to fp16): the lane already holds, for each 16-deep chunk of
 //    keys, the 8 values the operand wants -- in the key order {0-3, 8-11} or
@@ -188,10 +193,10 @@ struct AttnArgs {
     int nqb;  // query tiles per (batch, head)
 };
 
-template <int D_>
+template <int D_, int NW_ = 8>
 struct AttnCfg {
     static constexpr int D = D_;
-    static constexpr int BM = 256, BN = 64, NW = 8, NT = NW * kWave;
+    static constexpr int NW = NW_, BM = 32 * NW, BN = 64, NT = NW * kWave;
     static constexpr int KK = D / 16;             // 16-deep chunks of the QK^T reduction
     static constexpr int DB = D / 32;             // 32-wide blocks of O columns
     static constexpr int CPR = D / 8;             // 16-byte chunks per K / V row
@@ -226,7 +231,7 @@ __device__ __forceinline__ int v_swz(int r)
 }
 
 template <class T>
-__global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)
+__global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two waves per SIMD
 {
     __shared__ __attribute__((aligned(1024))) uint16_t ks0[T::TILE_HALVES];
     __shared__ __attribute__((aligned(1024))) uint16_t ks1[T::TILE_HALVES];
@@ -290,20 +295,31 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)
         koff[i] = (uint32_t)(r * D + 8 * (pc ^ k_swz<D>(r))) * 2u;
         voff[i] = (uint32_t)(r * D + 8 * (pc ^ v_swz<D>(r))) * 2u;
     }
-    auto issue = [&]<int S>(int j) {
+    // K tile j into K stage S, V tile j into V stage S
+    auto issue_k = [&]<int S>(int j) {
         const int kv0 = j * T::BN;
         const bool live = j < nkb;
         const uint64_t bytes = live ? (uint64_t)(Skv - kv0) * D * 2 : 0;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (int64_t)(live ? kv0 : 0) * D, bytes);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (int64_t)(live ? kv0 : 0) * D, bytes);
         uint16_t* kd = S == 0 ? ks0 : ks1;
-        uint16_t* vd = S == 0 ? vs0 : vs1;
 #pragma unroll
         for (int i = 0; i < T::LW; ++i) {
             const int gi = wave * T::LW + i;
             const bool in = kv0 + lrow[i] < Skv;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (GR_LDS void*)(kd + gi * 512), 16,
                                                      (int)(in ? koff[i] : kOOB), 0, 0, 0);
+        }
+    };
+    auto issue_v = [&]<int S>(int j) {
+        const int kv0 = j * T::BN;
+        const bool live = j < nkb;
+        const uint64_t bytes = live ? (uint64_t)(Skv - kv0) * D * 2 : 0;
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (int64_t)(live ? kv0 : 0) * D, bytes);
+        uint16_t* vd = S == 0 ? vs0 : vs1;
+#pragma unroll
+        for (int i = 0; i < T::LW; ++i) {
+            const int gi = wave * T::LW + i;
+            const bool in = kv0 + lrow[i] < Skv;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (GR_LDS void*)(vd + gi * 512), 16,
                                                      (int)(in ? voff[i] : kOOB), 0, 0, 0);
         }
@@ -342,12 +358,9 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)
     float m_run = -INFINITY;  // running maximum of this lane's row (log2 domain)
     float l_run = 0.f;        // running sum of this lane's share of the row
 
-    auto tile = [&]<int S>(int j) {
+    // S = Q K^T for the 64 keys of K stage S
+    auto qk = [&]<int S>(f32x16 (&sc)[2]) {
         const char* kb = reinterpret_cast<const char*>(S == 0 ? ks0 : ks1);
-        const char* vb = reinterpret_cast<const char*>(S == 0 ? vs0 : vs1);
-        const int kv0 = j * T::BN;
-        // S = Q K^T for the tile's 64 keys
-        f32x16 s[2];
         f16x8 kf[2][T::KK];
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
@@ -356,49 +369,89 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) s[jb][e] = 0.f;
+            for (int e = 0; e < 16; ++e) sc[jb][e] = 0.f;
 #pragma unroll
             for (int kk = 0; kk < T::KK; ++kk)
-                s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[jb][kk], qf[kk], s[jb], 0, 0, 0);
+                sc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[jb][kk], qf[kk], sc[jb], 0, 0, 0);
         }
-        // scale to the log2 domain; mask keys past the end or after the row
-        // (lane holds keys kv0 + 32 jb + 8 (e / 4) + 4 hi + e % 4)
-        // (the limit is Skv, or for a causal row min(Skv, qrow + 1); branch-free)
-        const int lim = p.causal ? min(Skv, qrow + 1) : Skv;
-        const int rel = lim - kv0 - 4 * hi;  // key offsets below rel are visible
+    };
+
+    // softmax of tile j's scores s, then O += P V with V stage S
+    auto softmax_pv = [&]<int S>(int j, f32x16 (&s)[2]) {
+        const char* vb = reinterpret_cast<const char*>(S == 0 ? vs0 : vs1);
+        const int kv0 = j * T::BN;
+        // Scores to the log2 domain and the tile's row maximum. Keys past the
+        // end, or after the row when causal, are masked to -inf; only tiles
+        // that reach the sequence end or cross the diagonal need the test
+        // (lane holds keys kv0 + 32 jb + 8 (e / 4) + 4 hi + e % 4).
+        const float c = p.scale_log2;
+        const bool edge = kv0 + T::BN > Skv || (p.causal && kv0 + T::BN - 1 > qw);
+        float mt;
+        if (edge) {
+            const int lim = p.causal ? min(Skv, qrow + 1) : Skv;
+            const int rel = lim - kv0 - 4 * hi;  // key offsets below rel are visible
+            mt = -INFINITY;
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
+            for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float t = s[jb][e] * p.scale_log2;
-                s[jb][e] = (32 * jb + 8 * (e / 4) + e % 4 < rel) ? t : -INFINITY;
-            }
-        float mt = -INFINITY;
+                for (int e = 0; e < 16; ++e) {
+                    const float t = (32 * jb + 8 * (e / 4) + e % 4 < rel) ? s[jb][e] * c : -INFINITY;
+                    s[jb][e] = t;
+                    mt = fmaxf(mt, t);
+                }
+        } else {
+            // max(s c) = c max(s) for c >= 0, c min(s) otherwise; the scaling
+            // is folded into the exponent below
+            float hi_s = -INFINITY, lo_s = INFINITY;
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
+            for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[jb][e]);
+                for (int e = 0; e < 16; ++e) {
+                    hi_s = fmaxf(hi_s, s[jb][e]);
+                    lo_s = fminf(lo_s, s[jb][e]);
+                }
+            mt = c >= 0.f ? hi_s * c : lo_s * c;
+        }
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        // a row with nothing visible yet keeps m = -inf; its p are 0
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2_fast(m_run - m_use);
-        m_run = m_new;
+        // Lazy rescaling: p = 2^(t - m_run) with m_run, the reference of the
+        // row, moved only when a score exceeds it by more than 2^kTau (then
+        // O and l are rescaled). Every p stays <= 2^kTau, so fp16 holds it
+        // with the same relative precision, and O / l is unchanged in exact
+        // arithmetic. A row with nothing visible yet keeps m_run = -inf.
+        constexpr float kTau = 8.0f;
+        if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = m_new == m_run ? 1.0f : exp2_fast(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc_o[db][e] *= alpha;
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float ls = 0.f;
         f16x8 pf[4];
+        if (edge) {
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
+            for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float pe = exp2_fast(s[jb][e] - m_use);
-                ls += pe;
-                pf[2 * jb + e / 8][e % 8] = (_Float16)pe;
-            }
-        l_run = l_run * alpha + ls;
+                for (int e = 0; e < 16; ++e) {
+                    const float pe = exp2_fast(s[jb][e] - m_use);
+                    ls += pe;
+                    pf[2 * jb + e / 8][e % 8] = (_Float16)pe;
+                }
+        } else {
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db)
+            for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc_o[db][e] *= alpha;
+                for (int e = 0; e < 16; ++e) {
+                    const float pe = exp2_fast(fmaf(s[jb][e], c, -m_use));
+                    ls += pe;
+                    pf[2 * jb + e / 8][e % 8] = (_Float16)pe;
+                }
+        }
+        l_run += ls;
         // O += P V: chunk c holds keys 16 c + {0-3, 8-11} (hi = 0) or
         // {4-7, 12-15} (hi = 1)
 #pragma unroll
@@ -413,22 +466,35 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)
             }
     };
 
-    // two LDS stages; every pass handles tiles j (stage 0) and j + 1 (stage 1)
-    auto sync = [&]<int N>() {
-        wait_vmcnt<N>();
+    // Software pipeline over key tiles, one barrier per tile. Iteration j:
+    //   wait for K(j+1) and V(j) (issued one iteration earlier), barrier;
+    //   issue K(j+2) and V(j+1) into the stages freed by iteration j-1;
+    //   S' = Q K(j+1)^T (matrix ops), then the softmax of tile j (VALU work
+    //   that runs while those matrix ops execute), then O += P V(j).
+    // K and V each have two stages, offset by one tile; j runs in pairs so
+    // every stage index is a compile-time constant.
+    auto sync = [&]() {
+        wait_vmcnt<0>();
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
     };
-    issue.template operator()<0>(0);
+    f32x16 sa[2], sb[2];
+    issue_k.template operator()<0>(0);
+    issue_v.template operator()<0>(0);
+    issue_k.template operator()<1>(1);
+    sync();
+    qk.template operator()<0>(sa);
     for (int j = 0; j < nkb2; j += 2) {
-        issue.template operator()<1>(j + 1);
-        sync.template operator()<2 * T::LW>();  // tile j has landed (tile j+1 in flight)
-        tile.template operator()<0>(j);
-        __builtin_amdgcn_s_barrier();           // stage 0 free again
-        issue.template operator()<0>(j + 2);
-        sync.template operator()<2 * T::LW>();
-        tile.template operator()<1>(j + 1);
-        __builtin_amdgcn_s_barrier();
+        sync();
+        issue_k.template operator()<0>(j + 2);
+        issue_v.template operator()<1>(j + 1);
+        qk.template operator()<1>(sb);
+        softmax_pv.template operator()<0>(j, sa);
+        sync();
+        issue_k.template operator()<1>(j + 3);
+        issue_v.template operator()<0>(j + 2);
+        qk.template operator()<0>(sa);
+        softmax_pv.template operator()<1>(j + 1, sb);
     }
     wait_vmcnt<0>();  // the last (empty) loads must land before the kernel ends
 
