@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <cmath>
 #include <mutex>
 
 #include "attention.h"
@@ -97,6 +98,7 @@ int flash_attn_fwd_f16(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
 {
     if (B < 0 || H < 0 || Sq < 0 || Skv < 0 || D < 0) return GEMM_RELU_EINVAL;
     if (causal != 0 && causal != 1) return GEMM_RELU_EINVAL;
+    if (!std::isfinite(scale)) return GEMM_RELU_EINVAL;
     if (D != 64 && D != 128) return GEMM_RELU_EUNSUPPORTED;
     if (B > INT32_MAX || H > INT32_MAX || B * H > INT32_MAX || Sq > INT32_MAX || Skv > INT32_MAX)
         return GEMM_RELU_EUNSUPPORTED;
@@ -126,7 +128,11 @@ int flash_attn_fwd_f16(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
     a.BH = (int)BH;
     a.Sq = (int)Sq;
     a.Skv = (int)Skv;
+    // the kernels fold the scale into their exponents and use its sign to
+    // take row maxima; a zero scale (every score 0) becomes a tiny positive
+    // one, which gives the same uniform weights
     a.scale_log2 = scale * gemm_relu::attn::kLog2e;
+    if (a.scale_log2 == 0.0f) a.scale_log2 = 1e-30f;
     a.causal = causal;
     a.nqb = (int)nqb;
     if (D == 64) launch_attn<64>(a, s);

@@ -376,42 +376,36 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two 
         }
     };
 
-    // softmax of tile j's scores s, then O += P V with V stage S
-    auto softmax_pv = [&]<int S>(int j, f32x16 (&s)[2]) {
-        const char* vb = reinterpret_cast<const char*>(S == 0 ? vs0 : vs1);
+    // The row statistics of tile j's scores s: keys past the end, or after
+    // the row when causal, are masked (only tiles at the sequence end or the
+    // diagonal need the test; lane holds keys kv0 + 32 jb + 8 (e / 4) + 4 hi +
+    // e % 4), the tile's row maximum is taken -- max(s c) = c max(s) for
+    // c > 0, c min(s) for c < 0 -- and the row's reference m_run moves when
+    // needed. Masked scores become the infinity that c turns into -inf.
+    // Returns the reference the exponents use.
+    auto stats = [&](int j, f32x16 (&s)[2]) -> float {
         const int kv0 = j * T::BN;
-        // Scores to the log2 domain and the tile's row maximum. Keys past the
-        // end, or after the row when causal, are masked to -inf; only tiles
-        // that reach the sequence end or cross the diagonal need the test
-        // (lane holds keys kv0 + 32 jb + 8 (e / 4) + 4 hi + e % 4).
         const float c = p.scale_log2;
         const bool edge = kv0 + T::BN > Skv || (p.causal && kv0 + T::BN - 1 > qw);
-        float mt;
         if (edge) {
             const int lim = p.causal ? min(Skv, qrow + 1) : Skv;
             const int rel = lim - kv0 - 4 * hi;  // key offsets below rel are visible
-            mt = -INFINITY;
+            const float dead = c > 0.f ? -INFINITY : INFINITY;
 #pragma unroll
             for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float t = (32 * jb + 8 * (e / 4) + e % 4 < rel) ? s[jb][e] * c : -INFINITY;
-                    s[jb][e] = t;
-                    mt = fmaxf(mt, t);
-                }
-        } else {
-            // max(s c) = c max(s) for c >= 0, c min(s) otherwise; the scaling
-            // is folded into the exponent below
-            float hi_s = -INFINITY, lo_s = INFINITY;
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    hi_s = fmaxf(hi_s, s[jb][e]);
-                    lo_s = fminf(lo_s, s[jb][e]);
-                }
-            mt = c >= 0.f ? hi_s * c : lo_s * c;
+                for (int e = 0; e < 16; ++e)
+                    s[jb][e] = (32 * jb + 8 * (e / 4) + e % 4 < rel) ? s[jb][e] : dead;
         }
+        float hi_s = -INFINITY, lo_s = INFINITY;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                hi_s = fmaxf(hi_s, s[jb][e]);
+                lo_s = fminf(lo_s, s[jb][e]);
+            }
+        float mt = c > 0.f ? hi_s * c : lo_s * c;
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         // Lazy rescaling: p = 2^(t - m_run) with m_run, the reference of the
         // row, moved only when a score exceeds it by more than 2^kTau (then
@@ -429,41 +423,73 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two 
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc_o[db][e] *= alpha;
         }
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        return m_run == -INFINITY ? 0.f : m_run;
+    };
+
+    // One straight-line stretch per tile, matrix ops and VALU work
+    // interleaved in a fixed order (scheduling barriers):
+    //   phase 1: S' = Q K(next)^T from K stage SK, each fragment read two
+    //            matrix ops ahead, with the exponentials of the current
+    //            tile's first 24 scores (chunks 0-2 of P) between them;
+    //   phase 2: O += P V from V stage SV, chunk by chunk, fragments read
+    //            one matrix op ahead, with the last 8 exponentials (chunk 3)
+    //            between the matrix ops of chunks 0 and 1.
+    // p = 2^(s c - m): the scale folded into one FMA per score.
+    auto fused = [&]<int SK, int SV>(f32x16 (&s_cur)[2], f32x16 (&s_next)[2], float m_use) {
+        const char* kb = reinterpret_cast<const char*>(SK == 0 ? ks0 : ks1);
+        const char* vb = reinterpret_cast<const char*>(SV == 0 ? vs0 : vs1);
+        const float c = p.scale_log2;
+        constexpr int NQ = 2 * T::KK;       // Q K^T matrix ops
+        constexpr int NP = 4 * T::DB;       // P V matrix ops
+        constexpr int EX1 = 24;             // exponentials in phase 1
         float ls = 0.f;
         f16x8 pf[4];
-        if (edge) {
+        auto expo = [&](int x) {  // score x of the lane: block x / 16, element x % 16 -> chunk x / 8
+            const float pe = exp2_fast(fmaf(s_cur[x / 16][x % 16], c, -m_use));
+            ls += pe;
+            pf[x / 8][x % 8] = (_Float16)pe;
+        };
+        // Q K^T op t: key block t % 2, reduction chunk t / 2 -- neighbouring
+        // matrix ops accumulate into different registers
+        auto read_k = [&](int t) -> f16x8 {
+            return *reinterpret_cast<const f16x8*>(kb + krd[t % 2][t / 2]);
+        };
+        auto read_v = [&](int u) -> f16x8 {
+            const char* base = vb + vrd[u / T::DB][u % T::DB];
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GR_LDS i16x4*)(base));
+            const i16x4 hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GR_LDS i16x4*)(base + 8 * D * 2));
+            return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hv, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
+        for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float pe = exp2_fast(s[jb][e] - m_use);
-                    ls += pe;
-                    pf[2 * jb + e / 8][e % 8] = (_Float16)pe;
-                }
-        } else {
+            for (int e = 0; e < 16; ++e) s_next[jb][e] = 0.f;
+        f16x8 kr[NQ];
+        kr[0] = read_k(0);
+        kr[1] = read_k(1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
+        for (int t = 0; t < NQ; ++t) {
+            if (t + 2 < NQ) kr[t + 2] = read_k(t + 2);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float pe = exp2_fast(fmaf(s[jb][e], c, -m_use));
-                    ls += pe;
-                    pf[2 * jb + e / 8][e % 8] = (_Float16)pe;
-                }
+            for (int x = t * EX1 / NQ; x < (t + 1) * EX1 / NQ; ++x) expo(x);
+            s_next[t % 2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kr[t], qf[t / 2], s_next[t % 2], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        f16x8 vr[NP];
+        vr[0] = read_v(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
+            if (u + 1 < NP) vr[u + 1] = read_v(u + 1);
+            constexpr int NEX2 = 32 - EX1;   // spread over the chunk-0 and chunk-1 matrix ops
+#pragma unroll
+            for (int x = EX1 + u * NEX2 / (2 * T::DB); x < EX1 + (u + 1) * NEX2 / (2 * T::DB) && x < 32; ++x)
+                if (u < 2 * T::DB) expo(x);
+            acc_o[u % T::DB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vr[u], pf[u / T::DB], acc_o[u % T::DB], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
         l_run += ls;
-        // O += P V: chunk c holds keys 16 c + {0-3, 8-11} (hi = 0) or
-        // {4-7, 12-15} (hi = 1)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int db = 0; db < T::DB; ++db) {
-                const char* base = vb + vrd[c][db];
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GR_LDS i16x4*)(base));
-                const i16x4 hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GR_LDS i16x4*)(base + 8 * D * 2));
-                const f16x8 vf = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hv, 0, 1, 2, 3, 4, 5, 6, 7));
-                acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[c], acc_o[db], 0, 0, 0);
-            }
     };
 
     // Software pipeline over key tiles, one barrier per tile. Iteration j:
@@ -488,13 +514,11 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two 
         sync();
         issue_k.template operator()<0>(j + 2);
         issue_v.template operator()<1>(j + 1);
-        qk.template operator()<1>(sb);
-        softmax_pv.template operator()<0>(j, sa);
+        fused.template operator()<1, 0>(sa, sb, stats(j, sa));
         sync();
         issue_k.template operator()<1>(j + 3);
         issue_v.template operator()<0>(j + 2);
-        qk.template operator()<0>(sa);
-        softmax_pv.template operator()<1>(j + 1, sb);
+        fused.template operator()<0, 1>(sb, sa, stats(j + 1, sb));
     }
     wait_vmcnt<0>();  // the last (empty) loads must land before the kernel ends
 
