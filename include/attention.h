@@ -46,9 +46,10 @@ int softmax_rows_f16(int64_t rows, int64_t cols, const void* X, void* Y, void* s
  *   lse       : NULL, or [B][H][Sq] fp32 receiving m_i + ln(sum_j exp(s_ij - m_i))
  *               (-inf for a row with no keys)
  *   D         : 64 or 128
- * Skv == 0 gives O = 0. Pointers must be 16-byte aligned (lse 4-byte); O must
- * not overlap Q, K, V or lse. Errors: EINVAL (negative size, NULL with data,
- * causal not 0/1, overlap), EUNSUPPORTED (D not 64/128, a size above the
+ * scale is any finite float (1/sqrt(D) is the usual choice). Skv == 0 gives
+ * O = 0. Pointers must be 16-byte aligned (lse 4-byte); O must not overlap Q,
+ * K, V or lse. Errors: EINVAL (negative size, NULL with data, causal not 0/1,
+ * scale not finite, overlap), EUNSUPPORTED (D not 64/128, a size above the
  * kernel's 32-bit offsets (B*H, Sq, Skv < 2^31, S * D < 2^30), misaligned
  * pointer, device not gfx950), EHIP.
  */

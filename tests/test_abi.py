@@ -255,6 +255,8 @@ def test_attention_arguments_rejected():
     assert f(1, 1, 4, 4, 64, Q, K, V, Q, 0, 0.1, 0) == gr.EINVAL       # O overlaps Q
     assert f(1, 1, 2 ** 24, 4, 64, Q, K, V, O, 0, 0.1, 0) == gr.EUNSUPPORTED  # in-head offsets
     assert f(1, 1, 0, 4, 64, 0, K, V, 0, 0, 0.1, 0) == gr.OK            # nothing to write
+    assert f(1, 1, 4, 4, 64, Q, K, V, O, 0, float("inf"), 0) == gr.EINVAL
+    assert f(1, 1, 4, 4, 64, Q, K, V, O, 0, float("nan"), 0) == gr.EINVAL
 
 
 def test_empty_output_is_a_no_op():

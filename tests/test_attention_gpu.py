@@ -176,3 +176,18 @@ def test_attention_deterministic():
     ref = gr.flash_attn_fwd(q, k, v, causal=True)
     for _ in range(20):
         assert torch.equal(gr.flash_attn_fwd(q, k, v, causal=True).view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.3])
+def test_attention_scale_sign_and_zero(scale):
+    # the kernels take row maxima through the sign of the scale; zero gives
+    # uniform weights over the visible keys
+    q = randn_f16((1, 2, 150, 64), 31)
+    k = randn_f16((1, 2, 170, 64), 32)
+    v = randn_f16((1, 2, 170, 64), 33)
+    for causal in (False, True):
+        got, lse = run_attn(q, k, v, causal, scale)
+        want, lse_o, pv = oracle.attention_f16(workloads.as_u16(q), workloads.as_u16(k), workloads.as_u16(v),
+                                               scale, causal, want_lse=True, want_pv=True)
+        check_attn(got, want, pv, lse, lse_o, score_bound(q, k, scale), f"scale {scale} causal {causal}")
+
