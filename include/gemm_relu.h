@@ -38,6 +38,10 @@
  * stream reuse it in order; calls on different streams use different
  * workspaces. Two host threads enqueueing on the same stream at the same
  * time race on the workspace. Failure to allocate gives GEMM_RELU_ENOMEM.
+ * Creating or growing a workspace is refused with GEMM_RELU_EUNSUPPORTED
+ * while the stream is being captured into a HIP graph (it allocates and
+ * clears memory); make one call of the same or a larger shape on that stream
+ * before capturing. Calls that fit the existing workspace capture normally.
  *
  * Errors: every entry point returns a gemm_relu_status. All argument checks
  * happen before any HIP runtime call, so a rejected call has no side effects.

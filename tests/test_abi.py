@@ -84,6 +84,15 @@ def test_tile_selection_is_host_only():
     assert name(1000, 1016, 1000).startswith("splitk_32x")
     assert name(512, 4096, 8192).startswith("splitk_64x")  # 256 tiles of 64x128
     assert name(256, 256, 256).startswith("16x64")  # latency-bound
+    # transposed layouts have their own rates: with A stored K x M the split-K
+    # tiles (element-wise A reads) lose to the pipelined ones at mid sizes
+    tname = lambda *s, **kw: gr.tile_name(gr.select_tile(*s, **kw))  # noqa: E731
+    assert tname(1024, 1024, 1024, trans_a=True).startswith("64x256")
+    assert tname(512, 4096, 8192, trans_a=True).startswith("64x256")
+    for ta in (False, True):
+        for tb in (False, True):
+            assert tname(16, 8192, 8192, trans_a=ta, trans_b=tb).startswith("splitk_16x")  # few rows
+            assert gr.select_tile(4096, 4096, 4096, trans_a=ta, trans_b=tb) == 0
     # the split-K kernel's 32-bit A offsets: M*K*2 must stay below 2^31
     assert "splitk" not in name(65536, 256, 16384)
     # K or N not a multiple of 8 -> the generic element-wise path

@@ -358,3 +358,37 @@ def test_raw_abi_call_and_empty_shapes():
     want = oracle.gemm_relu_f16(workloads.as_u16(a), workloads.as_u16(b))
     parity.check(workloads.as_u16(c.cpu()), want, label="raw call")
     assert gr.gemm_relu_f16(0, 64, 64, ad.data_ptr(), bd.data_ptr(), c.data_ptr(), 0) == gr.OK
+
+
+def test_splitk_workspace_under_graph_capture():
+    # a stream being captured cannot get a new workspace (allocation and a
+    # memset would land in the graph): the call is refused, nothing is
+    # recorded; after one call outside capture, capture and replays work
+    M, N, K = 16, 1024, 4096
+    a, b = workloads.make_inputs(M, N, K, dist="intsmall", seed=77)
+    want = oracle.gemm_relu_f16(workloads.as_u16(a), workloads.as_u16(b))
+    ad, bd = a.cuda(), b.cuda()
+    out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    s = torch.cuda.Stream()
+    assert "splitk" in gr.tile_name(gr.select_tile(M, N, K))
+    g = torch.cuda.CUDAGraph()
+    st = None
+    with torch.cuda.graph(g, stream=s):
+        st = gr.gemm_relu_f16(M, N, K, ad.data_ptr(), bd.data_ptr(), out.data_ptr(), s.cuda_stream)
+    assert st == gr.EUNSUPPORTED
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        gr.gemm_relu(ad, bd, out=out)   # creates the workspace on s
+    torch.cuda.synchronize()
+    assert np.array_equal(workloads.as_u16(out.cpu()), want)
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2, stream=s):
+        st = gr.gemm_relu_f16(M, N, K, ad.data_ptr(), bd.data_ptr(), out.data_ptr(), s.cuda_stream)
+    assert st == gr.OK
+    for rep in range(3):
+        out.fill_(3.0)
+        torch.cuda.synchronize()
+        g2.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(workloads.as_u16(out.cpu()), want), f"replay {rep}"
+

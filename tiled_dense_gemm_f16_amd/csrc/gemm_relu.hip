@@ -208,34 +208,39 @@ bool fast_path_ok(int64_t M, int64_t N, int64_t K, bool ta, bool tb, const void*
 // The split-K kernel addresses A with 32-bit offsets.
 bool splitk_ok(int64_t M, int64_t K) { return M * K * 2 < ((int64_t)1 << 31); }
 
-// The shape heuristic: a cost model whose constants were fitted to an offline
-// sweep (tune.py) of every tile and block order over 38 shapes, from 1 to 8192
-// rows, 64 to 8192 columns and 256 to 12288 deep. A tile's predicted time is
+// The shape heuristic: a cost model whose constants were fitted to offline
+// sweeps (tune.py) of every tile and block order: 38 shapes in the NN layout,
+// from 1 to 8192 rows, 64 to 8192 columns and 256 to 12288 deep, and 12 shapes
+// in each transposed layout. A tile's predicted time is
 //   rounds x (2 bm bn kc FLOP) / rate,   rounds = ceil(workgroups / 256),
 // floored by the HBM time of the algorithmic bytes, plus for split-K launches
 // the cost of writing and re-reading the fp32 partials and of the combine.
-// The rate is what one compute unit sustains on that tile (larger tiles reuse
-// each loaded byte more; the fitted rates already include the clock the chip
-// holds under load). The model picks the measured fastest tile on 31 of the
-// 38 shapes and is within 15 % of it on the rest (1 % slower on average);
-// the rules it replaced, which looked at M and the 256x256 tile count alone,
+// The rate is what one compute unit sustains on that tile in that operand
+// layout (larger tiles reuse each loaded byte more; the fitted rates include
+// the clock the chip holds under load). Two rules sit on top: few rows
+// (M <= 64) always take a split-K tile, and the 16x64 tile is only for
+// latency-bound outputs of at most 64 K elements. In the NN layout the model
+// picks a launch 1.5 % slower than the measured fastest on average (21 % at
+// worst); in the transposed layouts 1-6 % on average (27 % at worst). The
+// rules it replaced, which looked at M and the 256x256 tile count alone,
 // were up to 6x slower on shapes they were not written for.
 struct AutoTile {
     int id;
-    double tflops_per_cu;
+    double tflops_per_cu[4];  // NN, NT, TN, TT (index 2 * trans_a + trans_b)
 };
 constexpr AutoTile kAutoTiles[] = {
-    {0, 6.96},  // 256x256 pipelined
-    {9, 5.24},  // 128x256 pipelined
-    {10, 3.21}, // 64x256 pipelined
-    {6, 2.13},  // split-K 64x128
-    {5, 1.59},  // split-K 32x128
-    {4, 1.12},  // split-K 16x128
-    {2, 0.895}, // 64x64 staged
-    {3, 0.273}, // 16x64 staged
+    {0, {6.96, 5.78, 6.63, 6.10}},   // 256x256 pipelined
+    {9, {5.24, 3.90, 4.96, 4.04}},   // 128x256 pipelined
+    {10, {3.21, 2.21, 2.79, 2.25}},  // 64x256 pipelined
+    {6, {2.13, 1.27, 0.570, 0.517}}, // split-K 64x128
+    {5, {1.59, 0.772, 0.390, 0.344}},// split-K 32x128
+    {4, {1.12, 0.472, 0.408, 0.324}},// split-K 16x128
+    {2, {0.895, 1.24, 0.429, 0.756}},// 64x64 staged
+    {3, {0.273, 0.706, 0.118, 0.262}},// 16x64 staged
 };
 constexpr double kComputeUnits = 256.0;
 constexpr double kHbmBytesPerUs = 6.68e6;          // 6.68 TB/s
+constexpr double kStagedHbmShare = 0.75;           // the register-staged kernels reach less of it
 constexpr double kPartialUsPerByte = 0.97e-6;      // partials: written once, read once
 constexpr double kCombineUs = 3.25;                // last-workgroup combine and counters
 
@@ -244,29 +249,34 @@ struct Prediction {
     double compute;  // its compute part: breaks ties between HBM-bound tiles
 };
 
-Prediction predict(const AutoTile& at, int64_t M, int64_t N, int64_t K)
+Prediction predict(const AutoTile& at, int layout, int64_t M, int64_t N, int64_t K)
 {
     const gemm_relu_tile_desc& d = kTiles[at.id].desc;
     const int64_t tiles = ((M + d.bm - 1) / d.bm) * ((N + d.bn - 1) / d.bn);
     int splits = 1, kc = (int)K;
     if (d.split_k) choose_splits(K, tiles, splits, kc);
     const double rounds = (double)((tiles * splits + (int64_t)kComputeUnits - 1) / (int64_t)kComputeUnits);
-    const double compute = rounds * 2.0 * d.bm * d.bn * (double)kc / (at.tflops_per_cu * 1e6);
-    const double memory = 2.0 * ((double)M * K + (double)K * N + (double)M * N) / kHbmBytesPerUs;
+    const double compute = rounds * 2.0 * d.bm * d.bn * (double)kc / (at.tflops_per_cu[layout] * 1e6);
+    const double bw = kHbmBytesPerUs * (d.family == GEMM_RELU_FAMILY_STAGED ? kStagedHbmShare : 1.0);
+    const double memory = 2.0 * ((double)M * K + (double)K * N + (double)M * N) / bw;
     const double combine = splits > 1 ? kPartialUsPerByte * 8.0 * (double)M * N * splits + kCombineUs : 0.0;
     return {(compute > memory ? compute : memory) + combine, compute};
 }
 
 // The tile of least predicted time; among tiles bound by the same HBM time,
 // the one with the least compute (the fewest padded rows).
-int choose_tile(int64_t M, int64_t N, int64_t K)
+int choose_tile(int64_t M, int64_t N, int64_t K, bool ta, bool tb)
 {
     const bool sk = splitk_ok(M, K);
+    const bool few_rows = M <= 64 && sk;
+    const int layout = 2 * (ta ? 1 : 0) + (tb ? 1 : 0);
     int best = -1;
     Prediction bp{0.0, 0.0};
     for (const AutoTile& at : kAutoTiles) {
-        if (kTiles[at.id].desc.split_k && !sk) continue;
-        const Prediction p = predict(at, M, N, K);
+        const gemm_relu_tile_desc& d = kTiles[at.id].desc;
+        if (d.split_k ? !sk : few_rows) continue;
+        if (at.id == 3 && M * N > 65536) continue;
+        const Prediction p = predict(at, layout, M, N, K);
         const bool tie = p.us - bp.us < 1e-9 * bp.us && bp.us - p.us < 1e-9 * bp.us;
         if (best < 0 || (tie ? p.compute < bp.compute : p.us < bp.us)) {
             best = at.id;
@@ -299,6 +309,13 @@ int get_workspace(int dev, hipStream_t stream, size_t slots, size_t partial_byte
     std::lock_guard<std::mutex> lk(g_ws_mu);
     Workspace& w = g_ws[std::make_pair(dev, stream)];
     if (w.base == nullptr || w.counter_slots < slots || w.partial_bytes < partial_bytes) {
+        // creating or growing the workspace allocates, synchronises and clears
+        // it with a memset on the stream: none of that may be recorded into a
+        // graph, so a stream under capture must already have a workspace large
+        // enough (one such call made on it outside capture)
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return GEMM_RELU_EHIP;
+        if (cap != hipStreamCaptureStatusNone) return GEMM_RELU_EUNSUPPORTED;
         const size_t ns = slots > w.counter_slots ? slots : w.counter_slots;
         const size_t np = partial_bytes > w.partial_bytes ? partial_bytes : w.partial_bytes;
         if (w.base != nullptr) {
@@ -405,7 +422,7 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B,
 
     const bool vec = fast_path_ok(M, N, K, ta, tb, A, B, C);
     const int tile =
-        (opts && opts->tile != GEMM_RELU_TILE_AUTO) ? opts->tile : (vec ? choose_tile(M, N, K) : kGenericTile);
+        (opts && opts->tile != GEMM_RELU_TILE_AUTO) ? opts->tile : (vec ? choose_tile(M, N, K, ta, tb) : kGenericTile);
     // the split-K tiles have no element-wise instance: unaligned shapes take
     // the generic tile
     const TileEntry& te = (!vec && kTiles[tile].desc.split_k) ? kTiles[kGenericTile] : kTiles[tile];
@@ -487,8 +504,9 @@ int gemm_relu_select_tile_op(int64_t M, int64_t N, int64_t K, int op_a, int op_b
 {
     if ((op_a != GEMM_RELU_OP_N && op_a != GEMM_RELU_OP_T) || (op_b != GEMM_RELU_OP_N && op_b != GEMM_RELU_OP_T))
         return -1;
-    if (!fast_path_ok(M, N, K, op_a == GEMM_RELU_OP_T, op_b == GEMM_RELU_OP_T, A, B, C)) return -1;
-    return choose_tile(M, N, K);
+    const bool ta = op_a == GEMM_RELU_OP_T, tb = op_b == GEMM_RELU_OP_T;
+    if (!fast_path_ok(M, N, K, ta, tb, A, B, C)) return -1;
+    return choose_tile(M, N, K, ta, tb);
 }
 
 int gemm_relu_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C,

@@ -65,13 +65,15 @@ def candidates(M: int, N: int, K: int, lds_limit: int = LDS_PER_WORKGROUP) -> li
     return out
 
 
-def _inputs(M, N, K, epilogue, seed, device, copies):
+def _inputs(M, N, K, epilogue, seed, device, copies, trans_a=False, trans_b=False):
+    """Seeded inputs in their stored layouts (A as K x M with trans_a, B as
+    N x K with trans_b)."""
     import torch
 
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
-    a = torch.randn((M, K), generator=gen, device=device, dtype=torch.float32).half()
-    b = torch.randn((K, N), generator=gen, device=device, dtype=torch.float32).half()
+    a = torch.randn((K, M) if trans_a else (M, K), generator=gen, device=device, dtype=torch.float32).half()
+    b = torch.randn((N, K) if trans_b else (K, N), generator=gen, device=device, dtype=torch.float32).half()
     bias = None
     if epilogue == "bias_gelu":
         bias = (torch.randn((N,), generator=gen, device=device, dtype=torch.float32) * K ** 0.5).half()
@@ -80,10 +82,10 @@ def _inputs(M, N, K, epilogue, seed, device, copies):
     return a_s, b_s, bias
 
 
-def _reference(a, b, bias, epilogue):
+def _reference(a, b, bias, epilogue, trans_a=False, trans_b=False):
     import torch
 
-    r = a.double() @ b.double()
+    r = (a.double().t() if trans_a else a.double()) @ (b.double().t() if trans_b else b.double())
     if epilogue == "bias_gelu":
         return torch.nn.functional.gelu(r + bias.double())
     return torch.relu(r)
@@ -91,9 +93,10 @@ def _reference(a, b, bias, epilogue):
 
 def tune(M: int, N: int, K: int, *, epilogue: str = "relu", seed: int = 0, graph: int = 20,
          replays: int = 5, rotate_bytes: int = DEFAULT_ROTATE_BYTES, device: int = 0,
-         only: list[dict] | None = None) -> dict:
-    """Validates and times every candidate for (M, N, K); returns
-    {"shape", "epilogue", "arch", "results": [...] fastest first, "best"}.
+         only: list[dict] | None = None, trans_a: bool = False, trans_b: bool = False) -> dict:
+    """Validates and times every candidate for (M, N, K) with the operand
+    layouts trans_a / trans_b (A stored K x M, B stored N x K); returns
+    {"shape", "epilogue", "layout", "arch", "results": [...] fastest first, "best"}.
     Candidates whose output fails validation or whose call fails are kept in
     the results with "ok": False and never chosen."""
     import torch
@@ -107,8 +110,8 @@ def tune(M: int, N: int, K: int, *, epilogue: str = "relu", seed: int = 0, graph
     copies = max(1, min(8, -(-rotate_bytes // max(in_bytes, 1))))
     cands = only if only is not None else candidates(M, N, K)
     with torch.cuda.device(dev):
-        a_s, b_s, bias = _inputs(M, N, K, epilogue, seed, dev, copies)
-        ref = _reference(a_s[0], b_s[0], bias, epilogue)
+        a_s, b_s, bias = _inputs(M, N, K, epilogue, seed, dev, copies, trans_a, trans_b)
+        ref = _reference(a_s[0], b_s[0], bias, epilogue, trans_a, trans_b)
         bound = 1e-2 + 1e-2 * ref.abs()
         c = torch.empty((M, N), dtype=torch.float16, device=dev)
         stream = torch.cuda.Stream(dev)
@@ -118,10 +121,11 @@ def tune(M: int, N: int, K: int, *, epilogue: str = "relu", seed: int = 0, graph
 
             def call(i, opts=opts):
                 if epilogue == "bias_gelu":
-                    return gr.gemm_bias_gelu_f16_ex(M, N, K, a_s[i].data_ptr(), b_s[i].data_ptr(), bias.data_ptr(),
-                                                    c.data_ptr(), stream.cuda_stream, opts)
-                return gr.gemm_relu_f16_ex(M, N, K, a_s[i].data_ptr(), b_s[i].data_ptr(), c.data_ptr(),
-                                           stream.cuda_stream, opts)
+                    return gr.gemm_bias_gelu_f16_op(M, N, K, a_s[i].data_ptr(), int(trans_a), b_s[i].data_ptr(),
+                                                    int(trans_b), bias.data_ptr(), c.data_ptr(), stream.cuda_stream,
+                                                    opts)
+                return gr.gemm_relu_f16_op(M, N, K, a_s[i].data_ptr(), int(trans_a), b_s[i].data_ptr(), int(trans_b),
+                                           c.data_ptr(), stream.cuda_stream, opts)
 
             res = dict(cand)
             torch.cuda.synchronize(dev)
@@ -163,13 +167,15 @@ def tune(M: int, N: int, K: int, *, epilogue: str = "relu", seed: int = 0, graph
     results.sort(key=lambda r: (not r["ok"], r.get("us", float("inf"))))
     best = results[0] if results and results[0]["ok"] else None
     arch = torch.cuda.get_device_properties(dev).gcnArchName.split(":")[0]
-    return {"shape": [M, N, K], "epilogue": epilogue, "arch": arch, "copies": copies, "graph": graph,
-            "results": results, "best": best, "default": _default_of(M, N, K, results)}
+    layout = ("t" if trans_a else "n") + ("t" if trans_b else "n")
+    return {"shape": [M, N, K], "epilogue": epilogue, "layout": layout, "arch": arch, "copies": copies,
+            "graph": graph, "results": results, "best": best,
+            "default": _default_of(M, N, K, results, trans_a, trans_b)}
 
 
-def _default_of(M, N, K, results):
+def _default_of(M, N, K, results, trans_a=False, trans_b=False):
     """The result of the launch the library makes without opts, if it was timed."""
-    auto = gr.select_tile(M, N, K)
+    auto = gr.select_tile(M, N, K, trans_a=trans_a, trans_b=trans_b)
     if auto < 0:
         return None
     g = gr.tile_info(auto)["default_group_m"]
@@ -179,8 +185,8 @@ def _default_of(M, N, K, results):
     return None
 
 
-def _key(arch: str, epilogue: str, M: int, N: int, K: int) -> str:
-    return f"{arch}/{epilogue}/{M}x{N}x{K}"
+def _key(arch: str, epilogue: str, M: int, N: int, K: int, layout: str = "nn") -> str:
+    return f"{arch}/{epilogue}/{M}x{N}x{K}" + ("" if layout == "nn" else f"/{layout}")
 
 
 def save(result: dict, path: str) -> None:
@@ -192,7 +198,7 @@ def save(result: dict, path: str) -> None:
     if result["best"] is None:
         raise ValueError("no candidate passed validation")
     b = result["best"]
-    table[_key(result["arch"], result["epilogue"], *result["shape"])] = {
+    table[_key(result["arch"], result["epilogue"], *result["shape"], result.get("layout", "nn"))] = {
         "tile": b["tile"], "tile_name": b["tile_name"], "block_order": b["block_order"], "group_m": b["group_m"],
         "us": round(b["us"], 3), "candidates": len(result["results"])}
     tmp = path + ".tmp"
@@ -201,14 +207,14 @@ def save(result: dict, path: str) -> None:
     os.replace(tmp, path)
 
 
-def lookup(path: str, arch: str, epilogue: str, M: int, N: int, K: int) -> dict | None:
+def lookup(path: str, arch: str, epilogue: str, M: int, N: int, K: int, layout: str = "nn") -> dict | None:
     """Keyword arguments (tile, block_order, group_m) of the stored winner, or
     None. The tile is checked by name, so a table written for another build
     of the library is not applied to different kernels."""
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        e = json.load(f).get(_key(arch, epilogue, M, N, K))
+        e = json.load(f).get(_key(arch, epilogue, M, N, K, layout))
     if e is None or not (0 <= e["tile"] < gr.tile_count()) or gr.tile_name(e["tile"]) != e["tile_name"]:
         return None
     return {"tile": e["tile"], "block_order": e["block_order"], "group_m": e["group_m"]}
@@ -216,8 +222,9 @@ def lookup(path: str, arch: str, epilogue: str, M: int, N: int, K: int) -> dict 
 
 def format_result(r: dict, top: int = 0) -> str:
     M, N, K = r["shape"]
-    auto = gr.select_tile(M, N, K)
-    lines = [f"{r['epilogue']} {M}x{N}x{K} on {r['arch']}: {len(r['results'])} candidates, "
+    lay = r.get("layout", "nn")
+    auto = gr.select_tile(M, N, K, trans_a=lay[0] == "t", trans_b=lay[1] == "t")
+    lines = [f"{r['epilogue']} {lay} {M}x{N}x{K} on {r['arch']}: {len(r['results'])} candidates, "
              f"{r['copies']} input copies, graphs of {r['graph']}; library default tile {auto} "
              f"({gr.tile_name(auto) if auto >= 0 else 'generic'})"]
     d, b = r.get("default"), r["best"]
@@ -245,6 +252,8 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description="time and validate every compiled tile on the given shapes")
     ap.add_argument("shapes", nargs="+", type=_shape, metavar="MxNxK")
     ap.add_argument("--epilogue", choices=("relu", "bias_gelu"), default="relu")
+    ap.add_argument("--layout", choices=("nn", "nt", "tn", "tt"), default="nn",
+                    help="A stored K x M (t first) and/or B stored N x K (t second)")
     ap.add_argument("--table", default=None, help="JSON table to add the winners to")
     ap.add_argument("--graph", type=int, default=20)
     ap.add_argument("--replays", type=int, default=5)
@@ -253,7 +262,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
     everything = []
     for M, N, K in args.shapes:
-        r = tune(M, N, K, epilogue=args.epilogue, graph=args.graph, replays=args.replays)
+        r = tune(M, N, K, epilogue=args.epilogue, graph=args.graph, replays=args.replays,
+                 trans_a=args.layout[0] == "t", trans_b=args.layout[1] == "t")
         print(format_result(r, args.top), flush=True)
         everything.append(r)
         if args.table and r["best"] is not None:
