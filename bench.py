@@ -485,6 +485,14 @@ def main(argv=None) -> int:
                            args.layout)
             print(json.dumps(result_line(ow, orr, max(args.steps // 4, 50), max(args.warmup // 4, 10))),
                   file=sys.stderr, flush=True)
+        # the pages' own tile (128 x 128 x 64) on 1024^3, for comparison
+        pages_tile = next(t for t in range(gr.tile_count()) if gr.tile_name(t).startswith("128x128x64"))
+        pw = workloads.SQUARE_1024
+        prr = time_gpu(pw, max(args.steps // 4, 50), max(args.warmup // 4, 10), pages_tile, args.graph,
+                       args.epilogue, args.layout)
+        pl = result_line(pw, prr, max(args.steps // 4, 50), max(args.warmup // 4, 10))
+        pl["note"] = "the pages' 128x128x64 tile pinned, for comparison with the library's choice"
+        print(json.dumps(pl), file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline and args.epilogue == "relu" and args.layout == "nn":
         cpu = cpu_baseline(w, r, args.cpu_seconds)
