@@ -191,3 +191,21 @@ def test_attention_scale_sign_and_zero(scale):
                                                scale, causal, want_lse=True, want_pv=True)
         check_attn(got, want, pv, lse, lse_o, score_bound(q, k, scale), f"scale {scale} causal {causal}")
 
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_attention_wide_score_range(D):
+    # scores with a standard deviation near 9 (natural units): row maxima jump
+    # by more than the lazy-rescaling threshold many times along a row, and
+    # most rows are nearly one-hot
+    B, H, S = 1, 4, 777
+    q = randn_f16((B, H, S, D), 61, scale=3.0)
+    k = randn_f16((B, H, S, D), 62, scale=3.0)
+    v = randn_f16((B, H, S, D), 63)
+    scale = 1.0 / math.sqrt(D)
+    for causal in (False, True):
+        say(f"[attn] wide range D={D} causal={causal}")
+        got, lse = run_attn(q, k, v, causal, scale)
+        want, lse_o, pv = oracle.attention_f16(workloads.as_u16(q), workloads.as_u16(k), workloads.as_u16(v),
+                                               scale, causal, want_lse=True, want_pv=True)
+        check_attn(got, want, pv, lse, lse_o, score_bound(q, k, scale), f"wide D{D} c{causal}")
+
