@@ -270,28 +270,33 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two 
     const uint16_t* Kh = p.K + (int64_t)bh * Skv * D;
     const uint16_t* Vh = p.V + (int64_t)bh * Skv * D;
 
-    // ---- Q fragments, kept in registers: row qrow, columns 16 kk + 8 hi .. +7
+    // ---- Q fragments, kept in registers: row qrow, columns 16 kk + 8 hi .. +7.
+    // A negative scale is moved onto Q: the sign bits are flipped, which
+    // negates every score exactly, and the exponents use |scale|. So the
+    // row reference is always a maximum.
+    const float c = fabsf(p.scale_log2);
     f16x8 qf[T::KK];
     {
         const __amdgpu_buffer_rsrc_t rq =
             make_rsrc(p.Q + (int64_t)bh * Sq * D, (uint64_t)Sq * D * 2);
+        const uint32_t flip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 #pragma unroll
         for (int kk = 0; kk < T::KK; ++kk) {
             const uint32_t off = qrow < Sq ? (uint32_t)(qrow * D + 16 * kk + 8 * hi) * 2u : kOOB;
-            qf[kk] = __builtin_bit_cast(f16x8, load16(rq, off));
+            qf[kk] = __builtin_bit_cast(f16x8, load16(rq, off) ^ flip);
         }
     }
 
     // ---- direct loads of key / value tile j into stage S
-    // load i of a tile: rows i*RPL + lane / CPR, physical chunk lane % CPR
+    // load i of a tile: rows i*RPL + lane / CPR, physical chunk lane % CPR.
+    // The descriptor of tile j ends at the last key: a row past it lies
+    // wholly beyond the descriptor's range and reads as zeros.
     uint32_t koff[T::LW], voff[T::LW];
-    int lrow[T::LW];
 #pragma unroll
     for (int i = 0; i < T::LW; ++i) {
         const int gi = wave * T::LW + i;
         const int r = gi * T::RPL + lane / T::CPR;
         const int pc = lane % T::CPR;
-        lrow[i] = r;
         koff[i] = (uint32_t)(r * D + 8 * (pc ^ k_swz<D>(r))) * 2u;
         voff[i] = (uint32_t)(r * D + 8 * (pc ^ v_swz<D>(r))) * 2u;
     }
@@ -305,9 +310,7 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two 
 #pragma unroll
         for (int i = 0; i < T::LW; ++i) {
             const int gi = wave * T::LW + i;
-            const bool in = kv0 + lrow[i] < Skv;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (GR_LDS void*)(kd + gi * 512), 16,
-                                                     (int)(in ? koff[i] : kOOB), 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (GR_LDS void*)(kd + gi * 512), 16, (int)koff[i], 0, 0, 0);
         }
     };
     auto issue_v = [&]<int S>(int j) {
@@ -319,9 +322,7 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two 
 #pragma unroll
         for (int i = 0; i < T::LW; ++i) {
             const int gi = wave * T::LW + i;
-            const bool in = kv0 + lrow[i] < Skv;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (GR_LDS void*)(vd + gi * 512), 16,
-                                                     (int)(in ? voff[i] : kOOB), 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (GR_LDS void*)(vd + gi * 512), 16, (int)voff[i], 0, 0, 0);
         }
     };
 
@@ -376,37 +377,45 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two 
         }
     };
 
-    // The row statistics of tile j's scores s: keys past the end, or after
-    // the row when causal, are masked (only tiles at the sequence end or the
-    // diagonal need the test; lane holds keys kv0 + 32 jb + 8 (e / 4) + 4 hi +
-    // e % 4), the tile's row maximum is taken -- max(s c) = c max(s) for
-    // c > 0, c min(s) for c < 0 -- and the row's reference m_run moves when
-    // needed. Masked scores become the infinity that c turns into -inf.
-    // Returns the reference the exponents use.
-    auto stats = [&](int j, f32x16 (&s)[2]) -> float {
+    // Both halves of the wave hold the same 32 rows (lanes l and l + 32):
+    // the maximum of a value over the two.
+    auto pair_max = [](float v) -> float {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    };
+    // This lane's maximum over the 32 scores of s it holds; two chains of
+    // three-way maxima.
+    auto lane_max = [](const f32x16 (&s)[2]) -> float {
+        float a = -INFINITY, b = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            a = fmaxf(a, fmaxf(s[0][2 * q], s[0][2 * q + 1]));
+            b = fmaxf(b, fmaxf(s[1][2 * q], s[1][2 * q + 1]));
+        }
+        return fmaxf(a, b);
+    };
+
+    // The row statistics of tile j's scores s, whose lane maximum hs the
+    // caller took as the scores came out of the matrix ops: keys past the
+    // end, or after the row when causal, are masked (only tiles at the
+    // sequence end or the diagonal need the test, and there the maximum is
+    // taken again; the lane holds keys kv0 + 32 jb + 8 (e / 4) + 4 hi + e % 4),
+    // and the row's reference m_run moves when needed. Returns the reference
+    // the exponents use.
+    auto stats = [&](int j, f32x16 (&s)[2], float hs) -> float {
         const int kv0 = j * T::BN;
-        const float c = p.scale_log2;
         const bool edge = kv0 + T::BN > Skv || (p.causal && kv0 + T::BN - 1 > qw);
         if (edge) {
             const int lim = p.causal ? min(Skv, qrow + 1) : Skv;
             const int rel = lim - kv0 - 4 * hi;  // key offsets below rel are visible
-            const float dead = c > 0.f ? -INFINITY : INFINITY;
 #pragma unroll
             for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    s[jb][e] = (32 * jb + 8 * (e / 4) + e % 4 < rel) ? s[jb][e] : dead;
+                    s[jb][e] = (32 * jb + 8 * (e / 4) + e % 4 < rel) ? s[jb][e] : -INFINITY;
+            hs = lane_max(s);
         }
-        float hi_s = -INFINITY, lo_s = INFINITY;
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                hi_s = fmaxf(hi_s, s[jb][e]);
-                lo_s = fminf(lo_s, s[jb][e]);
-            }
-        float mt = c > 0.f ? hi_s * c : lo_s * c;
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mt = pair_max(hs * c);
         // Lazy rescaling: p = 2^(t - m_run) with m_run, the reference of the
         // row, moved only when a score exceeds it by more than 2^kTau (then
         // O and l are rescaled). Every p stays <= 2^kTau, so fp16 holds it
@@ -427,24 +436,29 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two 
     };
 
     // One straight-line stretch per tile, matrix ops and VALU work
-    // interleaved in a fixed order (scheduling barriers):
-    //   phase 1: S' = Q K(next)^T from K stage SK, each fragment read two
-    //            matrix ops ahead, with the exponentials of the current
-    //            tile's first 24 scores (chunks 0-2 of P) between them;
-    //   phase 2: O += P V from V stage SV, chunk by chunk, fragments read
-    //            one matrix op ahead, with the last 8 exponentials (chunk 3)
-    //            between the matrix ops of chunks 0 and 1.
-    // p = 2^(s c - m): the scale folded into one FMA per score.
-    auto fused = [&]<int SK, int SV>(f32x16 (&s_cur)[2], f32x16 (&s_next)[2], float m_use) {
+    // interleaved in a fixed order (scheduling barriers); every fragment read
+    // is issued two matrix ops ahead, in a stretch of its own so that it
+    // leaves before the matrix op it overlaps:
+    //   phase 1: S' = Q K(next)^T from K stage SK, with the exponentials of
+    //            the current tile's first 24 scores (chunks 0-2 of P) between
+    //            the matrix ops;
+    //   phase 2: O += P V from V stage SV, chunk by chunk, with the last 8
+    //            exponentials (chunk 3) and the lane maximum of S' between
+    //            the matrix ops.
+    // p = 2^(s c - m): the scale folded into one FMA per score. The row sums
+    // are pinned to their stretch (an empty asm statement that takes them),
+    // since nothing else ties them there. Returns the lane maximum of S'.
+    auto fused = [&]<int SK, int SV>(f32x16 (&s_cur)[2], f32x16 (&s_next)[2], float m_use) -> float {
         const char* kb = reinterpret_cast<const char*>(SK == 0 ? ks0 : ks1);
         const char* vb = reinterpret_cast<const char*>(SV == 0 ? vs0 : vs1);
-        const float c = p.scale_log2;
         constexpr int NQ = 2 * T::KK;       // Q K^T matrix ops
         constexpr int NP = 4 * T::DB;       // P V matrix ops
         constexpr int EX1 = 24;             // exponentials in phase 1
-        float ls = 0.f;
+        constexpr int NEX2 = 32 - EX1;      // over the first 2 DB matrix ops of phase 2
+        constexpr int NMX = 16;             // three-way maxima over S'
+        float ls1 = 0.f, ls2 = 0.f;
         f16x8 pf[4];
-        auto expo = [&](int x) {  // score x of the lane: block x / 16, element x % 16 -> chunk x / 8
+        auto expo = [&](int x, float& ls) {  // score x: block x / 16, element x % 16 -> chunk x / 8
             const float pe = exp2_fast(fmaf(s_cur[x / 16][x % 16], c, -m_use));
             ls += pe;
             pf[x / 8][x % 8] = (_Float16)pe;
@@ -471,25 +485,40 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two 
 #pragma unroll
         for (int t = 0; t < NQ; ++t) {
             if (t + 2 < NQ) kr[t + 2] = read_k(t + 2);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int x = t * EX1 / NQ; x < (t + 1) * EX1 / NQ; ++x) expo(x);
+            for (int x = t * EX1 / NQ; x < (t + 1) * EX1 / NQ; ++x) expo(x, ls1);
             s_next[t % 2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kr[t], qf[t / 2], s_next[t % 2], 0, 0, 0);
+            asm volatile("" : "+v"(ls1));
             __builtin_amdgcn_sched_barrier(0);
         }
         f16x8 vr[NP];
         vr[0] = read_v(0);
+        vr[1] = read_v(1);
         __builtin_amdgcn_sched_barrier(0);
+        float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
         for (int u = 0; u < NP; ++u) {
-            if (u + 1 < NP) vr[u + 1] = read_v(u + 1);
-            constexpr int NEX2 = 32 - EX1;   // spread over the chunk-0 and chunk-1 matrix ops
+            if (u + 2 < NP) vr[u + 2] = read_v(u + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            if (u < 2 * T::DB) {
 #pragma unroll
-            for (int x = EX1 + u * NEX2 / (2 * T::DB); x < EX1 + (u + 1) * NEX2 / (2 * T::DB) && x < 32; ++x)
-                if (u < 2 * T::DB) expo(x);
+                for (int x = EX1 + u * NEX2 / (2 * T::DB); x < EX1 + (u + 1) * NEX2 / (2 * T::DB); ++x) expo(x, ls2);
+            }
+            // S' is complete (phase 1 is over): its lane maximum, pairs of
+            // scores q = 2 i, 2 i + 1 of block i / 8, alternating chains
+#pragma unroll
+            for (int i = u * NMX / NP; i < (u + 1) * NMX / NP; ++i) {
+                float& mx = (i % 2) ? mx1 : mx0;
+                const int jb = i / 8, q = i % 8;
+                mx = fmaxf(mx, fmaxf(s_next[jb][2 * q], s_next[jb][2 * q + 1]));
+            }
             acc_o[u % T::DB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vr[u], pf[u / T::DB], acc_o[u % T::DB], 0, 0, 0);
+            asm volatile("" : "+v"(ls2), "+v"(mx0), "+v"(mx1));
             __builtin_amdgcn_sched_barrier(0);
         }
-        l_run += ls;
+        l_run += ls1 + ls2;
+        return fmaxf(mx0, mx1);
     };
 
     // Software pipeline over key tiles, one barrier per tile. Iteration j:
@@ -510,15 +539,16 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two 
     issue_k.template operator()<1>(1);
     sync();
     qk.template operator()<0>(sa);
+    float hs = lane_max(sa);
     for (int j = 0; j < nkb2; j += 2) {
         sync();
         issue_k.template operator()<0>(j + 2);
         issue_v.template operator()<1>(j + 1);
-        fused.template operator()<1, 0>(sa, sb, stats(j, sa));
+        hs = fused.template operator()<1, 0>(sa, sb, stats(j, sa, hs));
         sync();
         issue_k.template operator()<1>(j + 3);
         issue_v.template operator()<0>(j + 2);
-        fused.template operator()<0, 1>(sb, sa, stats(j + 1, sb));
+        hs = fused.template operator()<0, 1>(sb, sa, stats(j + 1, sb, hs));
     }
     wait_vmcnt<0>();  // the last (empty) loads must land before the kernel ends
 
