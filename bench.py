@@ -96,15 +96,18 @@ def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0, epilog
              layout: str = "nn"):
     """Times `steps` back-to-back launches on one stream, bracketed by two
     events on that stream. Successive launches cycle through R copies of
-    (A, B) with R * (|A| + |B|) >= 768 MiB (at most 8), so the inputs of a
-    launch are not left in the last-level cache by the previous ones: every
-    launch reads its inputs from HBM.
+    (A, B) with R * (|A| + |B|) >= 768 MiB (at most 4096 copies: the 256^3
+    shape falls short), so the inputs of a launch are not left in the
+    last-level cache by the previous ones: every launch reads its inputs
+    from HBM.
 
-    With graph_batch = G > 0 the launches are captured G at a time into a HIP
-    graph (after the warm-up, so any workspace already exists and nothing is
-    allocated or cleared inside the graph) and the timed region replays it
-    steps / G times: the device throughput without the host's per-call
-    launch cost, which otherwise dominates for kernels of a few microseconds.
+    With graph_batch = G > 0 the launches are captured G at a time into HIP
+    graphs (after the warm-up, so any workspace already exists and nothing is
+    allocated or cleared inside a graph): R / G graphs when R > G, which
+    together cycle once through the copies. The timed region replays them in
+    turn, steps / G replays: the device throughput without the host's
+    per-call launch cost, which otherwise dominates for kernels of a few
+    microseconds.
 
     Also times 200 single launches, each between its own pair of events, for
     the duration of one launch.
@@ -114,13 +117,14 @@ def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0, epilog
     entry points; the product is the same."""
     import torch
     import tiled_dense_gemm_f16_amd as gr
+    from tiled_dense_gemm_f16_amd import tune
 
     a, b = workloads.workload_inputs(w)
     ta, tb = layout[0] == "t", layout[1] == "t"
     a_st = a.t().contiguous() if ta else a
     b_st = b.t().contiguous() if tb else b
     in_bytes = 2 * (w.M * w.K + w.K * w.N)
-    rot = max(1, min(8, -(-ROTATE_BYTES // max(in_bytes, 1))))
+    rot = tune.rotation(in_bytes, graph_batch, ROTATE_BYTES)
     ads = [a_st.cuda() for _ in range(rot)]
     bds = [b_st.cuda() for _ in range(rot)]
     c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
@@ -145,22 +149,20 @@ def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0, epilog
             if st != gr.OK:
                 raise RuntimeError(gr.strerror(st))
         torch.cuda.synchronize()
-        graph = None
+        graphs = []
         if graph_batch > 0:
             steps = max(graph_batch, steps // graph_batch * graph_batch)
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=stream):
-                for i in range(graph_batch):
-                    call(*args[i % rot])
-            graph.replay()
+            graphs = tune.capture_rotation(lambda i: call(*args[i]), rot, graph_batch, stream)
+            for g in graphs:  # every copy once before the timed region
+                g.replay()
             torch.cuda.synchronize()
         # the whole timed region between two events on the launch stream
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(stream)
-        if graph is not None:
-            for _ in range(steps // graph_batch):
-                graph.replay()
+        if graphs:
+            for r in range(steps // graph_batch):
+                graphs[r % len(graphs)].replay()
         else:
             for i in range(steps):
                 call(*args[i % rot])

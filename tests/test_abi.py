@@ -9,6 +9,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -142,6 +143,44 @@ def test_tuner_candidates():
     # a tighter LDS budget prunes the big tiles
     small = tune.candidates(1024, 1024, 1024, lds_limit=64 * 1024)
     assert small and all(gr.tile_info(x["tile"])["lds_bytes"] <= 64 * 1024 for x in small)
+
+
+def test_timing_rotation_covers_the_last_level_cache():
+    from tiled_dense_gemm_f16_amd import tune
+
+    MiB = 1 << 20
+    # 4096^3: 64 MiB of inputs, 12 copies fit in one graph of 20
+    assert tune.rotation(64 * MiB, 20) == 12
+    # 1024^3: 4 MiB; 192 copies, rounded up to 10 graphs of 20
+    assert tune.rotation(4 * MiB, 20) == 200
+    assert tune.rotation(4 * MiB, 0) == 192
+    # every copy count covers 768 MiB, up to the cap (then whole graphs past it)
+    for in_bytes in (1, 3 * MiB + 5, 100 * MiB, 800 * MiB):
+        for batch in (0, 10, 20):
+            n = tune.rotation(in_bytes, batch)
+            assert n >= tune.MAX_COPIES or n * in_bytes >= tune.DEFAULT_ROTATE_BYTES
+            assert batch == 0 or n <= batch or n % batch == 0
+
+    # the graphs cycle once through every copy, in order
+    class FakeGraph:
+        log = []
+
+        def __enter__(self):
+            FakeGraph.log.append([])
+
+        def __exit__(self, *a):
+            return False
+
+    import types
+    fake_torch = types.SimpleNamespace(cuda=types.SimpleNamespace(CUDAGraph=object, graph=lambda g, stream: FakeGraph()))
+    saved = sys.modules.get("torch")
+    sys.modules["torch"] = fake_torch
+    try:
+        gs = tune.capture_rotation(lambda i: FakeGraph.log[-1].append(i), 60, 20, None)
+    finally:
+        if saved is not None:
+            sys.modules["torch"] = saved
+    assert len(gs) == 3 and FakeGraph.log == [list(range(0, 20)), list(range(20, 40)), list(range(40, 60))]
 
 
 def test_tuner_table_roundtrip(tmp_path):

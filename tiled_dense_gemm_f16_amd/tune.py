@@ -16,9 +16,10 @@ compiled; it is checked again here against the device's LDS per workgroup.
 Each candidate's output is validated against a float64 product that torch
 computes on the same device, with the contract's bound |c - ref| <= 1e-2 +
 1e-2 |ref| (torch is only the checker here; the candidate's result is the
-library's). It is timed as replays of a HIP graph of `graph` launches that
-cycle through copies of the inputs (at least `rotate_bytes` in all), so
-inputs come from HBM rather than the last-level cache. The winners go into a
+library's). It is timed as replays of HIP graphs of `graph` launches that
+together cycle through copies of the inputs (at least `rotate_bytes` in all,
+at most MAX_COPIES copies), so inputs come from HBM rather than the
+last-level cache. The winners go into a
 JSON table keyed by device architecture, epilogue and shape; `lookup` returns
 the keyword arguments that pin the winner in gemm_relu / gemm_bias_gelu.
 
@@ -37,6 +38,35 @@ from . import _binding as gr
 LDS_PER_WORKGROUP = 160 * 1024  # gfx950
 GROUP_SIZES = (1, 2, 4, 8, 16)
 DEFAULT_ROTATE_BYTES = 768 << 20  # three times the 256 MB last-level cache
+MAX_COPIES = 4096
+
+
+def rotation(in_bytes: int, batch: int, rotate_bytes: int = DEFAULT_ROTATE_BYTES) -> int:
+    """Number of input copies a timing loop cycles through so that a launch's
+    inputs were last touched at least `rotate_bytes` of other inputs ago (at
+    most MAX_COPIES). With graphs of `batch` launches and more copies than
+    that, the count is rounded up to a whole number of graphs."""
+    n = max(1, min(MAX_COPIES, -(-rotate_bytes // max(in_bytes, 1))))
+    if batch > 0 and n > batch:
+        n = -(-n // batch) * batch
+    return n
+
+
+def capture_rotation(call, copies: int, batch: int, stream) -> list:
+    """HIP graphs of `batch` launches of call(copy) that, replayed in turn,
+    cycle once through all `copies`: graph j runs copies j * batch ..
+    j * batch + batch - 1 (modulo copies). One graph when copies <= batch.
+    Nothing is allocated inside the graphs."""
+    import torch
+
+    graphs = []
+    for j in range(copies // batch if copies > batch else 1):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(batch):
+                call((j * batch + i) % copies)
+        graphs.append(g)
+    return graphs
 
 
 def _tiles(M: int, N: int, bm: int, bn: int) -> tuple[int, int]:
@@ -107,7 +137,7 @@ def tune(M: int, N: int, K: int, *, epilogue: str = "relu", seed: int = 0, graph
         raise ValueError("M and N must be positive")
     dev = torch.device("cuda", device)
     in_bytes = 2 * (M * K + K * N)
-    copies = max(1, min(8, -(-rotate_bytes // max(in_bytes, 1))))
+    copies = rotation(in_bytes, graph, rotate_bytes)
     cands = only if only is not None else candidates(M, N, K)
     with torch.cuda.device(dev):
         a_s, b_s, bias = _inputs(M, N, K, epilogue, seed, dev, copies, trans_a, trans_b)
@@ -146,21 +176,19 @@ def tune(M: int, N: int, K: int, *, epilogue: str = "relu", seed: int = 0, graph
                 for i in range(3):
                     call(i % copies)
                 stream.synchronize()
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    for i in range(graph):
-                        call(i % copies)
-                g.replay()
+                gs = capture_rotation(call, copies, graph, stream)
+                for g in gs:  # every copy once before timing
+                    g.replay()
                 times = []
-                for _ in range(replays):
+                for r in range(max(replays, len(gs))):
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
                     e0.record(stream)
-                    g.replay()
+                    gs[r % len(gs)].replay()
                     e1.record(stream)
                     e1.synchronize()
                     times.append(e0.elapsed_time(e1) * 1e3 / graph)
-                del g
+                del gs
             times.sort()
             res.update(ok=True, us=times[len(times) // 2], us_min=times[0])
             results.append(res)
