@@ -95,10 +95,16 @@ struct Cfg {
 };
 
 // A: row r of a stage holds 32 halves = four 16-byte chunks; logical chunk c
-// sits at physical chunk c ^ a_swz(r). Sixteen consecutive rows read at one
-// logical chunk then cover 16 distinct 16-byte slots of a 256-byte span,
-// and any 8 consecutive rows 8 distinct slots of a 128-byte span.
-__device__ __forceinline__ int a_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// sits at physical chunk c ^ a_swz(r), with a_swz(r) = (r / 4) % 4. Four
+// consecutive rows fill one 256-byte bank window, and each of the next three
+// groups of four takes another rotation of the chunks, so sixteen consecutive
+// rows read at one logical chunk touch every bank once. Measured with the
+// LDS bank-conflict counter on the fragment read below (32 rows, two logical
+// chunks per lane pair): zero conflicts; an XOR with row bits 1 and 3, which
+// spreads 16 rows just as well on paper, left a third of the read's LDS
+// cycles as conflicts, as did bits 1-2, so gfx950 does not serve a 16-byte
+// read in groups of 16 consecutive lanes.
+__device__ __forceinline__ int a_swz(int r) { return (r >> 2) & 3; }
 
 // B: row kr of a stage holds BN halves; logical chunk c sits at physical chunk
 // c ^ b_swz(kr). A transposing read touches four consecutive rows (kr % 4 =
