@@ -59,7 +59,7 @@ template <int D>
 void launch_attn(const AttnArgs& a, hipStream_t s)
 {
     using T = AttnCfg<D, GR_ATTN_NW>;
-    hipLaunchKernelGGL((gemm_relu::attn::attn_fwd_kernel<T>), dim3(a.BH * a.nqb), dim3(T::NT), 0, s, a);
+    hipLaunchKernelGGL((gemm_relu::attn::attn_fwd_kernel<T>), dim3(a.BH * a.npair), dim3(T::NT), 0, s, a);
 }
 
 }  // namespace
@@ -135,6 +135,7 @@ int flash_attn_fwd_f16(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
     if (a.scale_log2 == 0.0f) a.scale_log2 = 1e-30f;
     a.causal = causal;
     a.nqb = (int)nqb;
+    a.npair = (int)((nqb + 1) / 2);
     if (D == 64) launch_attn<64>(a, s);
     else launch_attn<128>(a, s);
     return hipGetLastError() == hipSuccess ? GEMM_RELU_OK : GEMM_RELU_EHIP;

@@ -190,7 +190,8 @@ struct AttnArgs {
     int BH, Sq, Skv;
     float scale_log2;  // softmax scale * log2(e)
     int causal;
-    int nqb;  // query tiles per (batch, head)
+    int nqb;    // query tiles per (batch, head)
+    int npair;  // work items per (batch, head): (nqb + 1) / 2
 };
 
 template <int D_, int NW_ = 8>
@@ -230,27 +231,13 @@ __device__ __forceinline__ int v_swz(int r)
     else return 4 * ((r >> 1) & 1);
 }
 
+// One query tile (BM rows) of batch-head bh against all its keys, in the
+// workgroup's four LDS stages.
 template <class T>
-__global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two waves per SIMD
+__device__ __forceinline__ void attn_tile(const AttnArgs& p, int bh, int qb, uint16_t* ks0, uint16_t* ks1,
+                                          uint16_t* vs0, uint16_t* vs1)
 {
-    __shared__ __attribute__((aligned(1024))) uint16_t ks0[T::TILE_HALVES];
-    __shared__ __attribute__((aligned(1024))) uint16_t ks1[T::TILE_HALVES];
-    __shared__ __attribute__((aligned(1024))) uint16_t vs0[T::TILE_HALVES];
-    __shared__ __attribute__((aligned(1024))) uint16_t vs1[T::TILE_HALVES];
     constexpr int D = T::D;
-
-    // workgroup -> (batch-head, query tile): XCD-contiguous ranges (die b % 8
-    // gets one run of work items), a head's tiles next to each other so they
-    // share its K and V in the die's L2, and within a head the tiles that see
-    // the most keys first
-    int w = blockIdx.x;
-    {
-        const int nblk = gridDim.x, q = nblk / 8, r = nblk % 8;
-        const int xcd = w % 8, idx = w / 8;
-        w = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-    }
-    const int bh = w / p.nqb;
-    const int qb = p.nqb - 1 - (w % p.nqb);
     const int Sq = p.Sq, Skv = p.Skv;
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -569,6 +556,39 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two 
             }
         if (p.lse && hi == 0)
             p.lse[(int64_t)bh * Sq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+}
+
+template <class T>
+__global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two waves per SIMD
+{
+    __shared__ __attribute__((aligned(1024))) uint16_t ks0[T::TILE_HALVES];
+    __shared__ __attribute__((aligned(1024))) uint16_t ks1[T::TILE_HALVES];
+    __shared__ __attribute__((aligned(1024))) uint16_t vs0[T::TILE_HALVES];
+    __shared__ __attribute__((aligned(1024))) uint16_t vs1[T::TILE_HALVES];
+
+    // Work item -> (batch-head, pair of query tiles). Items are taken in
+    // XCD-contiguous ranges (die b % 8 gets one run of them), and a head's
+    // items sit next to each other so they share its K and V in the die's L2.
+    // Item i of a head runs query tile nqb-1-i and then tile i: under the
+    // causal mask the two together see the same number of key tiles for
+    // every i, so all workgroups carry equal work (the middle tile of an odd
+    // count runs alone).
+    int w = blockIdx.x;
+    {
+        const int nblk = gridDim.x, q = nblk / 8, r = nblk % 8;
+        const int xcd = w % 8, idx = w / 8;
+        w = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+    }
+    const int bh = w / p.npair, i = w % p.npair;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+        const int qb = pass == 0 ? p.nqb - 1 - i : i;
+        if (pass == 1) {
+            if (qb == p.nqb - 1 - i) break;
+            __syncthreads();  // every wave is done with the stages before they refill
+        }
+        attn_tile<T>(p, bh, qb, ks0, ks1, vs0, vs1);
     }
 }
 
