@@ -54,13 +54,14 @@ def rotation(in_bytes: int, batch: int, rotate_bytes: int = DEFAULT_ROTATE_BYTES
 
 def capture_rotation(call, copies: int, batch: int, stream) -> list:
     """HIP graphs of `batch` launches of call(copy) that, replayed in turn,
-    cycle once through all `copies`: graph j runs copies j * batch ..
-    j * batch + batch - 1 (modulo copies). One graph when copies <= batch.
-    Nothing is allocated inside the graphs."""
+    cycle through all `copies`: graph j runs copies j * batch .. j * batch +
+    batch - 1 (modulo copies), ceil(copies / batch) graphs (one when copies
+    <= batch; exactly once through when copies is a multiple of batch, as
+    rotation() makes it). Nothing is allocated inside the graphs."""
     import torch
 
     graphs = []
-    for j in range(copies // batch if copies > batch else 1):
+    for j in range(-(-copies // batch) if copies > batch else 1):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for i in range(batch):
