@@ -404,10 +404,10 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& p, int bh, int qb, uin
         }
         const float mt = pair_max(hs * c);
         // Lazy rescaling: p = 2^(t - m_run) with m_run, the reference of the
-        // row, moved only when a score exceeds it by more than 2^kTau (then
-        // O and l are rescaled). Every p stays <= 2^kTau, so fp16 holds it
-        // with the same relative precision, and O / l is unchanged in exact
-        // arithmetic. A row with nothing visible yet keeps m_run = -inf.
+        // row, moved only when a scaled score t exceeds it by more than kTau
+        // (then O and l are rescaled). Every p stays <= 2^kTau, so fp16 holds
+        // it with the same relative precision, and O / l is unchanged in
+        // exact arithmetic. A row with nothing visible yet keeps m_run = -inf.
         constexpr float kTau = 8.0f;
         if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
             const float m_new = fmaxf(m_run, mt);
