@@ -40,13 +40,18 @@ import workloads  # noqa: E402
 PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "TFLOP/s and % of MI355X dense FP16 MFMA peak, fp16 GEMM+ReLU 4096³"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_relu.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 CSRC = os.path.join(ROOT, "tiled_dense_gemm_f16_amd", "csrc")
 
 
 def kernel_sources(tile: str) -> list[str]:
-    """Device sources of the kernel family that runs a tile."""
-    family = "pipelined.hpp" if "lds-dma" in tile else "splitk.hpp" if "splitk" in tile else "staged.hpp"
+    """Device sources of the kernel family that runs a tile (or, for the
+    second workload, the attention and softmax kernels: "attn_fwd_d128",
+    "softmax_rows")."""
+    if tile.startswith(("attn", "softmax")):
+        family = "attention.hpp"
+    else:
+        family = "pipelined.hpp" if "lds-dma" in tile else "splitk.hpp" if "splitk" in tile else "staged.hpp"
     return [os.path.join(CSRC, "common.hpp"), os.path.join(CSRC, family)]
 
 
@@ -344,10 +349,11 @@ def bench_attention(args) -> dict:
                        "causal": bool(args.causal), "dist": "normal", "input_copies_rotated": rot,
                        "parallelism": "single GPU"},
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None},
+                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                         "traffic": measured_traffic(name, f"attn_fwd_d{D}")},
             "kernel_ms_timed_region_mean": round(r["ms_per_step"], 5), "graph_batch": r["graph_batch"],
             "single_launch_event_ms": {"mean": round(r["launch_ms_mean"], 5), "min": round(r["launch_ms_min"], 5)},
-            "flops_per_launch": flops}
+            "flops_per_launch": flops, "kernel_source_sha256": source_hash(f"attn_fwd_d{D}")}
     if not args.no_cpu_baseline:
         import oracle
         Q = workloads.as_u16(qs[0].cpu())
@@ -398,7 +404,7 @@ def bench_softmax(args) -> dict:
             "config": {"workload": name, "rows": R, "cols": C, "dist": "normal", "input_copies_rotated": rot,
                        "parallelism": "single GPU"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(name, "softmax_rows")},
             "kernel_ms_timed_region_mean": round(r["ms_per_step"], 5), "graph_batch": r["graph_batch"],
             "single_launch_event_ms": {"mean": round(r["launch_ms_mean"], 5), "min": round(r["launch_ms_min"], 5)},
             "bytes_per_launch": moved}
