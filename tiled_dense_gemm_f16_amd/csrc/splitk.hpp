@@ -7,8 +7,9 @@
 // The design keeps as many bytes of B in flight as the chip allows and
 // touches nothing twice:
 //
-//  * A workgroup owns 16 * MB rows and TN = 128 columns of C and one range of
-//    K; each of its
+//  * A workgroup owns 16 * MB rows and TN = 128 columns of C (two halves of
+//    64 from neighbouring tiles' strips when B is K x N and N % 256 == 0)
+//    and one range of K; each of its
 //    four waves takes a quarter of that range (the reduction is split three
 //    ways: inside an MFMA, across the waves, across workgroups). Splitting K
 //    across CUs when the other dimensions are too small to fill the chip is
@@ -76,6 +77,14 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
     const int tile = blockIdx.x % ntiles, ks = blockIdx.x / ntiles;
     const int tm = tile / p.tiles_n, tn = tile % p.tiles_n;
     const int m0 = tm * T::BM, n0 = tn * T::TN;
+    // Logical column lc (0..127) of the tile -> column of C. With B stored
+    // K x N and whole pairs of tiles (N % 256 == 0), the first 64 columns
+    // come from this tile's 256-byte strip of each row of B and the last 64
+    // from the neighbouring tile's: a workgroup's rate depends on where its
+    // strip sits in a row (the memory channels behind it), and mixing two
+    // strips evens the workgroups out. Otherwise the columns are n0 + lc.
+    const bool halves = !TB && N % (2 * T::TN) == 0;
+    auto gcol = [&](int lc) -> int { return (halves && lc >= T::TN / 2) ? (tn ^ 1) * T::TN + lc : n0 + lc; };
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int kw = p.kc / T::NW;
@@ -85,7 +94,7 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
 
     const int g = lane / 16, i16 = lane % 16;
     // B: lane reads rows 8g + r (r = 0..7) of a step, columns ncol .. ncol+7
-    const int ncol = n0 + 8 * i16;
+    const int ncol = gcol(8 * i16);
     // (B given as N x K: rows k .. k+7 of column ncol + r, relative to
     // B + n0*K + k0)
     uint32_t boff[8];
@@ -189,7 +198,7 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
     }
 
     // ---- reduction across the four waves (fixed order) ----
-    // Lane holds acc[mb][e][r] = C[mb*16 + i16][n0 + 32g + 8r + e].
+    // Lane holds acc[mb][e][r] = C[mb*16 + i16][gcol(32g + 8r + e)].
 #pragma unroll
     for (int mb = 0; mb < T::MB; ++mb) {
         float* row = &red[wave][mb * 16 + i16][32 * g];
@@ -202,12 +211,12 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
     }
     __syncthreads();
     // Combine: thread t adds the waves' values for rows m0 + t/16 + j*RP
-    // (j = 0, 1, ...), columns n0 + 8*(t%16) .. +7 of the tile.
+    // (j = 0, 1, ...), logical columns 8*(t%16) .. +7 of the tile.
     constexpr int RP = T::ROWS_PER_PASS;
     constexpr int NJ = (T::BM + RP - 1) / RP;
     const int t = threadIdx.x;
     const int cm = t / 16, cn = 8 * (t % 16);
-    const int n = n0 + cn;
+    const int n = gcol(cn);
     float v[NJ][8];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
