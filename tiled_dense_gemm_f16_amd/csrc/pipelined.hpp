@@ -86,7 +86,7 @@ struct Cfg {
     static_assert(A_LOADS % NW == 0 && B_LOADS % NW == 0, "loads must split evenly over waves");
     static_assert(TM % 32 == 0 && TN % 128 == 0, "wave sub-tile: 32-row blocks, 128-column units");
     static_assert(2 * LPT < 64, "vmcnt range");
-    static_assert(STAGES >= 3 && STAGES <= 5, "ring of 3 to 5 slots");
+    static_assert(STAGES >= 3 && STAGES <= 8, "ring of 3 to 8 slots (one LDS array each)");
     static_assert((STAGES - 2) * LPT < 64, "vmcnt range");
     static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
     static_assert(C_ROWS_FIT >= 32 && BM <= STAGES * C_ROWS_PER_STAGE, "the C tile must fit in the ring");
@@ -164,16 +164,28 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     // One LDS array per stage (A tile, then B tile): the compiler tracks
     // direct-to-LDS writes per array, so distinct arrays keep the reads of
     // one stage from waiting on the loads into another.
-    __shared__ __attribute__((aligned(1024))) uint16_t st0[T::A_HALVES + T::B_HALVES];
-    __shared__ __attribute__((aligned(1024))) uint16_t st1[T::A_HALVES + T::B_HALVES];
-    __shared__ __attribute__((aligned(1024))) uint16_t st2[T::A_HALVES + T::B_HALVES];
-    // the last array holds slot 3 and, in a five-slot ring, slot 4
-    __shared__ __attribute__((aligned(1024))) uint16_t st3[(T::STAGES - 3) * (T::A_HALVES + T::B_HALVES)];
+    // (Two slots in one array would make the reads of either wait for the
+    // loads into both.) Arrays past the ring's last slot are never referenced
+    // and take no LDS.
+    constexpr int SLOT = T::A_HALVES + T::B_HALVES;
+    __shared__ __attribute__((aligned(1024))) uint16_t st0[SLOT];
+    __shared__ __attribute__((aligned(1024))) uint16_t st1[SLOT];
+    __shared__ __attribute__((aligned(1024))) uint16_t st2[SLOT];
+    __shared__ __attribute__((aligned(1024))) uint16_t st3[T::STAGES > 3 ? SLOT : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t st4[T::STAGES > 4 ? SLOT : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t st5[T::STAGES > 5 ? SLOT : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t st6[T::STAGES > 6 ? SLOT : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t st7[T::STAGES > 7 ? SLOT : 8];
     auto stage_a = [&]<int S>() -> uint16_t* {
+        static_assert(S >= 0 && S < T::STAGES, "ring slot");
         if constexpr (S == 0) return st0;
         else if constexpr (S == 1) return st1;
         else if constexpr (S == 2) return st2;
-        else return st3 + (S - 3) * (T::A_HALVES + T::B_HALVES);
+        else if constexpr (S == 3) return st3;
+        else if constexpr (S == 4) return st4;
+        else if constexpr (S == 5) return st5;
+        else if constexpr (S == 6) return st6;
+        else return st7;
     };
     auto stage_b = [&]<int S>() -> uint16_t* { return stage_a.template operator()<S>() + T::A_HALVES; };
 
@@ -448,7 +460,11 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     // Lane holds, for result rows d = 8q + 4*(lane/32) + r (r = 0..3), the
     // column 16*(j%4) + 64*(q/2) + 8*(q%2) + 4*(lane/32) + r of unit j/4.
     auto c_stage = [&](int s) -> char* {
-        return reinterpret_cast<char*>(s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3 + (s - 3) * (T::A_HALVES + T::B_HALVES));
+        char* r = reinterpret_cast<char*>(st0);
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            ((s == I ? (void)(r = reinterpret_cast<char*>(stage_a.template operator()<I>())) : (void)0), ...);
+        }(std::make_integer_sequence<int, T::STAGES>{});
+        return r;
     };
     with_epilogue(p, [&]<int ACT>() {
         // the bias of this lane's columns, loaded once for all its rows
