@@ -20,6 +20,16 @@ time the second workload the same way (graph replay, rotated inputs): the
 attention forward pass against the fp16 MFMA roofline, the row softmax
 against HBM bandwidth; each prints its own JSON line, with the oracle on
 sampled rows as its CPU baseline.
+
+    python bench.py --vs-torch [--all]
+
+adds, on stderr, torch.matmul (hipBLASLt, no ReLU) timed the same way on the
+same operands, as context.
+
+    python bench.py --sustain SECONDS [--sustain-op gemm|torch|attention]
+
+only runs one operation back to back on fixed inputs and prints its rate each
+second: the load under which board power and clocks are read with amd-smi.
 """
 from __future__ import annotations
 
@@ -417,6 +427,105 @@ def bench_softmax(args) -> dict:
     return line
 
 
+def time_torch_matmul(w, steps: int, warmup: int, graph_batch: int) -> float:
+    """Microseconds per launch of torch.matmul(a, b, out=c) (hipBLASLt; no
+    ReLU) on the same operands as time_gpu, with the same rotation over input
+    copies and the same graph replay: a context line, not part of the path."""
+    import torch
+    from tiled_dense_gemm_f16_amd import tune
+
+    a, b = workloads.workload_inputs(w)
+    rot = tune.rotation(2 * (w.M * w.K + w.K * w.N), graph_batch, ROTATE_BYTES)
+    ads = [a.cuda() for _ in range(rot)]
+    bds = [b.cuda() for _ in range(rot)]
+    c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.Stream()
+    call = lambda i: torch.matmul(ads[i], bds[i], out=c)  # noqa: E731
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            call(i % rot)
+        torch.cuda.synchronize()
+        steps = max(graph_batch, steps // graph_batch * graph_batch)
+        graphs = tune.capture_rotation(call, rot, graph_batch, stream)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for r in range(steps // graph_batch):
+            graphs[r % len(graphs)].replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / steps
+
+
+def sustain(args) -> int:
+    """Runs one operation back to back on the same inputs for args.sustain
+    seconds (batches of 50 launches, each batch between two events) and
+    prints the rate about once a second: the load under which board power and
+    clocks are sampled (amd-smi / rocm-smi from another process). --sustain-op
+    gemm is gemm_relu_f16 on --workload, torch is torch.matmul (hipBLASLt, no
+    ReLU) on the same operands, attention is flash_attn_fwd_f16 on the
+    --batch/--heads/--seq/--head-dim problem."""
+    import torch
+    import tiled_dense_gemm_f16_amd as gr
+
+    stream = torch.cuda.Stream()
+    if args.sustain_op == "attention":
+        B, H, S, D = args.batch, args.heads, args.seq, args.head_dim
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(0)
+        q, k, v = (torch.randn((B, H, S, D), generator=gen, device="cuda").half() for _ in range(3))
+        o = torch.empty_like(q)
+        pairs = S * (S + 1) // 2 if args.causal else S * S
+        flops = 4.0 * B * H * D * pairs
+        name = f"attention_fwd_f16_b{B}_h{H}_s{S}_d{D}" + ("_causal" if args.causal else "")
+
+        def call():
+            st = gr.flash_attn_fwd_f16(B, H, S, S, D, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), 0,
+                                       D ** -0.5, int(args.causal), stream.cuda_stream)
+            if st != gr.OK:
+                raise RuntimeError(gr.strerror(st))
+    else:
+        w = workloads.BY_NAME[args.workload]
+        a, b = (x.cuda() for x in workloads.workload_inputs(w))
+        c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+        flops = float(w.flops)
+        name = w.name + (" torch.matmul" if args.sustain_op == "torch" else " gemm_relu_f16")
+
+        def call():
+            if args.sustain_op == "torch":
+                torch.matmul(a, b, out=c)
+                return
+            st = gr.gemm_relu_f16(w.M, w.N, w.K, a.data_ptr(), b.data_ptr(), c.data_ptr(), stream.cuda_stream)
+            if st != gr.OK:
+                raise RuntimeError(gr.strerror(st))
+    batch = 50
+    end = time.time() + args.sustain
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            call()
+        torch.cuda.synchronize()
+        last, done, ms = time.time(), 0, 0.0
+        while time.time() < end:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(batch):
+                call()
+            e1.record(stream)
+            e1.synchronize()
+            done += batch
+            ms += e0.elapsed_time(e1)
+            if time.time() - last >= 1.0:
+                us = ms * 1e3 / done
+                print(f"[sustain] {name}: {us:.1f} us per launch, {flops / (us * 1e-6) / 1e12:.1f} TFLOP/s "
+                      f"({done} launches)", flush=True)
+                last, done, ms = time.time(), 0, 0.0
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -443,13 +552,18 @@ def main(argv=None) -> int:
     ap.add_argument("--causal", action="store_true")
     ap.add_argument("--rows", type=int, default=16384)
     ap.add_argument("--cols", type=int, default=8192)
+    ap.add_argument("--vs-torch", action="store_true",
+                    help="also time torch.matmul (hipBLASLt, no ReLU) on the same operands (lines on stderr)")
+    ap.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
+                    help="only run --sustain-op back to back for SECONDS, printing the rate each second")
+    ap.add_argument("--sustain-op", choices=("gemm", "torch", "attention"), default="gemm")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run an element-wise copy (negation) of MIB MiB, 20 times: a kernel of known "
                          "traffic, used to scale the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path shards along M or N without communication, but no multi-GPU run is made.",
               file=sys.stderr)
         return 2
@@ -470,6 +584,8 @@ def main(argv=None) -> int:
         return 0
     import tiled_dense_gemm_f16_amd as gr
     gr.load()
+    if args.sustain > 0:
+        return sustain(args)
     if args.op != "gemm":
         if args.graph == 50:
             args.graph = 10
@@ -485,6 +601,17 @@ def main(argv=None) -> int:
     r = time_gpu(w, args.steps, args.warmup, args.tile, args.graph, args.epilogue, args.layout)
     print(f"[bench] {w.name}: {r['ms_per_step'] * 1e3:.2f} us/step (graph batch {r['graph_batch']}), "
           f"single launches {r['launch_ms_mean'] * 1e3:.2f} us, tile {r['tile']}", file=sys.stderr, flush=True)
+
+    def vs_torch(ww, rr, steps, warmup):
+        if not args.vs_torch or args.layout != "nn":
+            return
+        t_us = time_torch_matmul(ww, steps, warmup, args.graph or 20)
+        ours = rr["ms_per_step"] * 1e3
+        print(json.dumps({"comparison": "torch.matmul (hipBLASLt, no ReLU), same operands and rotation",
+                          "workload": ww.name, "torch_us": round(t_us, 2), "gemm_relu_f16_us": round(ours, 2),
+                          "torch_over_ours": round(t_us / ours, 3)}), file=sys.stderr, flush=True)
+
+    vs_torch(w, r, args.steps, args.warmup)
     if args.all:
         for ow in workloads.ALL:
             if ow is w:
@@ -493,6 +620,7 @@ def main(argv=None) -> int:
                            args.layout)
             print(json.dumps(result_line(ow, orr, max(args.steps // 4, 50), max(args.warmup // 4, 10))),
                   file=sys.stderr, flush=True)
+            vs_torch(ow, orr, max(args.steps // 4, 50), max(args.warmup // 4, 10))
         # the pages' own tile (128 x 128 x 64) on 1024^3, for comparison
         pages_tile = next(t for t in range(gr.tile_count()) if gr.tile_name(t).startswith("128x128x64"))
         pw = workloads.SQUARE_1024

@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests skip cleanly on a host without a GPU (this build container);
+    # GPU tests skip cleanly on a host without a GPU;
     # on a GPU host a missing extension is an error, never a skip.
     try:
         import torch

