@@ -12,6 +12,8 @@
 namespace gemm_relu {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -165,21 +167,23 @@ __device__ __forceinline__ float bias_at(const Args& p, int n)
     return n < p.N ? (float)__builtin_bit_cast(_Float16, p.bias[n]) : 0.0f;
 }
 
-// Two consecutive outputs (columns n, n+1) through the epilogue and the
-// conversion to fp16, round to nearest even (v_cvt_f16_f32 under the default
-// rounding mode), as a packed bit pattern.
-template <int ACT>
-__device__ __forceinline__ uint32_t epi_pack2(const Args& p, float lo, float hi, int n)
+// Two fp32 values to a packed pair of fp16, each rounded to nearest even
+// (v_cvt_pk_f16_f32 under the default rounding mode; never the
+// round-toward-zero pack).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
 {
-    float a, b;
-    if constexpr (ACT == kActBiasGelu) {
-        a = gelu(lo + bias_at(p, n));
-        b = gelu(hi + bias_at(p, n + 1));
-    } else {
-        a = relu(lo);
-        b = relu(hi);
-    }
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+}
+
+// ReLU of a pair, applied after the rounding: max(fp16(x), 0) is fp16(max(x,
+// 0)) for every x (a positive x rounds to a value >= +0, a negative one to a
+// value <= 0 that the max turns into +0, and a sum that is exactly zero is
+// +0), and costs one packed conversion and one packed max per pair instead
+// of two maxima, two conversions and a merge.
+__device__ __forceinline__ uint32_t relu_pack_f16x2(float lo, float hi)
+{
+    const f16x2 h = __builtin_convertvector(f32x2{lo, hi}, f16x2);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(h, f16x2{(_Float16)0.0f, (_Float16)0.0f}));
 }
 
 // Bias of columns n .. n+3 (n % 4 == 0, N % 8 == 0: the vector paths), one
@@ -200,15 +204,8 @@ __device__ __forceinline__ f32x4 bias4(const Args& p, int n)
 template <int ACT>
 __device__ __forceinline__ uint32_t epi_pack2b(float lo, float hi, float blo, float bhi)
 {
-    float a, b;
-    if constexpr (ACT == kActBiasGelu) {
-        a = gelu(lo + blo);
-        b = gelu(hi + bhi);
-    } else {
-        a = relu(lo);
-        b = relu(hi);
-    }
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+    if constexpr (ACT == kActBiasGelu) return pack_f16x2(gelu(lo + blo), gelu(hi + bhi));
+    else return relu_pack_f16x2(lo, hi);
 }
 
 template <int ACT>

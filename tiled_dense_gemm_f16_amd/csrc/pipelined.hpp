@@ -42,10 +42,13 @@
 //    banks; the direct loads themselves write 1 KiB linearly.
 //  * When K is a multiple of 32 (KALIGNED) no step is partial: the loads carry
 //    no per-lane K test and each step only moves two buffer descriptors.
-//  * Epilogue: ReLU on the fp32 accumulators and v_cvt_f16_f32 (round to
-//    nearest even) into the now idle LDS ring, which holds the whole 256 x 256
-//    fp16 tile; then every lane stores 16 consecutive bytes of a row, so each
-//    store instruction writes two full 512-byte rows of C.
+//  * Epilogue: the fp32 accumulators go through v_cvt_pk_f16_f32 (round to
+//    nearest even) and a packed max with zero (ReLU) into the now idle LDS
+//    ring, which holds the whole 256 x 256 fp16 tile; then every lane stores
+//    16 consecutive bytes of a row, so each store instruction writes two full
+//    512-byte rows of C. Epilogue arithmetic runs at a quarter of the issue
+//    rate (64 lanes on 16-lane SIMDs) and all CUs reach it at once, so it is
+//    kept to two instructions per pair of outputs.
 //
 // Requirements (checked on the host): the leading dimension of each operand
 // (K or M for A, N or K for B) and N are multiples of 8, A, B and C are
@@ -471,6 +474,18 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         }(std::make_integer_sequence<int, T::STAGES>{});
         return r;
     };
+    // Stores of C: 16 bytes per lane, kLanesPerRow lanes per row of the tile.
+    constexpr int kRowsPerPass = T::C_ROWS_PER_PASS;  // BN / 8 lanes x 16 B per row
+    constexpr int kLanesPerRow = T::BN / 8;
+    constexpr int kPasses = T::BM / kRowsPerPass;
+    const int c = threadIdx.x % kLanesPerRow;
+    // pass `it`: this lane's row of the tile and its 16 bytes from the LDS copy
+    auto pass_row = [&](int it) -> int { return it * kRowsPerPass + (int)threadIdx.x / kLanesPerRow; };
+    auto pass_read = [&](int it) -> u32x4 {
+        const int rl = pass_row(it);
+        const char* cs = c_stage((it * kRowsPerPass) / T::C_ROWS_PER_STAGE);
+        return *reinterpret_cast<const u32x4*>(cs + (rl % T::C_ROWS_PER_STAGE) * (T::BN * 2) + ((c ^ c_swz(rl)) * 16));
+    };
     with_epilogue(p, [&]<int ACT>() {
         // the bias of this lane's columns, loaded once for all its rows
         f32x4 bias[T::FN][4];
@@ -504,17 +519,28 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     });
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    constexpr int kRowsPerPass = T::C_ROWS_PER_PASS;  // BN / 8 lanes x 16 B per row
-    constexpr int kLanesPerRow = T::BN / 8;
+    if (m0 + T::BM <= M && n0 + T::BN <= N) {
+        // the whole tile is in range: each batch's LDS reads are all issued
+        // before its stores, with no test per pass (a test per pass keeps each
+        // store waiting for its own read)
+        constexpr int kBatch = kPasses < 16 ? kPasses : 16;
+        static_assert(kPasses % kBatch == 0, "store batches");
 #pragma unroll
-    for (int it = 0; it < T::BM / kRowsPerPass; ++it) {
-        const int rl = it * kRowsPerPass + (int)threadIdx.x / kLanesPerRow;
-        const int c = threadIdx.x % kLanesPerRow;
-        const char* cs = c_stage((it * kRowsPerPass) / T::C_ROWS_PER_STAGE);
-        const u32x4 v = *reinterpret_cast<const u32x4*>(cs + (rl % T::C_ROWS_PER_STAGE) * (T::BN * 2) +
-                                                        ((c ^ c_swz(rl)) * 16));
-        const int m = m0 + rl, n = n0 + c * 8;
-        if (m < M && n < N) *reinterpret_cast<u32x4*>(p.C + (int64_t)m * N + n) = v;
+        for (int it0 = 0; it0 < kPasses; it0 += kBatch) {
+            u32x4 v[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) v[b] = pass_read(it0 + b);
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b)
+                *reinterpret_cast<u32x4*>(p.C + (int64_t)(m0 + pass_row(it0 + b)) * N + n0 + c * 8) = v[b];
+        }
+    } else {
+#pragma unroll
+        for (int it = 0; it < kPasses; ++it) {
+            const u32x4 v = pass_read(it);
+            const int m = m0 + pass_row(it), n = n0 + c * 8;
+            if (m < M && n < N) *reinterpret_cast<u32x4*>(p.C + (int64_t)m * N + n) = v;
+        }
     }
 }
 
