@@ -133,6 +133,32 @@ def test_each_tile_on_workloads(w, tile):
     parity.check(run(a, b, tile=tile), want, absdot=absdot, K=w.K, label=f"tile {tile}")
 
 
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (100, 72, 40), (16, 512, 256)])
+def test_tiny_negative_sums_give_plus_zero(M, N, K):
+    """Sums that round to zero in fp16 leave the epilogue as +0 (0x0000),
+    whatever their sign: products of +-2^-14 and +-2^-14 are +-2^-28, below
+    half the smallest fp16 subnormal, so the ReLU of the rounded value must
+    be +0, as in the oracle (ReLU first, then the rounding). Half of the rows
+    also get a term of ordinary size, so not every output is zero."""
+    rng = np.random.default_rng(M + N + K)
+    a = np.zeros((M, K), dtype=np.float16)
+    b = np.zeros((K, N), dtype=np.float16)
+    tiny = np.float16(2.0 ** -14)
+    a[:, 0] = tiny * rng.choice([-1, 1], M).astype(np.float16)
+    b[0, :] = tiny * rng.choice([-1, 1], N).astype(np.float16)
+    a[: M // 2, 1] = rng.choice([-1, 1], M // 2).astype(np.float16)
+    b[1, :] = rng.integers(-2, 3, N).astype(np.float16)
+    at = torch.from_numpy(a.view(np.int16)).view(torch.float16)
+    bt = torch.from_numpy(b.view(np.int16)).view(torch.float16)
+    want = oracle.gemm_relu_f16(workloads.as_u16(at), workloads.as_u16(bt))
+    assert (want[M // 2:] == 0).all() and (want[: M // 2] != 0).any()
+    for tile in [None] + list(range(gr.tile_count())):
+        say(f"[tiny] M={M} N={N} K={K} tile={tile}")
+        got = run(at, bt, tile=tile)
+        assert not (got == 0x8000).any(), f"tile {tile}: -0 in the output"
+        assert np.array_equal(got, want), f"tile {tile}: {np.sum(got != want)} mismatches"
+
+
 # ---------------------------------------------------------------------------
 # split-K: partial sums across workgroups, combined by the last one
 # ---------------------------------------------------------------------------
