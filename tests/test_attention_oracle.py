@@ -95,6 +95,17 @@ def ref_attention(Q, K, V, scale, causal):
     return np.einsum("bhij,bhjd->bhid", p, v), logsumexp(s, axis=-1)
 
 
+def ref_pv(Q, K, V, scale, causal):
+    """sum_j p_ij |V[j][d]| from scipy's softmax and a numpy product: the
+    error scale of a blocked P V product."""
+    q, k, v = vals(Q), vals(K), vals(V)
+    s = scale * np.einsum("bhid,bhjd->bhij", q, k)
+    if causal:
+        Sq, Skv = s.shape[-2:]
+        s = np.where(np.arange(Skv)[None, :] > np.arange(Sq)[:, None], -np.inf, s)
+    return np.einsum("bhij,bhjd->bhid", softmax(s, axis=-1), np.abs(v))
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,Sq,Skv,D", [(1, 1, 1, 1, 8), (1, 2, 9, 9, 16), (2, 3, 17, 17, 64),
                                           (1, 2, 5, 23, 32), (1, 1, 40, 12, 128)])
@@ -104,10 +115,11 @@ def test_attention_matches_numpy(B, H, Sq, Skv, D, causal):
     K = f16(rng.standard_normal((B, H, Skv, D)))
     V = f16(rng.standard_normal((B, H, Skv, D)))
     scale = 1.0 / math.sqrt(D)
-    O, od, lse = oracle.attention_f16(Q, K, V, scale, causal, want_double=True, want_lse=True)
+    O, od, lse, pv = oracle.attention_f16(Q, K, V, scale, causal, want_double=True, want_lse=True, want_pv=True)
     ref, ref_lse = ref_attention(Q, K, V, scale, causal)
     assert np.allclose(od, ref, rtol=1e-12, atol=1e-13)
     assert np.allclose(lse, ref_lse, rtol=1e-13, atol=1e-13)
+    assert np.allclose(pv, ref_pv(Q, K, V, scale, causal), rtol=1e-12, atol=1e-14)
     want = ref.astype(np.float16).view(np.uint16)
     assert ((O == want) | near_tie(ref)).all()
 
@@ -135,6 +147,29 @@ def test_attention_closed_forms():
     Qd[..., 0] = 1.0
     O = oracle.attention_f16(f16(Qd), f16(Kd), V, 1.0, False)
     assert np.array_equal(O[0, 0], np.broadcast_to(V[0, 0, 4], (S, D)))
+
+
+def test_attention_pv_closed_forms():
+    # pv = sum_j p_j |V[j]|: with non-negative values it is the output itself,
+    # it ignores the signs of V, and for equal scores it is the mean of |V|
+    rng = np.random.default_rng(13)
+    S, D = 9, 16
+    Q = f16(rng.standard_normal((1, 1, S, D)))
+    K = f16(rng.standard_normal((1, 1, S, D)))
+    V = f16(rng.standard_normal((1, 1, S, D)))
+    Vabs = V & np.uint16(0x7FFF)
+    for causal in (False, True):
+        _, od_abs = oracle.attention_f16(Q, K, Vabs, 0.3, causal, want_double=True)
+        _, pv = oracle.attention_f16(Q, K, V, 0.3, causal, want_pv=True)
+        _, pv_neg = oracle.attention_f16(Q, K, V ^ np.uint16(0x8000), 0.3, causal, want_pv=True)
+        assert np.allclose(pv, od_abs, rtol=1e-14, atol=0)
+        assert np.array_equal(pv, pv_neg)
+    Z = f16(np.zeros((1, 1, S, D)))
+    _, pv = oracle.attention_f16(Z, K, V, 1.0, True, want_pv=True)
+    for i in range(S):
+        assert np.allclose(pv[0, 0, i], np.abs(vals(V)[0, 0, :i + 1]).mean(axis=0), rtol=1e-13, atol=1e-15)
+    # causal row 0 sees one key: pv is |V[0]| exactly
+    assert np.array_equal(pv[0, 0, 0], np.abs(vals(V)[0, 0, 0]))
 
 
 def test_attention_key_permutation_invariance():
@@ -174,6 +209,9 @@ MUTANTS = {
                      "const double v = oracle_f16_to_f64(V[(d * nkeys + j) % (nkeys * D)]);"),
     "no_normalisation": ("const double p = s[j] / l;", "const double p = s[j];"),
     "lse_without_log": ("*lse = nkeys > 0 ? m + log(l) : -INFINITY;", "*lse = nkeys > 0 ? m + l : -INFINITY;"),
+    "pv_unnormalised": ("a[d] += p * fabs(v);", "a[d] += s[j] * fabs(v);"),
+    "pv_no_abs": ("a[d] += p * fabs(v);", "a[d] += p * v;"),
+    "pv_short_sum": ("a[d] += p * fabs(v);", "if (j + 1 < nkeys) a[d] += p * fabs(v);"),
     "k_index_of_q": ("oracle_f16_to_f64(K[j * D + d]);", "oracle_f16_to_f64(K[(j * D + d + 1) % (nkeys * D)]);"),
 }
 
@@ -186,6 +224,7 @@ def _pin_suite(mod) -> list[str]:
         ("attn_numpy", lambda: test_attention_matches_numpy(1, 2, 9, 9, 16, False)),
         ("attn_numpy_causal", lambda: test_attention_matches_numpy(2, 3, 17, 17, 64, True)),
         ("attn_closed", test_attention_closed_forms),
+        ("pv_closed", test_attention_pv_closed_forms),
     ]
     global oracle
     saved = oracle

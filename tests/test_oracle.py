@@ -768,3 +768,134 @@ def test_planted_transpose_mistake_is_caught(mutant, tmp_path):
     spec.loader.exec_module(mod)
     assert _trans_pin_suite(mod) != [], f"planted mistake {mutant} went unnoticed"
 
+
+
+# ---------------------------------------------------------------------------
+# 11. the error-scale output: absdot[i][j] = sum_k |A[i][k]| |B[k][j]|
+# ---------------------------------------------------------------------------
+# The GPU parity tests bound each output's fp32 accumulation error by
+# K 2^-24 absdot, so absdot must be the true sum of absolute products: a
+# value too large would loosen that bound without any test noticing. These
+# pins tie it to exact rational sums, to integer products, and to the
+# oracle's own signed sum of |A| and |B| (a separate code path).
+
+def exact_absdot(A_bits: np.ndarray, B_bits: np.ndarray) -> list:
+    M, K = A_bits.shape
+    _, N = B_bits.shape
+    Af = [[abs(exact_f16_value(int(A_bits[i, k]))) for k in range(K)] for i in range(M)]
+    Bf = [[abs(exact_f16_value(int(B_bits[k, j]))) for j in range(N)] for k in range(K)]
+    return [[sum((Af[i][k] * Bf[k][j] for k in range(K)), Fraction(0)) for j in range(N)] for i in range(M)]
+
+
+def abs_bits(X: np.ndarray) -> np.ndarray:
+    return X & np.uint16(0x7FFF)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (2, 3, 5), (5, 1, 16), (3, 17, 7), (7, 3, 17), (16, 5, 2)])
+def test_absdot_matches_exact_rational_sum(M, N, K):
+    rng = np.random.default_rng(M * 7919 + N * 104729 + K)
+    A = rand_f16_bits(rng, (M, K))
+    B = rand_f16_bits(rng, (K, N))
+    ex = exact_absdot(A, B)
+    _, sab = oracle.gemm_relu_f16(A, B, want_absdot=True)
+    ii, jj = np.divmod(np.arange(M * N), N)
+    _, sab_pts = oracle.gemm_relu_f16_points(A, B, ii, jj, want_absdot=True)
+    for i in range(M):
+        for j in range(N):
+            # K non-negative terms, each exact in double: relative error <= K 2^-53
+            bound = Fraction(K) * Fraction(1, 2 ** 53) * ex[i][j]
+            assert abs(Fraction(sab[i, j]) - ex[i][j]) <= bound, (i, j)
+            assert abs(Fraction(sab_pts[i * N + j]) - ex[i][j]) <= bound, (i, j)
+
+
+def test_absdot_integer_inputs_exact():
+    # integer-valued inputs: every term and partial sum is exact
+    a, b = workloads.make_inputs(13, 21, 37, dist="intsmall", seed=8)
+    A, B = workloads.as_u16(a), workloads.as_u16(b)
+    want = np.abs(a.numpy().astype(np.int64)) @ np.abs(b.numpy().astype(np.int64))
+    _, sab = oracle.gemm_relu_f16(A, B, want_absdot=True)
+    assert np.array_equal(sab, want.astype(np.float64))
+    _, sab_r = oracle.gemm_relu_f16(A, B, want_absdot=True, rows=(3, 11))
+    assert np.array_equal(sab_r, want[3:11].astype(np.float64))
+
+
+def test_absdot_sign_invariance_and_signed_sum_of_abs():
+    rng = np.random.default_rng(31)
+    A = rand_f16_bits(rng, (9, 33))
+    B = rand_f16_bits(rng, (33, 12))
+    _, s0 = oracle.gemm_relu_f16(A, B, want_absdot=True)
+    _, s1 = oracle.gemm_relu_f16(A ^ np.uint16(0x8000), B, want_absdot=True)
+    _, s2 = oracle.gemm_relu_f16(A, B ^ np.uint16(0x8000), want_absdot=True)
+    assert np.array_equal(s0, s1) and np.array_equal(s0, s2)
+    # the signed sum of |A| @ |B| follows the same k order, so it is the same double
+    _, pre_abs = oracle.gemm_relu_f16(abs_bits(A), abs_bits(B), want_pre=True)
+    assert np.array_equal(s0, pre_abs)
+    # it bounds the signed sum, with equality where all products share a sign
+    _, pre = oracle.gemm_relu_f16(A, B, want_pre=True)
+    assert (np.abs(pre) <= s0 * (1 + 33 * 2.0 ** -52)).all()
+
+
+def test_absdot_same_for_every_epilogue_and_layout():
+    rng = np.random.default_rng(32)
+    A = rand_f16_bits(rng, (6, 19))
+    B = rand_f16_bits(rng, (19, 10))
+    bias = rand_f16_bits(rng, (10,))
+    _, s0 = oracle.gemm_relu_f16(A, B, want_absdot=True)
+    _, sg = oracle.gemm_bias_gelu_f16(A, B, bias, want_absdot=True)
+    assert np.array_equal(s0, sg)  # the bias is not part of the product's error scale
+    for ta, tb in LAYOUTS:
+        _, st = oracle.gemm_relu_f16(_stored(A, ta), _stored(B, tb), want_absdot=True, trans_a=ta, trans_b=tb)
+        assert np.array_equal(st, s0), (ta, tb)
+
+
+ABSDOT_MUTANTS = {
+    "absdot_no_abs_b": ("sab[j] += aa * fabs(brow[j]);", "sab[j] += aa * brow[j];"),
+    "absdot_drop_last_k": ("sab[j] += aa * fabs(brow[j]);", "if (k + 1 < K) sab[j] += aa * fabs(brow[j]);"),
+    "absdot_doubled": ("if (sab) absdot[i * N + j] = sab[j];", "if (sab) absdot[i * N + j] = 2.0 * sab[j];"),
+    "absdot_points_no_abs_a": ("s += fabs(a) * fabs(b);", "s += a * fabs(b);"),
+    "absdot_points_extra_term": ("s += fabs(a) * fabs(b);", "s += fabs(a) * fabs(b) + (k == 0 ? fabs(a) : 0.0);"),
+}
+
+
+def _absdot_pin_suite(mod) -> list[str]:
+    global oracle
+    checks = [
+        ("exact", lambda: test_absdot_matches_exact_rational_sum(3, 17, 7)),
+        ("exact_k1", lambda: test_absdot_matches_exact_rational_sum(1, 1, 1)),
+        ("integer", test_absdot_integer_inputs_exact),
+        ("signs", test_absdot_sign_invariance_and_signed_sum_of_abs),
+        ("layouts", test_absdot_same_for_every_epilogue_and_layout),
+    ]
+    saved, fails = oracle, []
+    oracle = mod
+    try:
+        for name, fn in checks:
+            try:
+                fn()
+            except Exception:  # an assertion or a crash counts as caught
+                fails.append(name)
+    finally:
+        oracle = saved
+    return fails
+
+
+def test_absdot_pins_pass_on_real_oracle():
+    assert _absdot_pin_suite(oracle) == []
+
+
+@pytest.mark.parametrize("mutant", sorted(ABSDOT_MUTANTS))
+def test_planted_absdot_mistake_is_caught(mutant, tmp_path):
+    import importlib.util
+    src_dir = os.path.join(os.path.dirname(HERE), "oracle")
+    old, new = ABSDOT_MUTANTS[mutant]
+    text = open(os.path.join(src_dir, "gemm_relu_oracle.c")).read()
+    assert text.count(old) == 1, f"mutation anchor for {mutant} not found"
+    dst = tmp_path / "oracle_mut"
+    dst.mkdir()
+    (dst / "gemm_relu_oracle.c").write_text(text.replace(old, new, 1))
+    shutil.copy(os.path.join(src_dir, "__init__.py"), dst / "__init__.py")
+    shutil.copy(os.path.join(src_dir, "attention_oracle.c"), dst / "attention_oracle.c")
+    spec = importlib.util.spec_from_file_location(f"oracle_smut_{mutant}", dst / "__init__.py")
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert _absdot_pin_suite(mod) != [], f"planted mistake {mutant} went unnoticed"
