@@ -4,11 +4,14 @@
 
 A step is one call of gemm_relu_f16 on one batch of synthetic input that is
 already resident in HBM: the whole hot path (tile loads, MFMA main loop, ReLU,
-fp16 store) in one kernel. W untimed steps are followed by K timed ones,
-bracketed by stream synchronisation; the calls are captured G at a time into a
-HIP graph and replayed (--graph 0 launches them one by one). The line printed
-on stdout is one JSON object. Extra per-workload lines (``--all``) go to
-stderr.
+fp16 store) in one kernel. Exactly K timed steps follow the untimed warm-up,
+bracketed by stream synchronisation; the calls are captured min(G, K) at a
+time into HIP graphs and replayed (--graph 0 launches them one by one). The
+warm-up runs the same work back to back for at least W launches and at least
+--steady-ms milliseconds, so that the timed region sees the clock the chip
+settles at under this load; the shader clock is sampled and reported with the
+device's name and architecture. The line printed on stdout is one JSON
+object. Extra per-workload lines (``--all``) go to stderr.
 
 The CPU baseline leg times the oracle (plain C, all host threads) on a bounded
 slice of the same workload -- leading rows of C -- and scales it to TFLOP/s.
@@ -105,27 +108,184 @@ def measured_traffic(workload: str, tile: str, layout: str = "nn", epilogue: str
 
 
 ROTATE_BYTES = 768 << 20  # well above the 256 MB last-level (MALL) cache
+STEADY_MS = 500.0         # back-to-back work before the timed region
+
+
+def _sclk_file() -> str | None:
+    """The sysfs file whose line marked '*' is the GPU's current shader clock
+    (the only card on a one-GPU machine; else the first that has the file)."""
+    import glob
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    return paths[0] if paths else None
+
+
+class ClockSampler:
+    """Samples the current shader clock (MHz) every `period` seconds on a
+    thread, with host timestamps, so that the clock the chip held during a
+    timed region can be reported next to the time."""
+
+    def __init__(self, period: float = 0.005):
+        import threading
+        self.path = _sclk_file()
+        self.period = period
+        self.samples: list[tuple[float, float]] = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self) -> float | None:
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append((time.perf_counter(), v))
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+        return False
+
+    def summary(self, t0: float, t1: float) -> dict:
+        """Median, min and max of the samples taken in [t0, t1] (host clock)."""
+        v = sorted(x for t, x in self.samples if t0 <= t <= t1)
+        if not v:
+            return {"samples": 0, "source": self.path}
+        return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v), "source": self.path}
+
+
+def device_identity() -> dict:
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"gpu_name": torch.cuda.get_device_name(0), "gfx_arch": p.gcnArchName.split(":")[0],
+            "compute_units": p.multi_processor_count, "hbm_gib": round(p.total_memory / 2 ** 30, 1)}
+
+
+def time_launches(calls, steps: int, warmup: int, graph_batch: int, stream, steady_ms: float = STEADY_MS,
+                  singles: int = 200) -> dict:
+    """Times exactly `steps` launches on `stream`, bracketed by two events on
+    that stream (and torch.cuda.synchronize() on both sides). calls[i]() makes
+    the launch on input copy i and returns its status.
+
+    * Every copy is called once first, untimed (this creates any split-K
+      workspace, so nothing is allocated or cleared inside a graph).
+    * With graph_batch = G > 0 the launches are captured min(G, steps) at a
+      time into HIP graphs that cycle through the copies, plus one graph for
+      the remainder, so the timed region holds exactly `steps` launches
+      without the host's per-call cost; G = 0 launches them one by one.
+    * Before the timed region the same graphs (or calls) run back to back for
+      at least `warmup` launches and at least `steady_ms` milliseconds, so
+      that the chip's clock has settled under this load whatever `warmup`
+      says; the shader clock is sampled throughout.
+    * After it, `singles` launches each between their own pair of events give
+      the duration of one launch under the same load."""
+    import torch
+    from tiled_dense_gemm_f16_amd import tune
+    import tiled_dense_gemm_f16_amd as gr
+
+    rot = len(calls)
+
+    def checked(i):
+        st = calls[i]()
+        if st is not None and st != gr.OK:
+            raise RuntimeError(f"launch refused: {gr.strerror(st)}")
+
+    torch.cuda.synchronize()
+    with ClockSampler() as clk, torch.cuda.stream(stream):
+        for i in range(rot):
+            checked(i)
+        torch.cuda.synchronize()
+        batch = min(graph_batch, steps) if graph_batch > 0 else 0
+        if batch:
+            graphs = tune.capture_rotation(lambda i: calls[i](), rot, batch, stream)
+            rem = steps % batch
+            tail = None
+            if rem:
+                # the remainder: one graph of the first `rem` copies
+                tail = tune.capture_rotation(lambda i: calls[i](), min(rot, rem), rem, stream)[0]
+
+            def run_steps():
+                for r in range(steps // batch):
+                    graphs[r % len(graphs)].replay()
+                if tail is not None:
+                    tail.replay()
+
+            def warm_chunk(r):
+                graphs[r % len(graphs)].replay()
+                return batch
+        else:
+            def run_steps():
+                for i in range(steps):
+                    calls[i % rot]()
+
+            def warm_chunk(r):
+                for i in range(16):
+                    calls[(16 * r + i) % rot]()
+                return 16
+        torch.cuda.synchronize()
+        # steady state: the same work back to back, the host kept close
+        # behind the device by a synchronisation every few chunks
+        tw0 = time.perf_counter()
+        done, r = 0, 0
+        while done < warmup or (time.perf_counter() - tw0) * 1e3 < steady_ms:
+            done += warm_chunk(r)
+            r += 1
+            if r % 4 == 0:
+                stream.synchronize()
+        torch.cuda.synchronize()
+        tw1 = time.perf_counter()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        h0 = time.perf_counter()
+        t0.record(stream)
+        run_steps()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        h1 = time.perf_counter()
+        total_ms = t0.elapsed_time(t1)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(singles)]
+        for i, (e0, e1) in enumerate(evs):
+            e0.record(stream)
+            calls[i % rot]()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        h2 = time.perf_counter()
+    per = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    timed = clk.summary(h0, h1)
+    if timed["samples"] < 3:
+        # a short timed region: the clock over the last 100 ms of the same work before it as well
+        timed = dict(clk.summary(max(tw0, tw1 - 0.1), h1), window="last 100 ms of warm-up + timed region")
+    else:
+        timed["window"] = "timed region"
+    return {"total_ms": total_ms, "steps": steps, "ms_per_step": total_ms / steps,
+            "launch_ms_mean": float(per.mean()), "launch_ms_median": float(np.median(per)),
+            "launch_ms_min": float(per.min()), "rotation": rot, "graph_batch": batch,
+            "warmup_launches": done, "warmup_ms": round((tw1 - tw0) * 1e3, 1),
+            "sclk_mhz": timed, "sclk_mhz_single_launches": clk.summary(h1, h2)}
 
 
 def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0, epilogue: str = "relu",
-             layout: str = "nn"):
-    """Times `steps` back-to-back launches on one stream, bracketed by two
-    events on that stream. Successive launches cycle through R copies of
-    (A, B) with R * (|A| + |B|) >= 768 MiB (at most 4096 copies: the 256^3
-    shape falls short), so the inputs of a launch are not left in the
-    last-level cache by the previous ones: every launch reads its inputs
-    from HBM.
-
-    With graph_batch = G > 0 the launches are captured G at a time into HIP
-    graphs (after the warm-up, so any workspace already exists and nothing is
-    allocated or cleared inside a graph): R / G graphs when R > G, which
-    together cycle once through the copies. The timed region replays them in
-    turn, steps / G replays: the device throughput without the host's
-    per-call launch cost, which otherwise dominates for kernels of a few
-    microseconds.
-
-    Also times 200 single launches, each between its own pair of events, for
-    the duration of one launch.
+             layout: str = "nn", rotate_bytes: int = ROTATE_BYTES, steady_ms: float = STEADY_MS):
+    """Times `steps` launches of the GEMM on workload w (time_launches).
+    Successive launches cycle through R copies of (A, B) with R * (|A| + |B|)
+    >= rotate_bytes (at most 4096 copies: the 256^3 shape falls short of
+    768 MiB), so with the default the inputs of a launch are not left in the
+    256 MB last-level cache by the previous ones: every launch reads its
+    inputs from HBM. rotate_bytes = 0 reuses one copy (inputs cached).
 
     `layout` ("nn", "nt", "tn", "tt") stores A as K x M (t in first place)
     and/or B as N x K (t in second place) and calls the transposed-operand
@@ -139,7 +299,7 @@ def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0, epilog
     a_st = a.t().contiguous() if ta else a
     b_st = b.t().contiguous() if tb else b
     in_bytes = 2 * (w.M * w.K + w.K * w.N)
-    rot = tune.rotation(in_bytes, graph_batch, ROTATE_BYTES)
+    rot = tune.rotation(in_bytes, min(graph_batch, steps), rotate_bytes) if rotate_bytes > 0 else 1
     ads = [a_st.cuda() for _ in range(rot)]
     bds = [b_st.cuda() for _ in range(rot)]
     c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
@@ -150,56 +310,18 @@ def time_gpu(w, steps: int, warmup: int, tile=None, graph_batch: int = 0, epilog
         gen = torch.Generator(device="cpu")
         gen.manual_seed(w.seed + 1)
         bias = (torch.randn(w.N, generator=gen) * (w.K ** 0.5) * w.scale * w.scale).half().cuda()
-        call = gr.gemm_bias_gelu_f16_op
-        args = [(w.M, w.N, w.K, ads[i].data_ptr(), int(ta), bds[i].data_ptr(), int(tb), bias.data_ptr(),
-                 c.data_ptr(), stream.cuda_stream, opts) for i in range(rot)]
+        calls = [lambda i=i: gr.gemm_bias_gelu_f16_op(w.M, w.N, w.K, ads[i].data_ptr(), int(ta), bds[i].data_ptr(),
+                                                      int(tb), bias.data_ptr(), c.data_ptr(), stream.cuda_stream, opts)
+                 for i in range(rot)]
     else:
-        call = gr.gemm_relu_f16_op
-        args = [(w.M, w.N, w.K, ads[i].data_ptr(), int(ta), bds[i].data_ptr(), int(tb), c.data_ptr(),
-                 stream.cuda_stream, opts) for i in range(rot)]
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for i in range(warmup):
-            st = call(*args[i % rot])
-            if st != gr.OK:
-                raise RuntimeError(gr.strerror(st))
-        torch.cuda.synchronize()
-        graphs = []
-        if graph_batch > 0:
-            steps = max(graph_batch, steps // graph_batch * graph_batch)
-            graphs = tune.capture_rotation(lambda i: call(*args[i]), rot, graph_batch, stream)
-            for g in graphs:  # every copy once before the timed region
-                g.replay()
-            torch.cuda.synchronize()
-        # the whole timed region between two events on the launch stream
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        if graphs:
-            for r in range(steps // graph_batch):
-                graphs[r % len(graphs)].replay()
-        else:
-            for i in range(steps):
-                call(*args[i % rot])
-        t1.record(stream)
-        torch.cuda.synchronize()
-        total_ms = t0.elapsed_time(t1)
-        # per-launch event pairs (same stream) for the kernel's own duration
-        nper = min(steps, 200)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nper)]
-        for i, (e0, e1) in enumerate(evs):
-            e0.record(stream)
-            call(*args[i % rot])
-            e1.record(stream)
-        torch.cuda.synchronize()
-    per = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+        calls = [lambda i=i: gr.gemm_relu_f16_op(w.M, w.N, w.K, ads[i].data_ptr(), int(ta), bds[i].data_ptr(), int(tb),
+                                                 c.data_ptr(), stream.cuda_stream, opts) for i in range(rot)]
+    r = time_launches(calls, steps, warmup, graph_batch, stream, steady_ms)
     tile_id = (gr.select_tile(w.M, w.N, w.K, ads[0].data_ptr(), bds[0].data_ptr(), c.data_ptr(), trans_a=ta,
                               trans_b=tb) if tile is None else tile)
-    return {"total_ms": total_ms, "steps": steps, "ms_per_step": total_ms / steps,
-            "launch_ms_mean": float(per.mean()), "launch_ms_median": float(np.median(per)),
-            "launch_ms_min": float(per.min()), "tile": gr.tile_name(tile_id) if tile_id >= 0 else "generic",
-            "rotation": rot, "graph_batch": graph_batch, "epilogue": epilogue, "layout": layout,
-            "c": c, "a": a, "b": b}
+    r.update({"tile": gr.tile_name(tile_id) if tile_id >= 0 else "generic", "epilogue": epilogue, "layout": layout,
+              "c": c, "a": a, "b": b})
+    return r
 
 
 def cpu_baseline(w, gpu_c, target_s: float = 12.0):
@@ -232,6 +354,19 @@ def cpu_baseline(w, gpu_c, target_s: float = 12.0):
             "seconds": secs, "parity_of_sample": {"max_abs_err": float(err.max()), "violations": viol}}
 
 
+def timing_fields(r: dict) -> dict:
+    """What every line reports about how its time was taken."""
+    ratio = r["ms_per_step"] / r["launch_ms_mean"] if r["launch_ms_mean"] > 0 else None
+    return {"graph_batch": r["graph_batch"],
+            "single_launch_event_ms": {"mean": round(r["launch_ms_mean"], 5),
+                                       "median": round(r.get("launch_ms_median", r["launch_ms_mean"]), 5),
+                                       "min": round(r["launch_ms_min"], 5)},
+            "timed_over_single_launch_mean": round(ratio, 4) if ratio else None,
+            "steady_state": {"warmup_launches": r["warmup_launches"], "warmup_ms": r["warmup_ms"]},
+            "sclk_mhz": r["sclk_mhz"], "sclk_mhz_single_launches": r["sclk_mhz_single_launches"],
+            "device": device_identity()}
+
+
 def result_line(w, r, steps, warmup, cpu=None):
     bound = "hbm" if 2 * w.M * w.N * w.K / w.min_bytes < 315 and w.M <= 64 else "mfma"
     value = w.flops / (r["ms_per_step"] * 1e-3) / 1e12
@@ -257,9 +392,7 @@ def result_line(w, r, steps, warmup, cpu=None):
                        "parallelism": "single GPU"},
             "roofline": roof,
             "kernel_ms_timed_region_mean": round(r["ms_per_step"], 5),
-            "graph_batch": r["graph_batch"],
-            "single_launch_event_ms": {"mean": round(r["launch_ms_mean"], 5), "median": round(r["launch_ms_median"], 5),
-                                       "min": round(r["launch_ms_min"], 5)},
+            **timing_fields(r),
             "hbm_gbs_at_min_bytes": round(w.min_bytes / (r["ms_per_step"] * 1e-3) / 1e9, 1),
             "kernel_source_sha256": source_hash(r["tile"])}
     if cpu is not None:
@@ -268,41 +401,9 @@ def result_line(w, r, steps, warmup, cpu=None):
 
 
 def time_calls(calls, steps: int, warmup: int, graph_batch: int, stream) -> dict:
-    """Warm-up, then `steps` launches replayed from HIP graphs of `graph_batch`
-    (cycling through `calls`, one per input copy) between two events on
-    `stream`; then 50 single launches between their own events."""
-    import torch
-
-    rot = len(calls)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for i in range(warmup):
-            calls[i % rot]()
-        torch.cuda.synchronize()
-        steps = max(graph_batch, steps // graph_batch * graph_batch)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(graph_batch):
-                calls[i % rot]()
-        graph.replay()
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for _ in range(steps // graph_batch):
-            graph.replay()
-        t1.record(stream)
-        torch.cuda.synchronize()
-        total_ms = t0.elapsed_time(t1)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
-        for i, (e0, e1) in enumerate(evs):
-            e0.record(stream)
-            calls[i % rot]()
-            e1.record(stream)
-        torch.cuda.synchronize()
-    per = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
-    return {"ms_per_step": total_ms / steps, "steps": steps, "launch_ms_mean": float(per.mean()),
-            "launch_ms_min": float(per.min()), "rotation": rot, "graph_batch": graph_batch}
+    """The second workload's timing: time_launches over `calls` (one per
+    input copy)."""
+    return time_launches(calls, steps, warmup, graph_batch, stream)
 
 
 def cpu_sample(fn, total_rows: int, target_s: float) -> tuple[int, float]:
@@ -361,8 +462,7 @@ def bench_attention(args) -> dict:
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
                          "traffic": measured_traffic(name, f"attn_fwd_d{D}")},
-            "kernel_ms_timed_region_mean": round(r["ms_per_step"], 5), "graph_batch": r["graph_batch"],
-            "single_launch_event_ms": {"mean": round(r["launch_ms_mean"], 5), "min": round(r["launch_ms_min"], 5)},
+            "kernel_ms_timed_region_mean": round(r["ms_per_step"], 5), **timing_fields(r),
             "flops_per_launch": flops, "kernel_source_sha256": source_hash(f"attn_fwd_d{D}")}
     if not args.no_cpu_baseline:
         import oracle
@@ -415,8 +515,7 @@ def bench_softmax(args) -> dict:
                        "parallelism": "single GPU"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(name, "softmax_rows")},
-            "kernel_ms_timed_region_mean": round(r["ms_per_step"], 5), "graph_batch": r["graph_batch"],
-            "single_launch_event_ms": {"mean": round(r["launch_ms_mean"], 5), "min": round(r["launch_ms_min"], 5)},
+            "kernel_ms_timed_region_mean": round(r["ms_per_step"], 5), **timing_fields(r),
             "bytes_per_launch": moved}
     if not args.no_cpu_baseline:
         import oracle
@@ -557,6 +656,11 @@ def main(argv=None) -> int:
     ap.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
                     help="only run --sustain-op back to back for SECONDS, printing the rate each second")
     ap.add_argument("--sustain-op", choices=("gemm", "torch", "attention"), default="gemm")
+    ap.add_argument("--rotate-mib", type=int, default=ROTATE_BYTES >> 20, metavar="MIB",
+                    help="cycle the launches through copies of the inputs spanning at least MIB MiB "
+                         "(default: three times the last-level cache, so inputs come from HBM; 0: one copy)")
+    ap.add_argument("--steady-ms", type=float, default=STEADY_MS, metavar="MS",
+                    help="run the timed work back to back for at least MS ms before the timed region")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run an element-wise copy (negation) of MIB MiB, 20 times: a kernel of known "
                          "traffic, used to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -598,7 +702,8 @@ def main(argv=None) -> int:
         return 0
 
     w = workloads.BY_NAME[args.workload]
-    r = time_gpu(w, args.steps, args.warmup, args.tile, args.graph, args.epilogue, args.layout)
+    r = time_gpu(w, args.steps, args.warmup, args.tile, args.graph, args.epilogue, args.layout,
+                 args.rotate_mib << 20, args.steady_ms)
     print(f"[bench] {w.name}: {r['ms_per_step'] * 1e3:.2f} us/step (graph batch {r['graph_batch']}), "
           f"single launches {r['launch_ms_mean'] * 1e3:.2f} us, tile {r['tile']}", file=sys.stderr, flush=True)
 
@@ -617,7 +722,7 @@ def main(argv=None) -> int:
             if ow is w:
                 continue
             orr = time_gpu(ow, max(args.steps // 4, 50), max(args.warmup // 4, 10), None, args.graph, args.epilogue,
-                           args.layout)
+                           args.layout, args.rotate_mib << 20, args.steady_ms)
             print(json.dumps(result_line(ow, orr, max(args.steps // 4, 50), max(args.warmup // 4, 10))),
                   file=sys.stderr, flush=True)
             vs_torch(ow, orr, max(args.steps // 4, 50), max(args.warmup // 4, 10))
@@ -625,7 +730,7 @@ def main(argv=None) -> int:
         pages_tile = next(t for t in range(gr.tile_count()) if gr.tile_name(t).startswith("128x128x64"))
         pw = workloads.SQUARE_1024
         prr = time_gpu(pw, max(args.steps // 4, 50), max(args.warmup // 4, 10), pages_tile, args.graph,
-                       args.epilogue, args.layout)
+                       args.epilogue, args.layout, args.rotate_mib << 20, args.steady_ms)
         pl = result_line(pw, prr, max(args.steps // 4, 50), max(args.warmup // 4, 10))
         pl["note"] = "the pages' 128x128x64 tile pinned, for comparison with the library's choice"
         print(json.dumps(pl), file=sys.stderr, flush=True)

@@ -46,12 +46,14 @@ int softmax_rows_f16(int64_t rows, int64_t cols, const void* X, void* Y, void* s
  *   lse       : NULL, or [B][H][Sq] fp32 receiving m_i + ln(sum_j exp(s_ij - m_i))
  *               (-inf for a row with no keys)
  *   D         : 64 or 128
- * scale is any finite float (1/sqrt(D) is the usual choice). Skv == 0 gives
- * O = 0. Pointers must be 16-byte aligned (lse 4-byte); O must not overlap Q,
- * K, V or lse. Errors: EINVAL (negative size, NULL with data, causal not 0/1,
- * scale not finite, overlap), EUNSUPPORTED (D not 64/128, a size above the
- * kernel's 32-bit offsets (B*H, Sq, Skv < 2^31, S * D < 2^30), misaligned
- * pointer, device not gfx950), EHIP.
+ * scale is a finite float with |scale| <= 2^64 (1/sqrt(D) is the usual
+ * choice): the kernel scales scores in fp32, and with |Q.K| <= D * 65504^2
+ * that bound keeps every scaled score and every difference of two finite.
+ * Skv == 0 gives O = 0. Pointers must be 16-byte aligned (lse 4-byte); O must
+ * not overlap Q, K, V or lse. Errors: EINVAL (negative size, NULL with data,
+ * causal not 0/1, scale not finite, overlap), EUNSUPPORTED (D not 64/128,
+ * |scale| > 2^64, a size above the kernel's 32-bit offsets (B*H, Sq,
+ * Skv < 2^31, S * D < 2^30), misaligned pointer, device not gfx950), EHIP.
  */
 int flash_attn_fwd_f16(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, const void* Q, const void* K,
                        const void* V, void* O, void* lse, float scale, int causal, void* stream);

@@ -33,8 +33,10 @@
  * (partials plus one counter per output tile). The library allocates it with
  * hipMalloc on the first such call for a (device, stream) pair, clears its
  * counters with an asynchronous memset on that stream, keeps it until the
- * process ends, and grows it (after synchronising that stream) when a later
- * call needs more. Each launch leaves the counters at zero, so calls on one
+ * process ends, and grows it (to at least twice its size) when a later call
+ * needs more. A replaced workspace is kept, not freed, until the process
+ * ends, because a HIP graph captured on that stream earlier may still use
+ * it. Each launch leaves the counters at zero, so calls on one
  * stream reuse it in order; calls on different streams use different
  * workspaces. Two host threads enqueueing on the same stream at the same
  * time race on the workspace. Failure to allocate gives GEMM_RELU_ENOMEM.

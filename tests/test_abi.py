@@ -305,6 +305,10 @@ def test_attention_arguments_rejected():
     assert f(1, 1, 0, 4, 64, 0, K, V, 0, 0, 0.1, 0) == gr.OK            # nothing to write
     assert f(1, 1, 4, 4, 64, Q, K, V, O, 0, float("inf"), 0) == gr.EINVAL
     assert f(1, 1, 4, 4, 64, Q, K, V, O, 0, float("nan"), 0) == gr.EINVAL
+    # scales whose scaled scores could overflow fp32 are refused, before any HIP call
+    assert f(1, 1, 4, 4, 64, Q, K, V, O, 0, 1e30, 0) == gr.EUNSUPPORTED
+    assert f(1, 1, 4, 4, 64, Q, K, V, O, 0, -3e38, 1) == gr.EUNSUPPORTED
+    assert f(1, 1, 4, 4, 64, Q, K, V, O, 0, 2.0 ** 65, 0) == gr.EUNSUPPORTED
 
 
 def test_empty_output_is_a_no_op():
@@ -331,3 +335,4 @@ def test_product_path_never_imports_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".hpp", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
+

@@ -418,3 +418,60 @@ def test_splitk_workspace_under_graph_capture():
         torch.cuda.synchronize()
         assert np.array_equal(workloads.as_u16(out.cpu()), want), f"replay {rep}"
 
+
+
+def test_workspace_growth_keeps_captured_graphs_valid():
+    # a graph captured while the stream's workspace was small keeps that
+    # workspace's address; a later, larger call grows the workspace, and the
+    # graph's replays must still find their partial sums and counters where
+    # they were (the replaced workspace is kept, not freed)
+    Ms, Ns, Ks = 16, 512, 4096      # 4 tiles of 16 x 128 -> 32 splits, 1 MiB of partials
+    Ml, Nl, Kl = 64, 4096, 4096     # larger: 128 tiles of 16 x 128 -> 2 splits, 2 MiB of partials
+    a, b = workloads.make_inputs(Ms, Ns, Ks, dist="intsmall", seed=81)
+    al, bl = workloads.make_inputs(Ml, Nl, Kl, dist="intsmall", seed=82)
+    want = oracle.gemm_relu_f16(workloads.as_u16(a), workloads.as_u16(b))
+    want_l = oracle.gemm_relu_f16(workloads.as_u16(al), workloads.as_u16(bl))
+    assert "splitk" in gr.tile_name(gr.select_tile(Ms, Ns, Ks))
+    assert "splitk" in gr.tile_name(gr.select_tile(Ml, Nl, Kl))
+    ad, bd, ald, bld = a.cuda(), b.cuda(), al.cuda(), bl.cuda()
+    out = torch.empty((Ms, Ns), dtype=torch.float16, device="cuda")
+    out_l = torch.empty((Ml, Nl), dtype=torch.float16, device="cuda")
+    s = torch.cuda.Stream()
+    say(f"[workspace] capture {Ms}x{Ns}x{Ks}, then grow with {Ml}x{Nl}x{Kl}")
+    with torch.cuda.stream(s):
+        gr.gemm_relu(ad, bd, out=out)   # creates the small workspace on s
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        st = gr.gemm_relu_f16(Ms, Ns, Ks, ad.data_ptr(), bd.data_ptr(), out.data_ptr(), s.cuda_stream)
+    assert st == gr.OK
+    with torch.cuda.stream(s):
+        gr.gemm_relu(ald, bld, out=out_l)   # grows the workspace of s
+    torch.cuda.synchronize()
+    assert np.array_equal(workloads.as_u16(out_l.cpu()), want_l)
+    # fresh device memory that could reuse freed addresses
+    junk = [torch.full((1 << 20,), 7.0, device="cuda") for _ in range(8)]
+    for rep in range(3):
+        out.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(workloads.as_u16(out.cpu()), want), f"replay {rep}"
+        with torch.cuda.stream(s):
+            gr.gemm_relu(ald, bld, out=out_l)   # eager work on the grown workspace between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(workloads.as_u16(out_l.cpu()), want_l), f"eager {rep}"
+    assert all(bool((j == 7.0).all()) for j in junk)
+
+
+@pytest.mark.parametrize("group_m", [2 ** 31 - 1, 2 ** 28 + 1, 5])
+@pytest.mark.parametrize("tile", [0, 9, 2])
+def test_huge_group_m_is_the_whole_grid(group_m, tile):
+    # a group of more tile-rows than the grid has is one group of all of them:
+    # every tile is still written exactly once
+    M, N, K = 1024, 1024, 96
+    a, b = workloads.make_inputs(M, N, K, dist="intsmall", seed=83)
+    want = oracle.gemm_relu_f16(workloads.as_u16(a), workloads.as_u16(b))
+    say(f"[group_m] tile {tile} group_m {group_m}")
+    got = run(a, b, tile=tile, group_m=group_m)
+    assert np.array_equal(got, want)

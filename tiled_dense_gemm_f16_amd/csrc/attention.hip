@@ -99,6 +99,9 @@ int flash_attn_fwd_f16(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
     if (B < 0 || H < 0 || Sq < 0 || Skv < 0 || D < 0) return GEMM_RELU_EINVAL;
     if (causal != 0 && causal != 1) return GEMM_RELU_EINVAL;
     if (!std::isfinite(scale)) return GEMM_RELU_EINVAL;
+    // |scale * log2(e) * Q.K| <= 2^64 * 1.45 * 128 * 65504^2 < 2^108: finite
+    // in fp32, as is the difference of two such scores
+    if (std::fabs(scale) > 0x1p64f) return GEMM_RELU_EUNSUPPORTED;
     if (D != 64 && D != 128) return GEMM_RELU_EUNSUPPORTED;
     if (B > INT32_MAX || H > INT32_MAX || B * H > INT32_MAX || Sq > INT32_MAX || Skv > INT32_MAX)
         return GEMM_RELU_EUNSUPPORTED;

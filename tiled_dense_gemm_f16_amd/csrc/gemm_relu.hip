@@ -20,6 +20,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "gemm_relu.h"
 #include "pipelined.hpp"
@@ -300,6 +301,12 @@ struct Workspace {
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Workspaces replaced by larger ones. They are never freed: a HIP graph
+// captured on that stream earlier holds their addresses in its kernel
+// arguments and may be replayed at any time. Growth at least doubles both
+// parts, so the retired buffers of a stream add up to less than its current
+// workspace.
+std::vector<char*> g_ws_retired;
 
 size_t counter_bytes(size_t slots) { return (slots * 4 + 255) / 256 * 256; }
 
@@ -316,13 +323,11 @@ int get_workspace(int dev, hipStream_t stream, size_t slots, size_t partial_byte
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return GEMM_RELU_EHIP;
         if (cap != hipStreamCaptureStatusNone) return GEMM_RELU_EUNSUPPORTED;
-        const size_t ns = slots > w.counter_slots ? slots : w.counter_slots;
-        const size_t np = partial_bytes > w.partial_bytes ? partial_bytes : w.partial_bytes;
+        size_t ns = slots > w.counter_slots ? slots : w.counter_slots;
+        size_t np = partial_bytes > w.partial_bytes ? partial_bytes : w.partial_bytes;
         if (w.base != nullptr) {
-            // earlier launches on this stream may still use the old buffer
-            if (hipStreamSynchronize(stream) != hipSuccess) return GEMM_RELU_EHIP;
-            (void)hipFree(w.base);
-            w = Workspace{};
+            ns = ns > 2 * w.counter_slots ? ns : 2 * w.counter_slots;
+            np = np > 2 * w.partial_bytes ? np : 2 * w.partial_bytes;
         }
         char* p = nullptr;
         if (hipMalloc(reinterpret_cast<void**>(&p), counter_bytes(ns) + np) != hipSuccess) {
@@ -333,6 +338,9 @@ int get_workspace(int dev, hipStream_t stream, size_t slots, size_t partial_byte
             (void)hipFree(p);
             return GEMM_RELU_EHIP;
         }
+        // the old buffer stays allocated: earlier launches on this stream and
+        // graphs captured from them may still use it
+        if (w.base != nullptr) g_ws_retired.push_back(w.base);
         w.base = p;
         w.counter_slots = ns;
         w.partial_bytes = np;
@@ -416,9 +424,6 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B,
         if (rc != GEMM_RELU_OK) return rc;
     }
     if (M == 0 || N == 0) return GEMM_RELU_OK;
-    int dev = 0;
-    rc = check_device(dev);
-    if (rc != GEMM_RELU_OK) return rc;
 
     const bool vec = fast_path_ok(M, N, K, ta, tb, A, B, C);
     const int tile =
@@ -439,6 +444,10 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B,
     a.tiles_m = (int)((M + te.desc.bm - 1) / te.desc.bm);
     a.tiles_n = (int)((N + te.desc.bn - 1) / te.desc.bn);
     a.group_m = (opts && opts->group_m > 0) ? opts->group_m : te.desc.default_group_m;
+    // a group of more tile-rows than there are is the same order as one of
+    // all of them; clamping also keeps group_m * tiles_n within int32 in the
+    // kernels' block-order arithmetic
+    if (a.group_m > a.tiles_m) a.group_m = a.tiles_m;
     a.order = opts ? opts->block_order : GEMM_RELU_ORDER_DEFAULT;
     a.trans_a = ta ? 1 : 0;
     a.trans_b = tb ? 1 : 0;
@@ -453,11 +462,15 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B,
     if (splitk) {
         choose_splits(K, tiles, a.splits, a.kc);
         if (tiles * a.splits > INT32_MAX) return GEMM_RELU_EUNSUPPORTED;
-        if (a.splits > 1) {
-            rc = get_workspace(dev, s, (size_t)tiles, (size_t)a.splits * (size_t)M * (size_t)N * 4, &a.counters,
-                               &a.partial);
-            if (rc != GEMM_RELU_OK) return rc;
-        }
+    }
+    const size_t partial_bytes = (size_t)a.splits * (size_t)M * (size_t)N * 4;
+    const bool needs_scratch = splitk && a.splits > 1;
+    int dev = 0;
+    rc = check_device(dev);
+    if (rc != GEMM_RELU_OK) return rc;
+    if (needs_scratch) {
+        rc = get_workspace(dev, s, (size_t)tiles, partial_bytes, &a.counters, &a.partial);
+        if (rc != GEMM_RELU_OK) return rc;
     }
     const hipError_t e = (vec ? te.vec : te.generic)(a, s);
     return e == hipSuccess ? GEMM_RELU_OK : GEMM_RELU_EHIP;

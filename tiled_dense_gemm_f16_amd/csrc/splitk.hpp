@@ -275,6 +275,19 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
     // (vmcnt(0)), the workgroup meets, and only then one lane counts the
     // workgroup in. The last workgroup reads the partials with device-scope
     // atomic loads, all issued after it saw the final count.
+    // Why this order holds without release/acquire at device scope:
+    //  * hardware: a device-scope store is acknowledged (and vmcnt drops) only
+    //    once it is visible at the level the XCDs share, and device-scope
+    //    atomics and loads are performed at that level too. So when a
+    //    workgroup's count lands, all of its partials are already visible
+    //    there, and the last workgroup's loads, issued after its count
+    //    returned, read them from there;
+    //  * compiler: the relaxed stores may not sink below the empty asm with
+    //    a memory clobber that sits before the vmcnt(0) wait, and the wait
+    //    and the volatile asm keep their order; the barrier's
+    //    workgroup-scope fences keep the count after the wait, and the
+    //    last workgroup's loads after the barrier that publishes the count
+    //    (and they depend on it through the branch on last_flag).
     // partials travel as 8-byte device-scope atomics (pairs of fp32)
     auto pack = [](float lo, float hi) -> uint64_t {
         return (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
@@ -290,7 +303,9 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    wait_vmcnt<0>();  // this wave's partial stores are done
+    asm volatile("" ::: "memory");  // the stores above stay above the wait
+    wait_vmcnt<0>();                 // this wave's partial stores are acknowledged
+    asm volatile("" ::: "memory");
     __syncthreads();
     if (t == 0) {
         const uint32_t prev = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -13,10 +13,14 @@ gemm_relu_opts: the group size of the XCD-aware grouped block order, and the
 plain row-major order. The LDS budget is enforced when the library is
 compiled; it is checked again here against the device's LDS per workgroup.
 
-Each candidate's output is validated against a float64 product that torch
-computes on the same device, with the contract's bound |c - ref| <= 1e-2 +
-1e-2 |ref| (torch is only the checker here; the candidate's result is the
-library's). It is timed as replays of HIP graphs of `graph` launches that
+Each candidate's output is validated by a caller-supplied checker (`check`),
+which receives the candidate's C and the inputs as fp16 bit patterns on the
+host and returns the number of elements it rejects; the test suite passes
+one built on its independent CPU reference. Without a checker the candidates are only
+checked for agreement with the library's default launch, within the
+contract's bound |c - ref| <= 1e-2 + 1e-2 |ref| (numpy on the host): that
+catches a broken tile, not a fault every tile shares. The package itself
+computes no reference product. It is timed as replays of HIP graphs of `graph` launches that
 together cycle through copies of the inputs (at least `rotate_bytes` in all,
 at most MAX_COPIES copies), so inputs come from HBM rather than the
 last-level cache. The winners go into a
@@ -32,6 +36,8 @@ import argparse
 import json
 import os
 import sys
+
+import numpy as np
 
 from . import _binding as gr
 
@@ -65,7 +71,11 @@ def capture_rotation(call, copies: int, batch: int, stream) -> list:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for i in range(batch):
-                call((j * batch + i) % copies)
+                st = call((j * batch + i) % copies)
+                # a refused call records nothing: the graph would time an
+                # empty launch, so fail instead
+                if st is not None and st != gr.OK:
+                    raise RuntimeError(f"call refused while capturing a graph: {gr.strerror(st)}")
         graphs.append(g)
     return graphs
 
@@ -113,23 +123,39 @@ def _inputs(M, N, K, epilogue, seed, device, copies, trans_a=False, trans_b=Fals
     return a_s, b_s, bias
 
 
-def _reference(a, b, bias, epilogue, trans_a=False, trans_b=False):
+def _host_bits(t) -> np.ndarray:
+    """A device fp16 tensor's bit patterns, copied to the host."""
     import torch
 
-    r = (a.double().t() if trans_a else a.double()) @ (b.double().t() if trans_b else b.double())
-    if epilogue == "bias_gelu":
-        return torch.nn.functional.gelu(r + bias.double())
-    return torch.relu(r)
+    return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def agreement_check(ref_bits: np.ndarray):
+    """A checker that accepts outputs within 1e-2 + 1e-2 |ref| of `ref_bits`
+    (fp16 bit patterns) element by element."""
+    r = ref_bits.view(np.float16).astype(np.float64)
+
+    def check(c_bits: np.ndarray, *_inputs) -> int:
+        g = c_bits.view(np.float16).astype(np.float64)
+        return int((~(np.abs(g - r) <= 1e-2 + 1e-2 * np.abs(r))).sum())
+
+    return check
 
 
 def tune(M: int, N: int, K: int, *, epilogue: str = "relu", seed: int = 0, graph: int = 20,
          replays: int = 5, rotate_bytes: int = DEFAULT_ROTATE_BYTES, device: int = 0,
-         only: list[dict] | None = None, trans_a: bool = False, trans_b: bool = False) -> dict:
+         only: list[dict] | None = None, trans_a: bool = False, trans_b: bool = False,
+         check=None) -> dict:
     """Validates and times every candidate for (M, N, K) with the operand
     layouts trans_a / trans_b (A stored K x M, B stored N x K); returns
     {"shape", "epilogue", "layout", "arch", "results": [...] fastest first, "best"}.
     Candidates whose output fails validation or whose call fails are kept in
-    the results with "ok": False and never chosen."""
+    the results with "ok": False and never chosen.
+
+    check(c_bits, a_bits, b_bits, bias_bits) -> number of rejected elements,
+    all arguments fp16 bit patterns (numpy uint16) on the host, A and B in
+    their stored layouts, bias None for the ReLU epilogue. None: agreement
+    with the library's default launch (see the module docstring)."""
     import torch
 
     if epilogue not in ("relu", "bias_gelu"):
@@ -142,10 +168,24 @@ def tune(M: int, N: int, K: int, *, epilogue: str = "relu", seed: int = 0, graph
     cands = only if only is not None else candidates(M, N, K)
     with torch.cuda.device(dev):
         a_s, b_s, bias = _inputs(M, N, K, epilogue, seed, dev, copies, trans_a, trans_b)
-        ref = _reference(a_s[0], b_s[0], bias, epilogue, trans_a, trans_b)
-        bound = 1e-2 + 1e-2 * ref.abs()
         c = torch.empty((M, N), dtype=torch.float16, device=dev)
         stream = torch.cuda.Stream(dev)
+        host_in = (_host_bits(a_s[0]), _host_bits(b_s[0]), None if bias is None else _host_bits(bias))
+        if check is None:
+            # the library's default launch is the reference of the others
+            def default_call():
+                if epilogue == "bias_gelu":
+                    return gr.gemm_bias_gelu_f16_op(M, N, K, a_s[0].data_ptr(), int(trans_a), b_s[0].data_ptr(),
+                                                    int(trans_b), bias.data_ptr(), c.data_ptr(), stream.cuda_stream,
+                                                    None)
+                return gr.gemm_relu_f16_op(M, N, K, a_s[0].data_ptr(), int(trans_a), b_s[0].data_ptr(),
+                                           int(trans_b), c.data_ptr(), stream.cuda_stream, None)
+            with torch.cuda.stream(stream):
+                st = default_call()
+                stream.synchronize()
+            if st != gr.OK:
+                raise RuntimeError(f"the default launch failed: {gr.strerror(st)}")
+            check = agreement_check(_host_bits(c))
         results = []
         for cand in cands:
             opts = gr.make_opts(cand["tile"], cand["block_order"], cand["group_m"])
@@ -167,9 +207,7 @@ def tune(M: int, N: int, K: int, *, epilogue: str = "relu", seed: int = 0, graph
                 if st != gr.OK:
                     results.append(dict(res, ok=False, error=gr.strerror(st)))
                     continue
-                err = (c.double() - ref).abs()
-                bad = int((~(err <= bound)).sum())
-                res["max_abs_err"] = float(err.max()) if err.numel() else 0.0
+                bad = int(check(_host_bits(c), *host_in))
                 res["violations"] = bad
                 if bad:
                     results.append(dict(res, ok=False, error=f"{bad} elements outside 1e-2 + 1e-2|ref|"))
