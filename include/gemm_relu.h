@@ -68,7 +68,10 @@ typedef enum gemm_relu_status {
     /* the HIP runtime reported an error (no device, launch failure) */
     GEMM_RELU_EHIP = 3,
     /* a library-owned workspace could not be allocated */
-    GEMM_RELU_ENOMEM = 4
+    GEMM_RELU_ENOMEM = 4,
+    /* gemm_relu_f16_noalloc only: the launch needs more scratch than the
+       library's fixed array holds (see GEMM_RELU_NOALLOC_MAX_*) */
+    GEMM_RELU_ETOOBIG = 5
 } gemm_relu_status;
 
 /* Pass as gemm_relu_opts.tile to let the library choose. */
@@ -101,6 +104,31 @@ typedef struct gemm_relu_opts {
  */
 int gemm_relu_f16(int64_t M, int64_t N, int64_t K,
                   const void* A, const void* B, void* C, void* stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * operation, arguments, layout, ownership and errors as gemm_relu_f16, and
+ * the same kernels and results, but the call allocates nothing (no hipMalloc,
+ * no hipFree, no memset): where gemm_relu_f16 would use its per-stream
+ * split-K workspace, this entry point uses a fixed array that the library
+ * holds on each GPU until the process ends, of
+ *     GEMM_RELU_NOALLOC_MAX_TILES x 4 bytes of counters plus
+ *     GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES of fp32 partial sums.
+ * A split-K launch (M <= 64) over more output tiles of its split-K tile (16,
+ * 32 or 64 rows x 128 columns) than GEMM_RELU_NOALLOC_MAX_TILES, or with
+ * more partial sums than GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES (splits x M x
+ * N x 4 bytes), is refused with GEMM_RELU_ETOOBIG before any HIP call; other
+ * shapes need no scratch and have no such limit. Every call on one GPU shares
+ * that GPU's array: calls that may run at the same time on one GPU (on
+ * different streams, or from several host threads) race on it and must be
+ * ordered by the caller. The first call on a GPU enqueues one extra small
+ * kernel that clears the counters; each launch leaves them at zero.
+ */
+#define GEMM_RELU_NOALLOC_MAX_TILES 4096
+#define GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES (8 * 1024 * 1024)
+int gemm_relu_f16_noalloc(int64_t M, int64_t N, int64_t K,
+                          const void* A, const void* B, void* C, void* stream);
 
 /* Same as gemm_relu_f16; opts (may be NULL) pins the tile and block order. */
 int gemm_relu_f16_ex(int64_t M, int64_t N, int64_t K,

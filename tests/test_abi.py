@@ -336,3 +336,27 @@ def test_product_path_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
 
+
+def test_noalloc_refuses_oversized_scratch_before_any_hip_call():
+    # 64 rows over 129 tiles of 64 x 128: 2 splits, 8.06 MiB of partial sums,
+    # more than the fixed array holds; refused before the device is touched
+    F = 1 << 32  # never dereferenced
+    assert gr.tile_name(gr.select_tile(64, 16512, 8192)).startswith("splitk_64x128")
+    assert gr.gemm_relu_f16_noalloc(64, 16512, 8192, F, 2 * F, 3 * F, 0) == gr.ETOOBIG
+    assert "scratch" in gr.strerror(gr.ETOOBIG)
+    # the same argument checks as gemm_relu_f16
+    assert gr.gemm_relu_f16_noalloc(-1, 8, 8, F, 2 * F, 3 * F, 0) == gr.EINVAL
+    assert gr.gemm_relu_f16_noalloc(8, 8, 8, 0, 2 * F, 3 * F, 0) == gr.EINVAL
+    assert gr.gemm_relu_f16_noalloc(8, 8, 8, F + 1, 2 * F, 3 * F, 0) == gr.EUNSUPPORTED
+    assert gr.gemm_relu_f16_noalloc(8, 8, 8, F, 2 * F, F, 0) == gr.EINVAL   # C overlaps A
+    assert gr.gemm_relu_f16_noalloc(0, 8, 0, 0, 0, 0, 0) == gr.OK          # empty: no launch
+
+
+def test_noalloc_scratch_is_a_fixed_device_array():
+    # the array lives in the code object (a device symbol), not in a
+    # runtime allocation
+    out = subprocess.run(["nm", "-C", gr.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert any("scratch" in line for line in out.splitlines())
+    src = open(os.path.join(os.path.dirname(gr.LIB_PATH), "csrc", "gemm_relu.hip")).read()
+    assert "static __device__ __align__(256) char scratch[" in src
+    assert "hipGetSymbolAddress" in src

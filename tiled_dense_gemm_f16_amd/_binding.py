@@ -13,7 +13,9 @@ import threading
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgemm_relu.so")
 
-OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, 1, 2, 3, 4
+OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM, ETOOBIG = 0, 1, 2, 3, 4, 5
+NOALLOC_MAX_TILES = 4096                      # GEMM_RELU_NOALLOC_MAX_TILES
+NOALLOC_MAX_PARTIAL_BYTES = 8 * 1024 * 1024   # GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES
 TILE_AUTO = -1
 OP_N, OP_T = 0, 1  # operand as stored / stored transposed
 ORDER_DEFAULT, ORDER_ROW_MAJOR = 0, 1
@@ -47,7 +49,7 @@ class TileDesc(ctypes.Structure):
 _lock = threading.Lock()
 _lib = None
 
-EXPORTED = ("gemm_relu_f16", "gemm_relu_f16_ex", "gemm_relu_f16_op", "gemm_bias_gelu_f16",
+EXPORTED = ("gemm_relu_f16", "gemm_relu_f16_noalloc", "gemm_relu_f16_ex", "gemm_relu_f16_op", "gemm_bias_gelu_f16",
             "gemm_bias_gelu_f16_ex", "gemm_bias_gelu_f16_op", "gemm_relu_strerror", "gemm_relu_tile_count",
             "gemm_relu_tile_name", "gemm_relu_tile_info", "gemm_relu_select_tile", "gemm_relu_select_tile_op",
             "softmax_rows_f16", "flash_attn_fwd_f16")
@@ -66,6 +68,8 @@ def load():
         i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         lib.gemm_relu_f16.argtypes = [i64, i64, i64, p, p, p, p]
         lib.gemm_relu_f16.restype = i32
+        lib.gemm_relu_f16_noalloc.argtypes = [i64, i64, i64, p, p, p, p]
+        lib.gemm_relu_f16_noalloc.restype = i32
         lib.gemm_relu_f16_ex.argtypes = [i64, i64, i64, p, p, p, p, ctypes.POINTER(Opts)]
         lib.gemm_relu_f16_ex.restype = i32
         lib.gemm_bias_gelu_f16.argtypes = [i64, i64, i64, p, p, p, p, p]
@@ -116,6 +120,13 @@ def make_opts(tile: int | None = None, block_order: int = ORDER_DEFAULT, group_m
 def gemm_relu_f16(M: int, N: int, K: int, A: int, B: int, C: int, stream: int = 0) -> int:
     """Raw C-ABI call with integer device pointers; returns the status code."""
     return load().gemm_relu_f16(M, N, K, A or None, B or None, C or None, stream or None)
+
+
+def gemm_relu_f16_noalloc(M: int, N: int, K: int, A: int, B: int, C: int, stream: int = 0) -> int:
+    """Raw C-ABI call of the allocation-free variant of gemm_relu_f16 (its
+    split-K scratch is the library's fixed per-GPU array); returns the status
+    code."""
+    return load().gemm_relu_f16_noalloc(M, N, K, A or None, B or None, C or None, stream or None)
 
 
 def gemm_relu_f16_ex(M: int, N: int, K: int, A: int, B: int, C: int, stream: int = 0,

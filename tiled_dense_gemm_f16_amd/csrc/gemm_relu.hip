@@ -409,10 +409,63 @@ int check_device(int& dev)
     return g_dev_ok[dev] == 1 ? GEMM_RELU_OK : GEMM_RELU_EUNSUPPORTED;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: one array per GPU, in the
+// library's code object, holding the split-K counters and partial sums that
+// the per-stream workspaces hold for the other entry points. Its host-side
+// name is only a stand-in for the device symbol: host code uses the device
+// address that hipGetSymbolAddress returns for the current device, resolved
+// once per device.
+// ---------------------------------------------------------------------------
+
+constexpr size_t kStaticCounterSlots = GEMM_RELU_NOALLOC_MAX_TILES;
+constexpr size_t kStaticPartialBytes = GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES;
+static_assert(kStaticCounterSlots * 4 % 256 == 0, "the partial sums start 256-byte aligned");
+static __device__ __align__(256) char scratch[kStaticCounterSlots * 4 + kStaticPartialBytes];
+
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device (null until resolved)
+
+__global__ void zero_words(uint32_t* p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// The current device's scratch: counters first, then the partial sums. The
+// first call on a device resolves the address and clears the counters with a
+// kernel on `stream` (the array is zero when the code object loads; a kernel
+// rather than a memset, so that a stream under graph capture may make the
+// first call). Every split-K launch leaves the counters it used at zero.
+int static_scratch(int dev, hipStream_t stream, uint32_t** counters, float** partial)
+{
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return GEMM_RELU_EHIP;
+        }
+        hipLaunchKernelGGL(zero_words, dim3((unsigned)((kStaticCounterSlots + 255) / 256)), dim3(256), 0, stream,
+                           static_cast<uint32_t*>(p), (int)kStaticCounterSlots);
+        if (hipGetLastError() != hipSuccess) return GEMM_RELU_EHIP;
+        g_scratch_ptr[dev] = static_cast<char*>(p);
+    }
+    *counters = reinterpret_cast<uint32_t*>(g_scratch_ptr[dev]);
+    *partial = reinterpret_cast<float*>(g_scratch_ptr[dev] + kStaticCounterSlots * 4);
+    return GEMM_RELU_OK;
+}
+
+// Where a split-K launch keeps its partial sums and counters.
+enum class Scratch {
+    kStreamWorkspace,  // the library-allocated per-(device, stream) workspace
+    kStatic,           // the fixed per-device array above (allocates nothing)
+};
+
 // Validated call -> tile choice, split-K workspace, launch. `act` selects the
 // epilogue (kActRelu, or kActBiasGelu with `bias`).
 int run(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B, int op_b, void* C, void* stream,
-        const gemm_relu_opts* opts, int act, const void* bias)
+        const gemm_relu_opts* opts, int act, const void* bias, Scratch where = Scratch::kStreamWorkspace)
 {
     if ((op_a != GEMM_RELU_OP_N && op_a != GEMM_RELU_OP_T) || (op_b != GEMM_RELU_OP_N && op_b != GEMM_RELU_OP_T))
         return GEMM_RELU_EINVAL;
@@ -465,11 +518,15 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B,
     }
     const size_t partial_bytes = (size_t)a.splits * (size_t)M * (size_t)N * 4;
     const bool needs_scratch = splitk && a.splits > 1;
+    if (needs_scratch && where == Scratch::kStatic &&
+        ((size_t)tiles > kStaticCounterSlots || partial_bytes > kStaticPartialBytes))
+        return GEMM_RELU_ETOOBIG;
     int dev = 0;
     rc = check_device(dev);
     if (rc != GEMM_RELU_OK) return rc;
     if (needs_scratch) {
-        rc = get_workspace(dev, s, (size_t)tiles, partial_bytes, &a.counters, &a.partial);
+        rc = where == Scratch::kStatic ? static_scratch(dev, s, &a.counters, &a.partial)
+                                       : get_workspace(dev, s, (size_t)tiles, partial_bytes, &a.counters, &a.partial);
         if (rc != GEMM_RELU_OK) return rc;
     }
     const hipError_t e = (vec ? te.vec : te.generic)(a, s);
@@ -488,6 +545,9 @@ const char* gemm_relu_strerror(int status)
     case GEMM_RELU_EUNSUPPORTED: return "unsupported (size above INT32_MAX, misaligned pointer, device not gfx950, or unknown tile)";
     case GEMM_RELU_EHIP: return "HIP runtime error";
     case GEMM_RELU_ENOMEM: return "workspace allocation failed";
+    case GEMM_RELU_ETOOBIG:
+        return "the split-K launch needs more scratch than the allocation-free entry point holds "
+               "(more than GEMM_RELU_NOALLOC_MAX_TILES output tiles or GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES of partial sums)";
     default: return "unknown status";
     }
 }
@@ -531,6 +591,12 @@ int gemm_relu_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, const void*
 int gemm_relu_f16(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, void* stream)
 {
     return run(M, N, K, A, GEMM_RELU_OP_N, B, GEMM_RELU_OP_N, C, stream, nullptr, gemm_relu::kActRelu, nullptr);
+}
+
+int gemm_relu_f16_noalloc(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, void* stream)
+{
+    return run(M, N, K, A, GEMM_RELU_OP_N, B, GEMM_RELU_OP_N, C, stream, nullptr, gemm_relu::kActRelu, nullptr,
+               Scratch::kStatic);
 }
 
 int gemm_relu_f16_op(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B, int op_b, void* C,
