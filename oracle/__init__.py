@@ -29,18 +29,23 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gemm_relu_oracle.c")
 _SRCS = [_SRC, os.path.join(_HERE, "attention_oracle.c")]
-_LIB = os.path.join(_HERE, "liboracle_gemm_relu.so")
+# ORACLE_SANITIZE=1 selects the build with gcc's AddressSanitizer and
+# UndefinedBehaviorSanitizer (the process must preload gcc's libasan)
+_SANITIZE = os.environ.get("ORACLE_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "liboracle_gemm_relu_asan.so" if _SANITIZE else "liboracle_gemm_relu.so")
 _lock = threading.Lock()
 _lib = None
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 
 
 def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP, no fast-math). Returns the .so path."""
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math; with the
+    sanitizers when ORACLE_SANITIZE=1). Returns the .so path."""
     if not force and os.path.exists(_LIB) and all(os.path.getmtime(_LIB) >= os.path.getmtime(f) for f in _SRCS):
         return _LIB
     tmp = _LIB + f".tmp{os.getpid()}"
     cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-fno-fast-math", "-ffp-contract=off", *_SRCS, "-o", tmp, "-lm"]
+           "-fno-fast-math", "-ffp-contract=off", *(SANITIZE_FLAGS if _SANITIZE else []), *_SRCS, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB

@@ -11,7 +11,9 @@ import os
 import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libgemm_relu.so")
+# GEMM_RELU_LIB selects another build of the same library (the host-sanitized
+# one, for the CPU checks); the default is the in-tree build
+LIB_PATH = os.environ.get("GEMM_RELU_LIB") or os.path.join(PKG, "libgemm_relu.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM, ETOOBIG = 0, 1, 2, 3, 4, 5
 NOALLOC_MAX_TILES = 4096                      # GEMM_RELU_NOALLOC_MAX_TILES

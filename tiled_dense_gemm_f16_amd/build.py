@@ -34,10 +34,39 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str | None = None) -> str:
-    """Compile the HIP library. Always compiles (no staleness shortcut)."""
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the library's
+# argument checking, tile choice and workspace code (each -fsanitize= applies
+# to the host pass only; GPU code is built as usual). The result needs the
+# compiler's ASan runtime preloaded into the process (asan_runtime()).
+SANITIZE_FLAGS = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-g",
+]
+SANITIZED_LIB = os.path.join(PKG, "libgemm_relu_asan.so")
+
+
+def asan_runtime() -> str:
+    """The shared ASan runtime of the compiler that builds the library."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    out = subprocess.run([os.path.join(rocm, "llvm", "bin", "clang"), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True, check=True).stdout.strip()
+    if not os.path.isabs(out) or not os.path.exists(out):
+        raise RuntimeError("the compiler's ASan runtime was not found")
+    return out
+
+
+def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str | None = None,
+          sanitize: bool = False) -> str:
+    """Compile the HIP library. Always compiles (no staleness shortcut).
+    sanitize=True builds SANITIZED_LIB with SANITIZE_FLAGS instead."""
     import concurrent.futures
 
+    if sanitize:
+        extra_flags = [*(extra_flags or []), *SANITIZE_FLAGS]
+        out = out or SANITIZED_LIB
     out = out or LIB
     tag = f".tmp{os.getpid()}"
     objs = [out + f".{os.path.splitext(os.path.basename(src))[0]}{tag}.o" for src in SRCS]
@@ -57,7 +86,8 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
                 sys.stderr.write(res.stdout + res.stderr)
                 raise RuntimeError(f"hipcc failed ({res.returncode}) compiling {src}")
         tmp = out + tag
-        res = run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+        link_flags = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"] if sanitize else []
+        res = run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_flags, *objs, "-o", tmp])
         if res.returncode != 0:
             sys.stderr.write(res.stdout + res.stderr)
             raise RuntimeError(f"hipcc failed ({res.returncode}) linking {out}")
@@ -70,4 +100,4 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:]))
