@@ -64,7 +64,8 @@ def kernel_sources(tile: str) -> list[str]:
     if tile.startswith(("attn", "softmax")):
         family = "attention.hpp"
     else:
-        family = "pipelined.hpp" if "lds-dma" in tile else "splitk.hpp" if "splitk" in tile else "staged.hpp"
+        family = ("small.hpp" if "lds-small" in tile else "pipelined.hpp" if "lds-dma" in tile
+                  else "splitk.hpp" if "splitk" in tile else "staged.hpp")
     return [os.path.join(CSRC, "common.hpp"), os.path.join(CSRC, family)]
 
 

@@ -115,18 +115,19 @@ int gemm_relu_f16(int64_t M, int64_t N, int64_t K,
  * holds on each GPU until the process ends, of
  *     GEMM_RELU_NOALLOC_MAX_TILES x 4 bytes of counters plus
  *     GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES of fp32 partial sums.
- * A split-K launch (M <= 64) over more output tiles of its split-K tile (16,
- * 32 or 64 rows x 128 columns) than GEMM_RELU_NOALLOC_MAX_TILES, or with
- * more partial sums than GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES (splits x M x
- * N x 4 bytes), is refused with GEMM_RELU_ETOOBIG before any HIP call; other
- * shapes need no scratch and have no such limit. Every call on one GPU shares
+ * A launch that splits K across workgroups (few rows, or few output tiles
+ * of the split-K tiles of 16, 32 or 64 rows x 128 columns) over more output
+ * tiles than GEMM_RELU_NOALLOC_MAX_TILES, or with more partial sums than
+ * GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES (splits x M x N x 4 bytes), is refused
+ * with GEMM_RELU_ETOOBIG before any HIP call; other shapes need no scratch
+ * and have no such limit. Every call on one GPU shares
  * that GPU's array: calls that may run at the same time on one GPU (on
  * different streams, or from several host threads) race on it and must be
  * ordered by the caller. The first call on a GPU enqueues one extra small
  * kernel that clears the counters; each launch leaves them at zero.
  */
 #define GEMM_RELU_NOALLOC_MAX_TILES 4096
-#define GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES (8 * 1024 * 1024)
+#define GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES (4 * 1024 * 1024)
 int gemm_relu_f16_noalloc(int64_t M, int64_t N, int64_t K,
                           const void* A, const void* B, void* C, void* stream);
 
@@ -173,6 +174,8 @@ const char* gemm_relu_tile_name(int tile);
 #define GEMM_RELU_FAMILY_PIPELINED 0 /* direct-to-LDS loads into a ring of LDS stages */
 #define GEMM_RELU_FAMILY_STAGED 1    /* loads through registers into a double-buffered LDS tile */
 #define GEMM_RELU_FAMILY_SPLITK 2    /* waves and workgroups split K; fp32 partials are summed */
+#define GEMM_RELU_FAMILY_SMALL 3     /* direct-to-LDS loads of whole rows into a ring, small tiles
+                                        (operands as stored; transposed ones run the staged kernel) */
 
 /*
  * The launch parameters of one compiled tile: the search space of an offline

@@ -77,14 +77,19 @@ def test_tile_selection_is_host_only():
     assert gr.select_tile(4096, 4096, 4096) == 0
     assert name(16, 8192, 8192).startswith("splitk_16x")
     assert name(1, 8192, 8192).startswith("splitk_16x")
-    assert name(4096, 64, 4096).startswith("splitk_16x")  # narrow: 256 tiles of 16x128
+    assert name(4096, 64, 4096).startswith("32x64x64s4_w1x2")  # narrow: 128 tiles of 32x64
+    assert name(32, 8192, 8192).startswith("splitk_16x")     # few rows: split-K only
+    assert name(64, 8192, 8192).startswith("32x64x64s4_w1x2")
     assert gr.select_tile(3072, 3072, 3072) == 0  # 144 tiles of 256x256
     assert name(2560, 2560, 2560).startswith("128x256")  # 200 tiles
     assert name(2048, 2048, 2048).startswith("64x256")  # 256 tiles
-    assert name(1024, 1024, 1024).startswith("splitk_32x")  # 256 tiles of 32x128
+    assert name(1024, 1024, 1024).startswith("64x64x64s4_w2x2_mfma32x32x16_lds-small")  # 256 tiles of 64x64
+    assert name(1536, 1536, 1536).startswith("64x64x64s4_w2x2_mfma32x32x16_lds-small")  # 2.25 per compute unit
+    # rows of A and B that are not whole 128-byte lines cost the small tiles more L2 requests
     assert name(1000, 1016, 1000).startswith("splitk_32x")
     assert name(512, 4096, 8192).startswith("splitk_64x")  # 256 tiles of 64x128
-    assert name(256, 256, 256).startswith("16x64")  # latency-bound
+    assert name(256, 256, 256).startswith("32x64x64s4_w1x2")  # latency-bound: the most workgroups
+    assert name(512, 512, 512).startswith("32x64x64s4_w1x2")
     # transposed layouts have their own rates: with A stored K x M the split-K
     # tiles (element-wise A reads) lose to the pipelined ones at mid sizes
     tname = lambda *s, **kw: gr.tile_name(gr.select_tile(*s, **kw))  # noqa: E731
@@ -113,9 +118,10 @@ def test_tile_info_describes_every_tile():
         assert d["lds_bytes"] <= 160 * 1024, name
         assert d["threads"] == 64 * d["waves_m"] * d["waves_n"] * d["waves_k"], name
         assert f"{d['bm']}x{d['bn']}" in name, name
-        assert d["family"] in (gr.FAMILY_PIPELINED, gr.FAMILY_STAGED, gr.FAMILY_SPLITK)
+        assert d["family"] in (gr.FAMILY_PIPELINED, gr.FAMILY_STAGED, gr.FAMILY_SPLITK, gr.FAMILY_SMALL)
         assert bool(d["split_k"]) == ("splitk" in name) == (d["family"] == gr.FAMILY_SPLITK), name
-        if d["family"] == gr.FAMILY_PIPELINED:
+        assert ("lds-small" in name) == (d["family"] == gr.FAMILY_SMALL), name
+        if d["family"] in (gr.FAMILY_PIPELINED, gr.FAMILY_SMALL):
             assert f"x{d['bk']}s{d['stages']}_w{d['waves_m']}x{d['waves_n']}" in name, name
             assert d["lds_bytes"] == d["stages"] * (d["bm"] + d["bn"]) * d["bk"] * 2, name
         elif d["family"] == gr.FAMILY_STAGED:
@@ -338,11 +344,12 @@ def test_product_path_never_imports_the_oracle():
 
 
 def test_noalloc_refuses_oversized_scratch_before_any_hip_call():
-    # 64 rows over 129 tiles of 64 x 128: 2 splits, 8.06 MiB of partial sums,
+    # 32 rows over 65 tiles of 32 x 128: 4 splits, 4.06 MiB of partial sums,
     # more than the fixed array holds; refused before the device is touched
     F = 1 << 32  # never dereferenced
-    assert gr.tile_name(gr.select_tile(64, 16512, 8192)).startswith("splitk_64x128")
-    assert gr.gemm_relu_f16_noalloc(64, 16512, 8192, F, 2 * F, 3 * F, 0) == gr.ETOOBIG
+    assert gr.tile_name(gr.select_tile(32, 8320, 8192)).startswith("splitk_32x128")
+    assert 4 * 32 * 8320 * 4 > gr.NOALLOC_MAX_PARTIAL_BYTES
+    assert gr.gemm_relu_f16_noalloc(32, 8320, 8192, F, 2 * F, 3 * F, 0) == gr.ETOOBIG
     assert "scratch" in gr.strerror(gr.ETOOBIG)
     # the same argument checks as gemm_relu_f16
     assert gr.gemm_relu_f16_noalloc(-1, 8, 8, F, 2 * F, 3 * F, 0) == gr.EINVAL

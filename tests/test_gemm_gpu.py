@@ -426,7 +426,7 @@ def test_workspace_growth_keeps_captured_graphs_valid():
     # graph's replays must still find their partial sums and counters where
     # they were (the replaced workspace is kept, not freed)
     Ms, Ns, Ks = 16, 512, 4096      # 4 tiles of 16 x 128 -> 32 splits, 1 MiB of partials
-    Ml, Nl, Kl = 64, 4096, 4096     # larger: 128 tiles of 16 x 128 -> 2 splits, 2 MiB of partials
+    Ml, Nl, Kl = 32, 4096, 4096     # larger: 64 tiles of 16 x 128 -> 4 splits, 2 MiB of partials
     a, b = workloads.make_inputs(Ms, Ns, Ks, dist="intsmall", seed=81)
     al, bl = workloads.make_inputs(Ml, Nl, Kl, dist="intsmall", seed=82)
     want = oracle.gemm_relu_f16(workloads.as_u16(a), workloads.as_u16(b))

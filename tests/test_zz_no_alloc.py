@@ -45,7 +45,7 @@ def call_both(a, b, stream=None):
 
 @pytest.mark.parametrize("first,second", [
     ((16, 8192, 8192), (16, 2048, 4096)),     # split-K with 4, then 16 splits
-    ((64, 4096, 4096), (32, 1024, 2048)),     # 128 tiles, 2 splits; then 32 tiles, 8 splits
+    ((24, 4096, 4096), (32, 1024, 2048)),     # 64 tiles, 4 splits; then 16 tiles, 16 splits
     ((1000, 1016, 1000), (16, 8192, 1024)),   # no scratch, then split-K
 ])
 def test_two_calls_in_a_row_match_gemm_relu_f16(first, second):
@@ -98,9 +98,10 @@ def test_captured_calls_replay_correctly():
 
 
 def test_too_large_for_the_scratch_is_refused():
-    # 64 rows, 129 tiles of 64 x 128: 2 splits, 8.06 MiB of partial sums
-    M, N, K = 64, 16512, 8192
-    assert 2 * M * N * 4 > gr.NOALLOC_MAX_PARTIAL_BYTES
+    # 32 rows, 65 tiles of 32 x 128: 4 splits, 4.06 MiB of partial sums
+    M, N, K = 32, 8320, 8192
+    assert gr.tile_name(gr.select_tile(M, N, K)).startswith("splitk_32x128")
+    assert 4 * M * N * 4 > gr.NOALLOC_MAX_PARTIAL_BYTES
     a = torch.zeros((M, K), dtype=torch.float16, device="cuda")
     b = torch.zeros((K, N), dtype=torch.float16, device="cuda")
     c = torch.full((M, N), 9.0, dtype=torch.float16, device="cuda")
@@ -108,8 +109,10 @@ def test_too_large_for_the_scratch_is_refused():
     torch.cuda.synchronize()
     assert st == gr.ETOOBIG
     assert bool((c == 9.0).all())   # nothing was launched
-    # the array is still usable after a refusal
-    M, N, K = 16, 8192, 8192
+    # the array is still usable after a refusal (32 x 8192 x 8192: 128 tiles
+    # of 16 x 128, 2 splits, 2 MiB of partial sums)
+    M, N, K = 32, 8192, 8192
+    assert "splitk" in gr.tile_name(gr.select_tile(M, N, K))
     w = workloads.Workload("noalloc_after_refusal", M, N, K, "normal", 0.02, 96)
     a, b = workloads.workload_inputs(w)
     got, ref = call_both(a.cuda(), b.cuda())

@@ -17,7 +17,7 @@ LIB_PATH = os.environ.get("GEMM_RELU_LIB") or os.path.join(PKG, "libgemm_relu.so
 
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM, ETOOBIG = 0, 1, 2, 3, 4, 5
 NOALLOC_MAX_TILES = 4096                      # GEMM_RELU_NOALLOC_MAX_TILES
-NOALLOC_MAX_PARTIAL_BYTES = 8 * 1024 * 1024   # GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES
+NOALLOC_MAX_PARTIAL_BYTES = 4 * 1024 * 1024   # GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES
 TILE_AUTO = -1
 OP_N, OP_T = 0, 1  # operand as stored / stored transposed
 ORDER_DEFAULT, ORDER_ROW_MAJOR = 0, 1
@@ -34,7 +34,7 @@ class Opts(ctypes.Structure):
                 ("group_m", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
-FAMILY_PIPELINED, FAMILY_STAGED, FAMILY_SPLITK = 0, 1, 2
+FAMILY_PIPELINED, FAMILY_STAGED, FAMILY_SPLITK, FAMILY_SMALL = 0, 1, 2, 3
 
 
 class TileDesc(ctypes.Structure):

@@ -17,6 +17,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <cmath>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -24,6 +25,7 @@
 
 #include "gemm_relu.h"
 #include "pipelined.hpp"
+#include "small.hpp"
 #include "splitk.hpp"
 #include "staged.hpp"
 
@@ -40,6 +42,8 @@ using P256W8 = gemm_relu::pipelined::Cfg<256, 256, 4, 2>; // 8 waves x 64x128: t
 using P256S5 = gemm_relu::pipelined::Cfg<256, 256, 2, 2, 5>; // five-slot ring: 4 steps in flight
 using P128 = gemm_relu::pipelined::Cfg<128, 256, 2, 2>;      // 4 waves x 64x128
 using P64 = gemm_relu::pipelined::Cfg<64, 256, 1, 2>;        // 2 waves x 64x128
+using Q64 = gemm_relu::small::Cfg<64, 64, 2, 2, 2, 4>;     // 4 waves x 32x32, 64-deep steps, 4 slots
+using Q32 = gemm_relu::small::Cfg<32, 64, 1, 2, 2, 4>;     // 2 waves x 32x32, 64-deep steps, 4 slots
 using S256 = gemm_relu::staged::Tile<256, 256, 64, 2, 2>;  // generic instance of the same tile
 using S128 = gemm_relu::staged::Tile<128, 128, 64, 2, 2, 1, 3>;  // the pages' 128x128x64 tile
 using S64 = gemm_relu::staged::Tile<64, 64, 64, 2, 2, 1, 4>;      // 4 waves x 32x32
@@ -104,6 +108,20 @@ hipError_t launch_pipelined(const Args& a, hipStream_t s)
     return hipGetLastError();
 }
 
+// The small-tile kernel covers operands as stored (NN); with a transposed
+// operand the register-staged kernel of the same tile size runs instead.
+template <class T, class Fallback>
+hipError_t launch_small(const Args& a, hipStream_t s)
+{
+    if (a.trans_a || a.trans_b) return launch_staged<Fallback, true>(a, s);
+    const int blocks = a.tiles_m * a.tiles_n;
+    if (a.K % T::BK == 0)
+        hipLaunchKernelGGL((gemm_relu::small::small_kernel<T, true>), dim3(blocks), dim3(T::NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((gemm_relu::small::small_kernel<T, false>), dim3(blocks), dim3(T::NT), 0, s, a);
+    return hipGetLastError();
+}
+
 template <class T, bool TA, bool TB>
 void launch_splitk_as(const Args& a, hipStream_t s)
 {
@@ -129,6 +147,13 @@ constexpr gemm_relu_tile_desc pipelined_desc(int group_m)
 {
     return {T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, 1, T::NT, T::STAGES * T::STAGE_BYTES,
             0, group_m, GEMM_RELU_FAMILY_PIPELINED, {0, 0, 0, 0}};
+}
+
+template <class T>
+constexpr gemm_relu_tile_desc small_desc(int group_m)
+{
+    return {T::BM, T::BN, T::BK, T::STAGES, T::WAVES_M, T::WAVES_N, 1, T::NT, T::STAGES * T::SLOT * 2,
+            0, group_m, GEMM_RELU_FAMILY_SMALL, {0, 0, 0, 0}};
 }
 
 template <class T>
@@ -170,6 +195,10 @@ const TileEntry kTiles[] = {
     {"128x256x32s4_w2x2_mfma32x32x16_lds-dma", pipelined_desc<P128>(4), launch_pipelined<P128>,
      launch_staged<S128, false>},
     {"64x256x32s4_w1x2_mfma32x32x16_lds-dma", pipelined_desc<P64>(4), launch_pipelined<P64>,
+     launch_staged<S64, false>},
+    {"64x64x64s4_w2x2_mfma32x32x16_lds-small", small_desc<Q64>(4), launch_small<Q64, S64>,
+     launch_staged<S64, false>},
+    {"32x64x64s4_w1x2_mfma32x32x16_lds-small", small_desc<Q32>(4), launch_small<Q32, S64>,
      launch_staged<S64, false>},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
@@ -239,6 +268,29 @@ constexpr AutoTile kAutoTiles[] = {
     {2, {0.895, 1.24, 0.429, 0.756}},// 64x64 staged
     {3, {0.273, 0.706, 0.118, 0.262}},// 16x64 staged
 };
+// The small tiles (direct-to-LDS, NN only) on the problems they fill: their
+// time is a fixed part (first loads' latency, epilogue) plus the bytes each
+// compute unit loads at the rate this access pattern sustains per unit
+// (64 x 64 tiles: 4.7 us at 256^3, 9.1 us at 1024^3, 22.8 us at 1536^3). Rows
+// of A or B that are not whole 128-byte lines take more L2 requests (1000 x
+// 1016 x 1000: 13.6 us against 9.1 at 1024^3). The three constants were
+// chosen on a sweep of 46 shapes (every tile and block order, inputs from
+// HBM) for the choices they lead to against the other tiles' predictions:
+// the default launch is 1.023x the fastest on average, 1.135x at worst.
+struct SmallTile {
+    int id;
+};
+constexpr SmallTile kSmallTiles[] = {{11}, {12}};
+constexpr double kSmallFixedUs = 2.25;
+// The rate model below predicts times that are, over the sweep, about
+// 1.455 x + 4.0 us short of the measured ones (4096^3: 77 -> 116 us, 2048^3:
+// 20.9 -> 34.4 us, 1024^3 split-K: 5.3 -> 11.9 us); a small tile's time is
+// mapped into the same units before the two are compared.
+constexpr double kRateModelScale = 1.455;
+constexpr double kRateModelOffsetUs = 4.0;
+constexpr double kSmallBytesPerUsPerCu = 44.0e3;  // 44 GB/s
+constexpr double kSmallMisalignedRows = 0.40;     // extra per operand whose rows are not whole lines
+
 constexpr double kComputeUnits = 256.0;
 constexpr double kHbmBytesPerUs = 6.68e6;          // 6.68 TB/s
 constexpr double kStagedHbmShare = 0.75;           // the register-staged kernels reach less of it
@@ -264,13 +316,29 @@ Prediction predict(const AutoTile& at, int layout, int64_t M, int64_t N, int64_t
     return {(compute > memory ? compute : memory) + combine, compute};
 }
 
+// Predicted time of a small tile (operands as stored).
+double predict_small(const SmallTile& st, int64_t M, int64_t N, int64_t K)
+{
+    const gemm_relu_tile_desc& d = kTiles[st.id].desc;
+    const double wgs = (double)(((M + d.bm - 1) / d.bm) * ((N + d.bn - 1) / d.bn));
+    // bytes one compute unit loads: workgroups are handed out as units free
+    // up, so a unit's share is the average (at least one workgroup)
+    const double per_cu = wgs / kComputeUnits;
+    const double bytes = (per_cu > 1.0 ? per_cu : 1.0) * (double)(d.bm + d.bn) * (double)K * 2.0;
+    const double misaligned = 1.0 + ((K * 2) % 128 ? kSmallMisalignedRows : 0.0) + ((N * 2) % 128 ? kSmallMisalignedRows : 0.0);
+    return kSmallFixedUs + bytes * misaligned / kSmallBytesPerUsPerCu;
+}
+
 // The tile of least predicted time; among tiles bound by the same HBM time,
 // the one with the least compute (the fewest padded rows).
 int choose_tile(int64_t M, int64_t N, int64_t K, bool ta, bool tb)
 {
     const bool sk = splitk_ok(M, K);
-    const bool few_rows = M <= 64 && sk;
     const int layout = 2 * (ta ? 1 : 0) + (tb ? 1 : 0);
+    // few rows: only the split-K tiles (up to 64 rows with a transposed
+    // operand; with operands as stored the 32 x 64 small tile competes from
+    // 33 rows on)
+    const bool few_rows = M <= (layout == 0 ? 32 : 64) && sk;
     int best = -1;
     Prediction bp{0.0, 0.0};
     for (const AutoTile& at : kAutoTiles) {
@@ -282,6 +350,16 @@ int choose_tile(int64_t M, int64_t N, int64_t K, bool ta, bool tb)
         if (best < 0 || (tie ? p.compute < bp.compute : p.us < bp.us)) {
             best = at.id;
             bp = p;
+        }
+    }
+    // the small tiles: operands as stored, more than a few rows
+    if (layout == 0 && !few_rows) {
+        for (const SmallTile& st : kSmallTiles) {
+            const double us = (predict_small(st, M, N, K) - kRateModelOffsetUs) / kRateModelScale;
+            if (us < bp.us) {
+                best = st.id;
+                bp = {us, 0.0};
+            }
         }
     }
     return best;

@@ -245,7 +245,9 @@ def _default_of(M, N, K, results, trans_a=False, trans_b=False):
     auto = gr.select_tile(M, N, K, trans_a=trans_a, trans_b=trans_b)
     if auto < 0:
         return None
-    g = gr.tile_info(auto)["default_group_m"]
+    info = gr.tile_info(auto)
+    # the library clamps the group to the number of tile-rows
+    g = min(info["default_group_m"], -(-M // info["bm"]))
     for r in results:
         if r["tile"] == auto and r["block_order"] == gr.ORDER_DEFAULT and r["group_m"] in (0, g):
             return r
