@@ -367,3 +367,25 @@ def test_noalloc_scratch_is_a_fixed_device_array():
     src = open(os.path.join(os.path.dirname(gr.LIB_PATH), "csrc", "gemm_relu.hip")).read()
     assert "static __device__ __align__(256) char scratch[" in src
     assert "hipGetSymbolAddress" in src
+
+
+def test_ordinary_build_has_no_timestamp_hook():
+    # the per-workgroup timestamps exist only in the profiling build
+    out = subprocess.run(["nm", "-D", "--defined-only", gr.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    assert "gemm_relu_stamps_set" not in out
+
+
+def test_stamps_summary_on_synthetic_rows():
+    import numpy as np
+    from tiled_dense_gemm_f16_amd import stamps
+    # two dies, two workgroups each: start, first data, loop end, end (100 MHz ticks), -, die
+    rows = np.array([[1000, 1100, 1500, 1600, 0, 0, 0, 0],
+                     [1002, 1104, 1510, 1620, 0, 0, 0, 0],
+                     [1001, 1101, 1520, 1700, 0, 1, 0, 0],
+                     [1003, 1103, 1530, 1650, 0, 1, 0, 0],
+                     [0, 0, 0, 0, 0, 0, 0, 0]], dtype=np.int64)  # a row nothing wrote
+    s = stamps.summarise(rows)
+    assert s["workgroups"] == 4 and s["span_ns"] == 7000
+    assert s["first_data_after_start_ns"][0] == 1000 and s["main_loop_ns"][2] == 4270
+    assert [d["die"] for d in s["per_die"]] == [0, 1] and s["per_die"][1]["end_ns_max"] == 7000

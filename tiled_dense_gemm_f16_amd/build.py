@@ -46,6 +46,9 @@ SANITIZE_FLAGS = [
     "-Xarch_host", "-g",
 ]
 SANITIZED_LIB = os.path.join(PKG, "libgemm_relu_asan.so")
+# The timestamp build (GR_STAMPS): the same kernels with per-workgroup
+# timestamps at a few points (see common.hpp), for stamps.py.
+STAMPS_LIB = os.path.join(PKG, "libgemm_relu_stamps.so")
 
 
 def asan_runtime() -> str:
@@ -59,14 +62,18 @@ def asan_runtime() -> str:
 
 
 def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str | None = None,
-          sanitize: bool = False) -> str:
+          sanitize: bool = False, stamps: bool = False) -> str:
     """Compile the HIP library. Always compiles (no staleness shortcut).
-    sanitize=True builds SANITIZED_LIB with SANITIZE_FLAGS instead."""
+    sanitize=True builds SANITIZED_LIB with SANITIZE_FLAGS instead;
+    stamps=True builds STAMPS_LIB with per-workgroup timestamps."""
     import concurrent.futures
 
     if sanitize:
         extra_flags = [*(extra_flags or []), *SANITIZE_FLAGS]
         out = out or SANITIZED_LIB
+    if stamps:
+        extra_flags = [*(extra_flags or []), "-DGR_STAMPS"]
+        out = out or STAMPS_LIB
     out = out or LIB
     tag = f".tmp{os.getpid()}"
     objs = [out + f".{os.path.splitext(os.path.basename(src))[0]}{tag}.o" for src in SRCS]
@@ -100,4 +107,4 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
 
 
 if __name__ == "__main__":
-    print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:]))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:], stamps="--stamps" in sys.argv[1:]))

@@ -138,7 +138,8 @@ int flash_attn_fwd_f16(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
     if (a.scale_log2 == 0.0f) a.scale_log2 = 1e-30f;
     a.causal = causal;
     a.nqb = (int)nqb;
-    a.npair = (int)((nqb + 1) / 2);
+    a.paired = causal;
+    a.npair = (int)(causal ? (nqb + 1) / 2 : nqb);
     if (D == 64) launch_attn<64>(a, s);
     else launch_attn<128>(a, s);
     return hipGetLastError() == hipSuccess ? GEMM_RELU_OK : GEMM_RELU_EHIP;

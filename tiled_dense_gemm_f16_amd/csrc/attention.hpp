@@ -191,7 +191,8 @@ struct AttnArgs {
     float scale_log2;  // softmax scale * log2(e)
     int causal;
     int nqb;    // query tiles per (batch, head)
-    int npair;  // work items per (batch, head): (nqb + 1) / 2
+    int npair;  // work items per (batch, head): (nqb + 1) / 2 when paired, else nqb
+    int paired; // 1: an item runs two query tiles (causal); 0: one
 };
 
 template <int D_, int NW_ = 8>
@@ -567,13 +568,16 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two 
     __shared__ __attribute__((aligned(1024))) uint16_t vs0[T::TILE_HALVES];
     __shared__ __attribute__((aligned(1024))) uint16_t vs1[T::TILE_HALVES];
 
-    // Work item -> (batch-head, pair of query tiles). Items are taken in
+    // Work item -> (batch-head, query tiles). Items are taken in
     // XCD-contiguous ranges (die b % 8 gets one run of them), and a head's
     // items sit next to each other so they share its K and V in the die's L2.
-    // Item i of a head runs query tile nqb-1-i and then tile i: under the
-    // causal mask the two together see the same number of key tiles for
-    // every i, so all workgroups carry equal work (the middle tile of an odd
-    // count runs alone).
+    // Causal: item i of a head runs query tile nqb-1-i and then tile i; the
+    // two together see the same number of key tiles for every i, so all
+    // workgroups carry equal work (the middle tile of an odd count runs
+    // alone). Without the mask every tile sees every key, and item i runs
+    // tile i alone: a die's resident workgroups then cover two heads, whose
+    // K and V (2 MiB each at 4096 x 128) its 4 MiB L2 holds while the
+    // workgroups walk them in step, instead of four heads walked twice.
     int w = blockIdx.x;
     {
         const int nblk = gridDim.x, q = nblk / 8, r = nblk % 8;
@@ -581,6 +585,10 @@ __global__ void __launch_bounds__(T::NT, 2) attn_fwd_kernel(AttnArgs p)  // two 
         w = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
     }
     const int bh = w / p.npair, i = w % p.npair;
+    if (!p.paired) {
+        attn_tile<T>(p, bh, i, ks0, ks1, vs0, vs1);
+        return;
+    }
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
         const int qb = pass == 0 ? p.nqb - 1 - i : i;

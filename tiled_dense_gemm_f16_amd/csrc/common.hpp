@@ -50,7 +50,48 @@ struct Args {
     uint32_t* counters;  // one per column tile, zero between launches (splits > 1)
     int splits;          // workgroups along K
     int kc;              // K range of one workgroup
+    // timestamp builds only (GR_STAMPS): kStampWords words per workgroup, or null
+    uint64_t* stamps;
 };
+
+// Per-workgroup timestamps, compiled in only when GR_STAMPS is defined (the
+// profiling build of build.py --stamps): the first wave keeps the 100 MHz
+// realtime counter of a few points of a kernel in registers (constant slots,
+// no memory traffic inside the kernel), and at the end its first lane writes
+// them, with the die (XCC_ID) and hardware ids, to p.stamps. Slots: 0 start,
+// 1 first tile data in LDS or registers, 2 main loop done, 3 last store
+// acknowledged; 4 split-K partials stored and counted; 5 die, 6 HW_ID.
+// Ordinary builds compile none of it.
+constexpr int kStampWords = 8;
+#ifdef GR_STAMPS
+#define GR_STAMP_DECL uint64_t gr_stamps[kStampWords] = {}
+#define GR_STAMP(i)                                          \
+    do {                                                     \
+        gr_stamps[i] = __builtin_amdgcn_s_memrealtime();     \
+    } while (0)
+#define GR_STAMP_FLUSH(p)                                                                   \
+    do {                                                                                    \
+        __builtin_amdgcn_s_waitcnt(0);                                                      \
+        gr_stamps[3] = __builtin_amdgcn_s_memrealtime();                                    \
+        if (threadIdx.x == 0 && (p).stamps) {                                               \
+            unsigned gr_xcc, gr_hw;                                                         \
+            asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(gr_xcc));            \
+            asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(gr_hw));              \
+            gr_stamps[5] = gr_xcc;                                                          \
+            gr_stamps[6] = gr_hw;                                                           \
+            _Pragma("unroll") for (int gr_k = 0; gr_k < kStampWords; ++gr_k)               \
+                (p).stamps[(int64_t)blockIdx.x * kStampWords + gr_k] = gr_stamps[gr_k];     \
+        }                                                                                   \
+    } while (0)
+#else
+#define GR_STAMP_DECL static_assert(true, "")
+#define GR_STAMP(i) \
+    do {            \
+    } while (0)
+#define GR_STAMP_FLUSH(p) \
+    do {                  \
+    } while (0)
+#endif
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes)
 {

@@ -540,6 +540,13 @@ enum class Scratch {
     kStatic,           // the fixed per-device array above (allocates nothing)
 };
 
+#ifdef GR_STAMPS
+// The timestamp build's buffer: kStampWords words per workgroup for launches
+// of at most g_stamp_max_wg workgroups (larger launches record nothing).
+uint64_t* g_stamp_buf = nullptr;
+int64_t g_stamp_max_wg = 0;
+#endif
+
 // Validated call -> tile choice, split-K workspace, launch. `act` selects the
 // epilogue (kActRelu, or kActBiasGelu with `bias`).
 int run(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B, int op_b, void* C, void* stream,
@@ -588,6 +595,7 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B,
     a.counters = nullptr;
     a.splits = 1;
     a.kc = (int)(K < 1 ? 1 : K);
+    a.stamps = nullptr;
     const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
     if (tiles > INT32_MAX) return GEMM_RELU_EUNSUPPORTED;
     if (splitk) {
@@ -607,6 +615,9 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B,
                                        : get_workspace(dev, s, (size_t)tiles, partial_bytes, &a.counters, &a.partial);
         if (rc != GEMM_RELU_OK) return rc;
     }
+#ifdef GR_STAMPS
+    if (tiles * a.splits <= g_stamp_max_wg) a.stamps = g_stamp_buf;
+#endif
     const hipError_t e = (vec ? te.vec : te.generic)(a, s);
     return e == hipSuccess ? GEMM_RELU_OK : GEMM_RELU_EHIP;
 }
@@ -629,6 +640,18 @@ const char* gemm_relu_strerror(int status)
     default: return "unknown status";
     }
 }
+
+#ifdef GR_STAMPS
+// Timestamp build only (not part of the ABI in include/): device buffer of
+// max_workgroups * 8 words that later launches fill, one row per workgroup
+// (see GR_STAMP_FLUSH in common.hpp); NULL or 0 turns recording off.
+int gemm_relu_stamps_set(void* buf, int64_t max_workgroups)
+{
+    g_stamp_buf = static_cast<uint64_t*>(buf);
+    g_stamp_max_wg = buf ? max_workgroups : 0;
+    return GEMM_RELU_OK;
+}
+#endif
 
 int gemm_relu_tile_count(void) { return kNumTiles; }
 

@@ -193,6 +193,8 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     auto stage_b = [&]<int S>() -> uint16_t* { return stage_a.template operator()<S>() + T::A_HALVES; };
 
     static_assert(!TA || (T::BM >= 64 && 512 % T::BM == 0), "a transposed A tile row is 64 to 512 halves");
+    GR_STAMP_DECL;
+    GR_STAMP(0);
     int tm, tn;
     tile_coords(p, tm, tn);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
@@ -442,6 +444,7 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
                 ...);
         }(std::make_integer_sequence<int, AHEAD>{});
         sync.template operator()<(AHEAD - 1) * T::LPT>();
+        GR_STAMP(1);
 #pragma unroll
         for (int s = 0; s < T::NSLOT; ++s) read_slot.template operator()<0>(0, s, x);
 #pragma unroll
@@ -462,6 +465,7 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     // the zero-filling loads past the end must land, and every wave must be
     // done with its fragment reads, before the ring is reused
     sync.template operator()<0>();
+    GR_STAMP(2);
 
     // ---- epilogue: ReLU (or bias + GELU), fp16 (nearest even) into LDS, then
     // row stores ----
@@ -542,6 +546,7 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
             if (m < M && n < N) *reinterpret_cast<u32x4*>(p.C + (int64_t)m * N + n) = v;
         }
     }
+    GR_STAMP_FLUSH(p);
 }
 
 }  // namespace pipelined

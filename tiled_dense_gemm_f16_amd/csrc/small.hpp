@@ -110,6 +110,8 @@ __global__ void __launch_bounds__(T::NT, T::NW >= 4 ? 2 : 3) small_kernel(Args p
         else return st7;
     };
 
+    GR_STAMP_DECL;
+    GR_STAMP(0);
     int tm, tn;
     tile_coords(p, tm, tn);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
@@ -303,6 +305,7 @@ __global__ void __launch_bounds__(T::NT, T::NW >= 4 ? 2 : 3) small_kernel(Args p
                 ...);
         }(std::make_integer_sequence<int, R>{});
         sync.template operator()<(R - 1) * T::LPW>();
+        GR_STAMP(1);
 #pragma unroll
         for (int q = 0; q < T::NREAD; ++q) read_one.template operator()<0>(q, x);
     }
@@ -315,6 +318,7 @@ __global__ void __launch_bounds__(T::NT, T::NW >= 4 ? 2 : 3) small_kernel(Args p
     }
     // the zero-filling loads past the end must land before the waves exit
     __builtin_amdgcn_s_waitcnt(0);
+    GR_STAMP(2);
 
     // ---- epilogue: lane holds, for rows 32i + lane%32 of the wave tile, the
     // columns 32j + 8q + 4(lane/32) + 0..3 in acc[.][i][j][4q .. 4q+3] ----
@@ -338,6 +342,7 @@ __global__ void __launch_bounds__(T::NT, T::NW >= 4 ? 2 : 3) small_kernel(Args p
             }
         }
     });
+    GR_STAMP_FLUSH(p);
 }
 
 }  // namespace small

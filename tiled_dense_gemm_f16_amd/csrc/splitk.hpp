@@ -69,6 +69,8 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
 {
     __shared__ __attribute__((aligned(16))) float red[T::NW][T::BM][T::RED_ROW];
     __shared__ uint32_t last_flag;
+    GR_STAMP_DECL;
+    GR_STAMP(0);
 
     const int M = p.M, N = p.N, K = p.K;
     // workgroup -> (row tile, column tile, split); the splits of one tile are
@@ -191,12 +193,16 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
 #pragma unroll
         for (int d = 0; d < T::D; ++d) {
             compute(d);
+#ifdef GR_STAMPS
+            if (s0 == 0 && d == 0) GR_STAMP(1);
+#endif
             __builtin_amdgcn_sched_barrier(0);
             issue(d, s0 + d + T::D);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 
+    GR_STAMP(2);
     // ---- reduction across the four waves (fixed order) ----
     // Lane holds acc[mb][e][r] = C[mb*16 + i16][gcol(32g + 8r + e)].
 #pragma unroll
@@ -263,6 +269,7 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
 
     if (p.splits == 1) {
         store_c(v);
+        GR_STAMP_FLUSH(p);
         return;
     }
 
@@ -312,7 +319,11 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
         last_flag = (prev == (uint32_t)(p.splits - 1)) ? 1u : 0u;
     }
     __syncthreads();
-    if (!last_flag) return;
+    GR_STAMP(4);
+    if (!last_flag) {
+        GR_STAMP_FLUSH(p);
+        return;
+    }
     // Up to kBatch splits' partials are loaded before any is added, so their
     // latencies overlap; the additions keep split order.
     constexpr int kBatch = 8;
@@ -348,6 +359,7 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
     }
     store_c(sum);
     if (t == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    GR_STAMP_FLUSH(p);
 }
 
 }  // namespace splitk
