@@ -169,11 +169,37 @@ class ClockSampler:
         return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v), "source": self.path}
 
 
+def _sysfs_device() -> dict:
+    """Product name and PCI ids of the card behind the clock file, from sysfs
+    (empty where the files are missing)."""
+    out = {}
+    path = _sclk_file()
+    if not path:
+        return out
+    d = os.path.dirname(path)
+    for key, name in (("product_name", "product_name"), ("vendor", "pci_vendor"), ("device", "pci_device")):
+        try:
+            with open(os.path.join(d, key)) as f:
+                v = f.read().strip()
+        except OSError:
+            continue
+        if v:
+            out[name] = v
+    return out
+
+
 def device_identity() -> dict:
     import torch
     p = torch.cuda.get_device_properties(0)
-    return {"gpu_name": torch.cuda.get_device_name(0), "gfx_arch": p.gcnArchName.split(":")[0],
-            "compute_units": p.multi_processor_count, "hbm_gib": round(p.total_memory / 2 ** 30, 1)}
+    sysfs = _sysfs_device()
+    name = torch.cuda.get_device_name(0) or sysfs.get("product_name", "")
+    if not name and "pci_device" in sysfs:
+        name = f"PCI {sysfs.get('pci_vendor', '?')}:{sysfs['pci_device']}"
+    out = {"gpu_name": name, "gfx_arch": p.gcnArchName.split(":")[0],
+           "compute_units": p.multi_processor_count, "hbm_gib": round(p.total_memory / 2 ** 30, 1)}
+    if "pci_device" in sysfs:
+        out["pci_id"] = f"{sysfs.get('pci_vendor', '?')}:{sysfs['pci_device']}"
+    return out
 
 
 def time_launches(calls, steps: int, warmup: int, graph_batch: int, stream, steady_ms: float = STEADY_MS,
