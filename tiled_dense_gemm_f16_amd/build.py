@@ -49,6 +49,11 @@ SANITIZED_LIB = os.path.join(PKG, "libgemm_relu_asan.so")
 # The timestamp build (GR_STAMPS): the same kernels with per-workgroup
 # timestamps at a few points (see common.hpp), for stamps.py.
 STAMPS_LIB = os.path.join(PKG, "libgemm_relu_stamps.so")
+# The matrix-core ceiling probe: a stand-alone program (no library, no
+# Python) that times back-to-back matrix ops with the shader clock and board
+# power it reads from sysfs.
+CEILING_SRC = os.path.join(PKG, "csrc", "mfma_ceiling.hip")
+CEILING_BIN = os.path.join(PKG, "mfma_ceiling")
 
 
 def asan_runtime() -> str:
@@ -106,5 +111,24 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
     return out
 
 
+def build_ceiling(verbose: bool = False) -> str:
+    """Compile the matrix-core ceiling probe (CEILING_BIN)."""
+    tmp = CEILING_BIN + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f != "-fPIC"], CEILING_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        if os.path.exists(tmp):
+            os.remove(tmp)
+        raise RuntimeError(f"hipcc failed ({res.returncode}) compiling {CEILING_SRC}")
+    os.replace(tmp, CEILING_BIN)
+    return CEILING_BIN
+
+
 if __name__ == "__main__":
-    print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:], stamps="--stamps" in sys.argv[1:]))
+    if "--ceiling" in sys.argv[1:]:
+        print(build_ceiling(verbose=True))
+    else:
+        print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:], stamps="--stamps" in sys.argv[1:]))
