@@ -662,6 +662,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--all", action="store_true", help="also time every workload (lines on stderr)")
+    ap.add_argument("--shards", action="store_true",
+                    help="also time one GPU's share of the 4096^3 and 16x8192x8192 workloads under 2-, 4- "
+                         "and 8-way column splits (lines on stderr)")
     ap.add_argument("--epilogue", choices=("relu", "bias_gelu"), default="relu",
                     help="relu: C = ReLU(A @ B) (the headline); bias_gelu: C = GELU(A @ B + bias)")
     ap.add_argument("--layout", choices=("nn", "nt", "tn", "tt"), default="nn",
@@ -761,6 +764,25 @@ def main(argv=None) -> int:
         pl = result_line(pw, prr, max(args.steps // 4, 50), max(args.warmup // 4, 10))
         pl["note"] = "the pages' 128x128x64 tile pinned, for comparison with the library's choice"
         print(json.dumps(pl), file=sys.stderr, flush=True)
+    if args.shards:
+        # one GPU's share of a column split: no exchange is needed, so a
+        # ways-GPU run would take this shard's time (C stays distributed)
+        full = {w.name: r}
+        for fw in (workloads.SQUARE_4096, workloads.SKINNY):
+            if fw.name not in full:
+                full[fw.name] = time_gpu(fw, max(args.steps // 4, 50), max(args.warmup // 4, 10), None, args.graph,
+                                         args.epilogue, args.layout, args.rotate_mib << 20, args.steady_ms)
+        for sw in workloads.SHARDS:
+            base = workloads.SQUARE_4096 if sw.M == workloads.SQUARE_4096.M else workloads.SKINNY
+            ways = base.N // sw.N
+            srr = time_gpu(sw, max(args.steps // 4, 50), max(args.warmup // 4, 10), None, args.graph, args.epilogue,
+                           args.layout, args.rotate_mib << 20, args.steady_ms)
+            sl = result_line(sw, srr, max(args.steps // 4, 50), max(args.warmup // 4, 10))
+            t_full = full[base.name]["ms_per_step"]
+            sl["shard_of"] = {"workload": base.name, "ways": ways, "split": "columns of B and C",
+                              "full_ms_per_step_one_gpu": t_full,
+                              "speedup_if_each_gpu_runs_one_shard": round(t_full / srr["ms_per_step"], 3)}
+            print(json.dumps(sl), file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline and args.epilogue == "relu" and args.layout == "nn":
         cpu = cpu_baseline(w, r, args.cpu_seconds)

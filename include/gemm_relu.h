@@ -127,7 +127,7 @@ int gemm_relu_f16(int64_t M, int64_t N, int64_t K,
  * kernel that clears the counters; each launch leaves them at zero.
  */
 #define GEMM_RELU_NOALLOC_MAX_TILES 4096
-#define GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES (4 * 1024 * 1024)
+#define GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES (2 * 1024 * 1024)
 int gemm_relu_f16_noalloc(int64_t M, int64_t N, int64_t K,
                           const void* A, const void* B, void* C, void* stream);
 

@@ -43,8 +43,9 @@ def neg(t):
 # the five workloads
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("w", [workloads.SQUARE_256, workloads.SQUARE_1024, workloads.RAGGED,
-                               workloads.SKINNY], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [workloads.SQUARE_256, workloads.SQUARE_1024, workloads.RAGGED, workloads.SKINNY,
+                               *[s for s in workloads.SHARDS if s.M == workloads.SKINNY.M]],
+                         ids=lambda w: w.name)
 def test_workload_full_parity(w):
     say(f"[parity] {w.name} M={w.M} N={w.N} K={w.K} seed={w.seed} tile={gr.select_tile(w.M, w.N, w.K)}")
     a, b = workloads.workload_inputs(w)
@@ -56,8 +57,9 @@ def test_workload_full_parity(w):
         say(f"  sign={sign:+d} {st}")
 
 
-def test_workload_4096_sampled():
-    w = workloads.SQUARE_4096
+@pytest.mark.parametrize("w", [workloads.SQUARE_4096, *[s for s in workloads.SHARDS if s.M == 4096]],
+                         ids=lambda w: w.name)
+def test_workload_4096_sampled(w):
     say(f"[parity] {w.name} sampled, tile={gr.select_tile(w.M, w.N, w.K)}")
     a, b = workloads.workload_inputs(w)
     A, B = workloads.as_u16(a), workloads.as_u16(b)

@@ -17,7 +17,7 @@ LIB_PATH = os.environ.get("GEMM_RELU_LIB") or os.path.join(PKG, "libgemm_relu.so
 
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM, ETOOBIG = 0, 1, 2, 3, 4, 5
 NOALLOC_MAX_TILES = 4096                      # GEMM_RELU_NOALLOC_MAX_TILES
-NOALLOC_MAX_PARTIAL_BYTES = 4 * 1024 * 1024   # GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES
+NOALLOC_MAX_PARTIAL_BYTES = 2 * 1024 * 1024   # GEMM_RELU_NOALLOC_MAX_PARTIAL_BYTES
 TILE_AUTO = -1
 OP_N, OP_T = 0, 1  # operand as stored / stored transposed
 ORDER_DEFAULT, ORDER_ROW_MAJOR = 0, 1

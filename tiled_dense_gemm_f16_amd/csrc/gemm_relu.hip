@@ -54,9 +54,6 @@ using S16 = gemm_relu::staged::Tile<16, 64, 64, 1, 4, 1, 4>;      // 4 waves x 1
 #ifndef GR_SPLITK_D
 #define GR_SPLITK_D 4
 #endif
-#ifndef GR_SPLITK_TARGET
-#define GR_SPLITK_TARGET 256
-#endif
 using K16 = gemm_relu::splitk::Cfg<1, GR_SPLITK_NW, GR_SPLITK_D>;  // split-K, 16 rows x 128 columns
 using K32 = gemm_relu::splitk::Cfg<2, GR_SPLITK_NW, GR_SPLITK_D>;  // split-K, 32 rows x 128 columns
 using K64 = gemm_relu::splitk::Cfg<4, GR_SPLITK_NW, GR_SPLITK_D>;  // split-K, 64 rows x 128 columns
@@ -205,22 +202,48 @@ constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kGenericTile = 2;  // tile used by the element-wise path
 constexpr int kSplitKTN = 128;   // columns of a split-K workgroup
 constexpr int kSplitKStep = GR_SPLITK_NW * 32;  // K granularity of a split-K workgroup (waves x 32)
-constexpr int kTargetBlocks = GR_SPLITK_TARGET;  // workgroups to aim for
 
 // How many workgroups share the K range of one split-K tile, and the K range
-// of each (a multiple of kSplitKStep).
+// of each (a multiple of kSplitKStep). Candidates are powers of two up to one
+// step per workgroup and at most one workgroup per CU (a second round never
+// paid in the sweeps); among them the one with the least predicted time:
+//   a fixed part + a cost per split (partials written, counted and re-read
+//   by the last workgroup) + the streaming of B, bytes over the smaller of
+//   (workgroups x one CU's streaming rate) and the HBM rate + the serial depth
+//   of one workgroup's K range.
+// The constants were fitted to split-K launches of 16 x N x K (N = 1024 to
+// 8192, K = 2048 to 8192) with 1 to 64 splits; for those shapes the model's
+// choice is the measured best or within 4 % of it.
+constexpr double kSplitPerSplitUs = 0.431;
+constexpr double kSplitCuBytesPerUs = 58.07e3;   // one CU streaming B
+constexpr double kSplitHbmBytesPerUs = 6.18e6;   // all CUs streaming B
+constexpr double kSplitDepthUsPer1024 = 1.89;    // per 1024 rows of a workgroup's K range
+constexpr int64_t kSplitMaxWorkgroups = 256;     // one per CU
+
 void choose_splits(int64_t K, int64_t tiles, int& splits, int& kc)
 {
-    int64_t s = tiles >= kTargetBlocks ? 1 : (kTargetBlocks + tiles - 1) / tiles;
     const int64_t max_s = (K + kSplitKStep - 1) / kSplitKStep;  // at least one step per workgroup
-    if (s > max_s) s = max_s;
-    if (s < 1) s = 1;
-    int64_t c = (K + s - 1) / s;
-    c = (c + kSplitKStep - 1) / kSplitKStep * kSplitKStep;
-    if (c < kSplitKStep) c = kSplitKStep;
-    kc = (int)c;
-    splits = (int)((K + c - 1) / c);
-    if (splits < 1) splits = 1;
+    const double bytes = (double)tiles * kSplitKTN * (double)K * 2.0;  // B, once per row tile
+    double best = 0.0;
+    splits = 1;
+    kc = (int)((K + kSplitKStep - 1) / kSplitKStep * kSplitKStep);
+    if (kc < kSplitKStep) kc = kSplitKStep;
+    for (int64_t s = 1; s <= max_s; s *= 2) {
+        int64_t c = (K + s - 1) / s;
+        c = (c + kSplitKStep - 1) / kSplitKStep * kSplitKStep;
+        if (c < kSplitKStep) c = kSplitKStep;
+        const int64_t se = (K + c - 1) / c < 1 ? 1 : (K + c - 1) / c;
+        const int64_t wgs = tiles * se;
+        if (se > 1 && wgs > kSplitMaxWorkgroups) break;
+        const double rate = (double)wgs * kSplitCuBytesPerUs < kSplitHbmBytesPerUs
+                                ? (double)wgs * kSplitCuBytesPerUs : kSplitHbmBytesPerUs;
+        const double us = kSplitPerSplitUs * (double)se + bytes / rate + kSplitDepthUsPer1024 * (double)c / 1024.0;
+        if (s == 1 || us < best) {
+            best = us;
+            splits = (int)se;
+            kc = (int)c;
+        }
+    }
 }
 
 // The vector kernels: 16-byte aligned pointers and leading dimensions (K or M

@@ -51,7 +51,24 @@ RAGGED = Workload("gemm_relu_f16_1000x1016x1000_uniform", 1000, 1016, 1000, "uni
 SKINNY = Workload("gemm_relu_f16_16x8192x8192_normal0.02", 16, 8192, 8192, "normal", 0.02)
 
 ALL = (SQUARE_256, SQUARE_1024, SQUARE_4096, RAGGED, SKINNY)
-BY_NAME = {w.name: w for w in ALL}
+
+
+def n_shard(w: Workload, ways: int) -> Workload:
+    """One GPU's share of `w` when C's columns are split `ways` ways: each GPU
+    holds a replica of A and the column panel B[:, N_g] and writes C[:, N_g],
+    with no exchange between GPUs (the ReLU is element-wise). Same
+    distribution and seed; the shape is M x N/ways x K."""
+    if ways < 1 or w.N % ways:
+        raise ValueError(f"{w.name}: N = {w.N} does not split {ways} ways")
+    n = w.N // ways
+    name = w.name.replace(f"_{w.M}x{w.N}x{w.K}_", f"_{w.M}x{n}x{w.K}_") + f"_nsplit{ways}"
+    return Workload(name, w.M, n, w.K, w.dist, w.scale, w.seed)
+
+
+# One GPU's share of the headline square problem and of the skinny one under
+# 2-, 4- and 8-way column splits.
+SHARDS = tuple(n_shard(w, ways) for w in (SQUARE_4096, SKINNY) for ways in (2, 4, 8))
+BY_NAME = {w.name: w for w in ALL + SHARDS}
 
 
 def _draw(gen: torch.Generator, shape, dist: str, scale: float) -> torch.Tensor:
