@@ -662,6 +662,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--all", action="store_true", help="also time every workload (lines on stderr)")
+    ap.add_argument("--floor", action="store_true",
+                    help="also time each workload's launch with K = 64 on the same tile (one reduction step: "
+                         "launch, first loads, epilogue and stores; lines on stderr)")
     ap.add_argument("--shards", action="store_true",
                     help="also time one GPU's share of the 4096^3 and 16x8192x8192 workloads under 2-, 4- "
                          "and 8-way column splits (lines on stderr)")
@@ -764,6 +767,22 @@ def main(argv=None) -> int:
         pl = result_line(pw, prr, max(args.steps // 4, 50), max(args.warmup // 4, 10))
         pl["note"] = "the pages' 128x128x64 tile pinned, for comparison with the library's choice"
         print(json.dumps(pl), file=sys.stderr, flush=True)
+    if args.floor:
+        # what a launch costs without its reduction: the same tile and grid
+        # with one 64-deep step, so what remains is the launch, the first
+        # loads' latency, the epilogue and the stores of C
+        for fw in workloads.ALL:
+            frr = r if fw is w else time_gpu(fw, max(args.steps // 4, 50), max(args.warmup // 4, 10), None, args.graph,
+                                             args.epilogue, args.layout, args.rotate_mib << 20, args.steady_ms)
+            tile_id = next(t for t in range(gr.tile_count()) if gr.tile_name(t) == frr["tile"])
+            kw = workloads.Workload(fw.name.replace(f"x{fw.K}_", "x64_", 1) + "_floor", fw.M, fw.N, 64, fw.dist,
+                                    fw.scale, fw.seed)
+            krr = time_gpu(kw, max(args.steps // 4, 50), max(args.warmup // 4, 10), tile_id, args.graph, args.epilogue,
+                           args.layout, args.rotate_mib << 20, args.steady_ms)
+            print(json.dumps({"floor": kw.name, "tile": krr["tile"], "us_k64": round(krr["ms_per_step"] * 1e3, 3),
+                              "workload": fw.name, "us_full": round(frr["ms_per_step"] * 1e3, 3),
+                              "share_of_full": round(krr["ms_per_step"] / frr["ms_per_step"], 3)}),
+                  file=sys.stderr, flush=True)
     if args.shards:
         # one GPU's share of a column split: no exchange is needed, so a
         # ways-GPU run would take this shard's time (C stays distributed)
