@@ -62,10 +62,11 @@ def kernel_sources(tile: str) -> list[str]:
     second workload, the attention and softmax kernels: "attn_fwd_d128",
     "softmax_rows")."""
     if tile.startswith(("attn", "softmax")):
-        family = "attention.hpp"
-    else:
-        family = ("small.hpp" if "lds-small" in tile else "pipelined.hpp" if "lds-dma" in tile
-                  else "splitk.hpp" if "splitk" in tile else "staged.hpp")
+        # the kernels and their launch configuration (waves per workgroup)
+        return [os.path.join(CSRC, "common.hpp"), os.path.join(CSRC, "attention.hpp"),
+                os.path.join(CSRC, "attention.hip")]
+    family = ("small.hpp" if "lds-small" in tile else "pipelined.hpp" if "lds-dma" in tile
+              else "splitk.hpp" if "splitk" in tile else "staged.hpp")
     return [os.path.join(CSRC, "common.hpp"), os.path.join(CSRC, family)]
 
 
