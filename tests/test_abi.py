@@ -144,11 +144,29 @@ def test_tuner_candidates():
         if x["block_order"] == gr.ORDER_ROW_MAJOR:
             assert x["group_m"] == 0 and not d["split_k"]
         assert x["group_m"] <= -(-4096 // d["bm"])
+    # the library's own group is always timed (384 x 6144: 6 tile-rows of 64,
+    # default group 8 -> 4)
+    c384 = tune.candidates(384, 6144, 6144)
+    t64 = next(t for t in range(gr.tile_count()) if gr.tile_name(t).startswith("64x64x64s4"))
+    g_def = tune.default_group(gr.tile_info(t64)["default_group_m"], 6)
+    assert g_def == 4
+    assert any(x["tile"] == t64 and x["block_order"] == gr.ORDER_DEFAULT and x["group_m"] == g_def for x in c384)
     # a grid one tile-row high has no block order to choose
     assert all(x["group_m"] == 0 and x["block_order"] == gr.ORDER_DEFAULT for x in tune.candidates(16, 8192, 8192))
     # a tighter LDS budget prunes the big tiles
     small = tune.candidates(1024, 1024, 1024, lds_limit=64 * 1024)
     assert small and all(gr.tile_info(x["tile"])["lds_bytes"] <= 64 * 1024 for x in small)
+
+
+def test_default_group_rule():
+    from tiled_dense_gemm_f16_amd import tune
+
+    # (tile default, tile-rows) -> group: a power of two, at least two groups
+    # from four tile-rows on
+    cases = {(8, 16): 8, (8, 8): 4, (8, 6): 4, (8, 4): 2, (8, 3): 2, (8, 2): 2, (8, 1): 1,
+             (4, 16): 4, (4, 4): 2, (4, 5): 4, (1, 16): 1, (16, 1024): 16}
+    for (g, tm), want in cases.items():
+        assert tune.default_group(g, tm) == want, (g, tm)
 
 
 def test_timing_rotation_covers_the_last_level_cache():

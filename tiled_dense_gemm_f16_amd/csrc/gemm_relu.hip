@@ -193,12 +193,25 @@ const TileEntry kTiles[] = {
      launch_staged<S128, false>},
     {"64x256x32s4_w1x2_mfma32x32x16_lds-dma", pipelined_desc<P64>(4), launch_pipelined<P64>,
      launch_staged<S64, false>},
-    {"64x64x64s4_w2x2_mfma32x32x16_lds-small", small_desc<Q64>(4), launch_small<Q64, S64>,
+    {"64x64x64s4_w2x2_mfma32x32x16_lds-small", small_desc<Q64>(8), launch_small<Q64, S64>,
      launch_staged<S64, false>},
     {"32x64x64s4_w1x2_mfma32x32x16_lds-small", small_desc<Q32>(4), launch_small<Q32, S64>,
      launch_staged<S64, false>},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+// The group a launch without opts uses: the tile's default, cut to a power of
+// two that leaves at least two groups when the grid has four tile-rows or
+// more. A group spanning every tile-row measured 3-5 % slower on average over
+// the sweeps than 4 or 8 rows (384 x 6144 x 6144 with 64 x 64 tiles, 6 rows:
+// 84.9 us in one group of 6 against 77.6 in groups of 4).
+int default_group(int group, int tiles_m)
+{
+    int g = 1;
+    while (2 * g <= group && 2 * g <= tiles_m) g *= 2;
+    if (g == tiles_m && tiles_m >= 4) g /= 2;
+    return g;
+}
 constexpr int kGenericTile = 2;  // tile used by the element-wise path
 constexpr int kSplitKTN = 128;   // columns of a split-K workgroup
 constexpr int kSplitKStep = GR_SPLITK_NW * 32;  // K granularity of a split-K workgroup (waves x 32)
@@ -302,8 +315,13 @@ constexpr AutoTile kAutoTiles[] = {
 // the default launch is 1.023x the fastest on average, 1.135x at worst.
 struct SmallTile {
     int id;
+    bool one_round;  // only for grids of at most one workgroup per CU
 };
-constexpr SmallTile kSmallTiles[] = {{11}, {12}};
+// The 32 x 64 tile moves 1.5x the bytes of the 64 x 64 one per FLOP; it pays
+// only where the 64 x 64 grid leaves CUs idle and its own grid still fits one
+// round: with a partial second round (768^3: 288 workgroups) the units that
+// run two take twice as long (8.8 us against 7.2 for 64 x 64).
+constexpr SmallTile kSmallTiles[] = {{11, false}, {12, true}};
 constexpr double kSmallFixedUs = 2.25;
 // The rate model below predicts times that are, over the sweep, about
 // 1.455 x + 4.0 us short of the measured ones (4096^3: 77 -> 116 us, 2048^3:
@@ -378,6 +396,8 @@ int choose_tile(int64_t M, int64_t N, int64_t K, bool ta, bool tb)
     // the small tiles: operands as stored, more than a few rows
     if (layout == 0 && !few_rows) {
         for (const SmallTile& st : kSmallTiles) {
+            const gemm_relu_tile_desc& d = kTiles[st.id].desc;
+            if (st.one_round && ((M + d.bm - 1) / d.bm) * ((N + d.bn - 1) / d.bn) > (int64_t)kComputeUnits) continue;
             const double us = (predict_small(st, M, N, K) - kRateModelOffsetUs) / kRateModelScale;
             if (us < bp.us) {
                 best = st.id;
@@ -604,11 +624,15 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B,
     a.K = (int)K;
     a.tiles_m = (int)((M + te.desc.bm - 1) / te.desc.bm);
     a.tiles_n = (int)((N + te.desc.bn - 1) / te.desc.bn);
-    a.group_m = (opts && opts->group_m > 0) ? opts->group_m : te.desc.default_group_m;
-    // a group of more tile-rows than there are is the same order as one of
-    // all of them; clamping also keeps group_m * tiles_n within int32 in the
-    // kernels' block-order arithmetic
-    if (a.group_m > a.tiles_m) a.group_m = a.tiles_m;
+    if (opts && opts->group_m > 0) {
+        a.group_m = opts->group_m;
+        // a group of more tile-rows than there are is the same order as one
+        // of all of them; clamping also keeps group_m * tiles_n within int32
+        // in the kernels' block-order arithmetic
+        if (a.group_m > a.tiles_m) a.group_m = a.tiles_m;
+    } else {
+        a.group_m = default_group(te.desc.default_group_m, a.tiles_m);
+    }
     a.order = opts ? opts->block_order : GEMM_RELU_ORDER_DEFAULT;
     a.trans_a = ta ? 1 : 0;
     a.trans_b = tb ? 1 : 0;

@@ -63,6 +63,9 @@
 namespace gemm_relu {
 namespace pipelined {
 
+// tiles one launch places one per compute unit (256 CUs)
+constexpr int kSkewTilesOneRound = 256;
+
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_ = 4>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = STAGES_;
@@ -203,6 +206,23 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
     const int nk = (K + T::BK - 1) / T::BK;
+    // This tile's first K step (the walk wraps around): tiles of a die that
+    // share an A row panel or a B column panel then read different steps of
+    // it at any moment instead of requesting the same lines at once.
+    // 64- and 128-row tiles skew over the whole K range (2048^3 33.3 -> 31.2
+    // us). 256 x 256 tiles skew by at most 7 steps, and only when there are
+    // more tiles than CUs (8192 x 8192 x 1024: 141.2 -> 134.0 us): with one
+    // tile per CU, as at 4096^3, the dies' tiles walk K in step and share
+    // what each die fetches, and a skew measured no better. Below 8 steps
+    // every load is a first touch from HBM, where reading the same lines
+    // together shares their latency.
+    int kskew = 0;
+    if (nk >= 8) {
+        if constexpr (T::BM == 256 && T::BN == 256)
+            kskew = p.tiles_m * p.tiles_n > kSkewTilesOneRound ? ((tm + tn) % 8) % nk : 0;
+        else
+            kskew = (tm + tn) % nk;
+    }
 
     // ---- per-lane global offsets of this wave's direct loads (bytes, relative
     // to the step's descriptor base: A + m0*K + k0 and B + k0*N) ----
@@ -252,8 +272,8 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         __amdgpu_buffer_rsrc_t a, b;
     };
     auto descriptors = [&](int kt) -> Rsrc {
-        const int k0 = kt * T::BK;
         const bool live = kt < nk;
+        const int k0 = live ? ((kt + kskew) % nk) * T::BK : 0;
         int64_t arem = TA ? ((int64_t)K - k0) * M * 2 : ((int64_t)(M - m0) * K - k0) * 2;
         int64_t brem = TB ? ((int64_t)(N - n0) * K - k0) * 2 : ((int64_t)K - k0) * N * 2;
         arem = live ? arem : 0;
@@ -272,14 +292,16 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
             const __amdgpu_buffer_rsrc_t ra = r.a;
             uint32_t off = a_off[i];
             // a k-contiguous tile masks the K tail per lane
-            if constexpr (!KALIGNED && !TA) off = (kt * T::BK + a_kc[i] * 8 < K) ? off : kOOB;
+            if constexpr (!KALIGNED && !TA)
+                off = (kt < nk && ((kt + kskew) % nk) * T::BK + a_kc[i] * 8 < K) ? off : kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (GR_LDS void*)(sa + (wave * T::A_LOADS_W + i) * 512), 16, (int)off, 0, 0, 0);
         } else {
             const __amdgpu_buffer_rsrc_t rb = r.b;
             const int j = i - T::A_LOADS_W;
             uint32_t off = b_off[j];
-            if constexpr (!KALIGNED && TB) off = (kt * T::BK + b_kc[j] * 8 < K) ? off : kOOB;
+            if constexpr (!KALIGNED && TB)
+                off = (kt < nk && ((kt + kskew) % nk) * T::BK + b_kc[j] * 8 < K) ? off : kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rb, (GR_LDS void*)(sb + (wave * T::B_LOADS_W + j) * 512), 16, (int)off, 0, 0, 0);
         }
