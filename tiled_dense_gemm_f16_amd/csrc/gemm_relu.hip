@@ -284,12 +284,14 @@ bool splitk_ok(int64_t M, int64_t K) { return M * K * 2 < ((int64_t)1 << 31); }
 // The rate is what one compute unit sustains on that tile in that operand
 // layout (larger tiles reuse each loaded byte more; the fitted rates include
 // the clock the chip holds under load). Two rules sit on top: few rows
-// (M <= 64) always take a split-K tile, and the 16x64 tile is only for
-// latency-bound outputs of at most 64 K elements. In the NN layout the model
-// picks a launch 1.5 % slower than the measured fastest on average (21 % at
-// worst); in the transposed layouts 1-6 % on average (27 % at worst). The
-// rules it replaced, which looked at M and the 256x256 tile count alone,
-// were up to 6x slower on shapes they were not written for.
+// (M <= 32 with operands as stored, M <= 64 otherwise) always take a split-K
+// tile, and the 16x64 tile is only for latency-bound outputs of at most 64 K
+// elements. Over the offline sweeps the default launch (this model, the
+// small-tile model below and the group rule) is 1.4 % slower than the
+// measured fastest on average in NN (8 % at worst, 46 shapes) and 1.3-1.7 %
+// in the transposed layouts (5 % at worst, 12 shapes each). The rules it
+// replaced, which looked at M and the 256x256 tile count alone, were up to
+// 6x slower on shapes they were not written for.
 struct AutoTile {
     int id;
     double tflops_per_cu[4];  // NN, NT, TN, TT (index 2 * trans_a + trans_b)
@@ -298,10 +300,15 @@ constexpr AutoTile kAutoTiles[] = {
     {0, {6.96, 5.78, 6.63, 6.10}},   // 256x256 pipelined
     {9, {5.24, 3.90, 4.96, 4.04}},   // 128x256 pipelined
     {10, {3.21, 2.21, 2.79, 2.25}},  // 64x256 pipelined
-    {6, {2.13, 1.27, 0.570, 0.517}}, // split-K 64x128
+    {6, {2.13, 1.15, 0.570, 0.517}}, // split-K 64x128
     {5, {1.59, 0.772, 0.390, 0.344}},// split-K 32x128
     {4, {1.12, 0.472, 0.408, 0.324}},// split-K 16x128
     {2, {0.895, 1.24, 0.429, 0.756}},// 64x64 staged
+    // 128x128 staged: with B stored N x K (NT) it needs no transpose and beat
+    // the pipelined tiles at 2048^3 and 4096 x 1024 x 4096 (39.1 against
+    // 40.7 us, 71.1 against 76.8); its other rates keep it out of the NN, TN
+    // and TT choices, where it was 1.15-3x off the best.
+    {1, {1.0, 2.35, 0.9, 1.4}},
     {3, {0.273, 0.706, 0.118, 0.262}},// 16x64 staged
 };
 // The small tiles (direct-to-LDS, NN only) on the problems they fill: their
