@@ -102,6 +102,41 @@ def test_integer_inputs_bit_exact(M, N, K):
     assert np.array_equal(got, want), f"{np.sum(got != want)} mismatches"
 
 
+# Each tile walks K from a step set by its position; with a K tail (K not a
+# multiple of the step) the partial step lands anywhere in the walk. Integer
+# inputs keep every fp32 sum exact, so any walk order must give the oracle's
+# bits: the 256 x 256 tile past one round (where it skews), the 64 x 256 and
+# 64 x 64 tiles, operands as stored and transposed.
+SKEW_CASES = [(0, 4160, 4160, 1000, False, False), (0, 4160, 4160, 1000, True, True), (0, 4160, 4160, 1000, False, True),
+              (10, 1088, 1024, 1000, False, False), (10, 1088, 1024, 1000, True, False),
+              (11, 1088, 1088, 1000, False, False), (9, 2112, 2048, 1000, False, False)]
+
+
+@pytest.mark.parametrize("tile,M,N,K,ta,tb", SKEW_CASES)
+def test_skewed_k_walk_with_k_tail_bit_exact(tile, M, N, K, ta, tb):
+    say(f"[skew] tile={tile} {gr.tile_name(tile)} M={M} N={N} K={K} ta={ta} tb={tb}")
+    a, b = workloads.make_inputs(M, N, K, dist="intsmall", seed=M + 3 * N + 7 * K + tile)
+    a_st = a.t().contiguous() if ta else a
+    b_st = b.t().contiguous() if tb else b
+    c = gr.gemm_relu(a_st.cuda(), b_st.cuda(), trans_a=ta, trans_b=tb, tile=tile)
+    torch.cuda.synchronize()
+    got = workloads.as_u16(c.cpu())
+    A, B = workloads.as_u16(a), workloads.as_u16(b)
+    if M * N * K <= 2 ** 31:
+        want = oracle.gemm_relu_f16(A, B)
+        assert np.array_equal(got, want), f"{np.sum(got != want)} mismatches"
+    else:
+        # whole rows at the start, middle and end: every column tile, every
+        # row tile's position in its group
+        for r0 in (0, M // 2 - 4, M - 8):
+            want = oracle.gemm_relu_f16(A, B, rows=(r0, r0 + 8))
+            assert np.array_equal(got[r0:r0 + 8], want), f"rows {r0}: {np.sum(got[r0:r0 + 8] != want)} mismatches"
+        rng = np.random.default_rng(M + K)
+        ii, jj = rng.integers(0, M, 4096), rng.integers(0, N, 4096)
+        want = oracle.gemm_relu_f16_points(A, B, ii, jj)
+        assert np.array_equal(got[ii, jj], want), f"{np.sum(got[ii, jj] != want)} point mismatches"
+
+
 EDGE = [1, 7, 8, 9, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 257]
 
 
