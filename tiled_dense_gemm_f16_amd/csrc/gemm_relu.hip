@@ -318,8 +318,9 @@ constexpr AutoTile kAutoTiles[] = {
 // of A or B that are not whole 128-byte lines take more L2 requests (1000 x
 // 1016 x 1000: 13.6 us against 9.1 at 1024^3). The three constants were
 // chosen on a sweep of 46 shapes (every tile and block order, inputs from
-// HBM) for the choices they lead to against the other tiles' predictions:
-// the default launch is 1.023x the fastest on average, 1.135x at worst.
+// HBM) for the choices they lead to against the other tiles' predictions
+// (the kernels have since become faster with their skewed K walks, which
+// left the choices as they were apart from 768^3, below).
 struct SmallTile {
     int id;
     bool one_round;  // only for grids of at most one workgroup per CU
