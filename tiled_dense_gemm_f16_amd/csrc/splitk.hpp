@@ -19,7 +19,8 @@
 //    eight consecutive columns (8 x 16 bytes; a load instruction covers four
 //    rows x 256 contiguous bytes) and transposes the 8 x 8 block in registers,
 //    which yields k-contiguous operands for v_mfma_f32_16x16x32_f16 without a
-//    trip through LDS. D = 4 steps of 32 rows are in flight per wave.
+//    trip through LDS. D steps of 32 rows are in flight per wave (the
+//    library uses 2).
 //  * The B fragment is the first MFMA operand. Matrix op e of a lane uses the
 //    columns 8 * (lane % 16) + e, so the sixteen results of one op are spread
 //    with stride 8, and after the eight ops each lane holds 32 consecutive
@@ -51,7 +52,7 @@
 namespace gemm_relu {
 namespace splitk {
 
-template <int MB_, int NW_ = 4, int D_ = 4>
+template <int MB_, int NW_ = 4, int D_ = 2>
 struct Cfg {
     static constexpr int MB = MB_;          // 16-row blocks
     static constexpr int BM = 16 * MB;
