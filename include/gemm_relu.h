@@ -77,9 +77,13 @@ typedef enum gemm_relu_status {
 /* Pass as gemm_relu_opts.tile to let the library choose. */
 #define GEMM_RELU_TILE_AUTO (-1)
 
-/* Block orders for gemm_relu_opts.block_order. */
-#define GEMM_RELU_ORDER_DEFAULT 0   /* XCD-aware grouped order */
-#define GEMM_RELU_ORDER_ROW_MAJOR 1 /* plain row-major tile order (ablation) */
+/*
+ * Block orders for gemm_relu_opts.block_order. GEMM_RELU_ORDER_DEFAULT with
+ * group_m > 0 is always the XCD-aware grouped order; with group_m = 0 the
+ * library picks the order (gemm_relu_default_order says which).
+ */
+#define GEMM_RELU_ORDER_DEFAULT 0   /* XCD-aware grouped order, or the library's pick */
+#define GEMM_RELU_ORDER_ROW_MAJOR 1 /* plain row-major tile order */
 
 /*
  * Optional launch choices. They change speed, never the set of admissible
@@ -207,6 +211,19 @@ typedef struct gemm_relu_tile_desc {
  * left untouched). Host-only; makes no HIP call.
  */
 int gemm_relu_tile_info(int tile, gemm_relu_tile_desc* desc);
+
+/*
+ * The block order and group size a launch of `tile` over an M x N output
+ * uses when opts leave both at their defaults (block_order
+ * GEMM_RELU_ORDER_DEFAULT, group_m 0), as chosen for the grid of tiles that
+ * the TileLang example's block-order swizzle (section "Escribamos un GEMM")
+ * walks: *block_order gets GEMM_RELU_ORDER_DEFAULT (grouped) or
+ * GEMM_RELU_ORDER_ROW_MAJOR, *group_m the tile-rows per group of the grouped
+ * order. Returns GEMM_RELU_EINVAL for a NULL pointer or a negative size and
+ * GEMM_RELU_EUNSUPPORTED for an unknown tile (outputs then left untouched).
+ * Host-only; makes no HIP call.
+ */
+int gemm_relu_default_order(int tile, int64_t M, int64_t N, int32_t* block_order, int32_t* group_m);
 
 /*
  * Transposed operands: the transpose_A / transpose_B flags of the tile-level

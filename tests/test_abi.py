@@ -148,7 +148,7 @@ def test_tuner_candidates():
     # default group 8 -> 4)
     c384 = tune.candidates(384, 6144, 6144)
     t64 = next(t for t in range(gr.tile_count()) if gr.tile_name(t).startswith("64x64x64s4"))
-    g_def = tune.default_group(gr.tile_info(t64)["default_group_m"], 6)
+    g_def = gr.default_order(t64, 384, 6144)[1]
     assert g_def == 4
     assert any(x["tile"] == t64 and x["block_order"] == gr.ORDER_DEFAULT and x["group_m"] == g_def for x in c384)
     # a grid one tile-row high has no block order to choose
@@ -158,15 +158,49 @@ def test_tuner_candidates():
     assert small and all(gr.tile_info(x["tile"])["lds_bytes"] <= 64 * 1024 for x in small)
 
 
-def test_default_group_rule():
-    from tiled_dense_gemm_f16_amd import tune
+def _tile_named(prefix):
+    return next(t for t in range(gr.tile_count()) if gr.tile_name(t).startswith(prefix))
 
+
+def test_default_group_rule():
     # (tile default, tile-rows) -> group: a power of two, at least two groups
-    # from four tile-rows on
+    # from four tile-rows on (tile-columns do not matter)
+    tiles = {8: _tile_named("64x64x64s4"), 4: _tile_named("256x256x32s4_w2x2"), 1: _tile_named("16x64x64")}
     cases = {(8, 16): 8, (8, 8): 4, (8, 6): 4, (8, 4): 2, (8, 3): 2, (8, 2): 2, (8, 1): 1,
-             (4, 16): 4, (4, 4): 2, (4, 5): 4, (1, 16): 1, (16, 1024): 16}
+             (4, 16): 4, (4, 4): 2, (4, 5): 4, (1, 16): 1}
     for (g, tm), want in cases.items():
-        assert tune.default_group(g, tm) == want, (g, tm)
+        t = tiles[g]
+        d = gr.tile_info(t)
+        assert d["default_group_m"] == g
+        for N in (64, 8192):
+            assert gr.default_order(t, tm * d["bm"], N)[1] == want, (g, tm, N)
+        # a ragged last tile-row counts as a row
+        assert gr.default_order(t, (tm - 1) * d["bm"] + 1, 64)[1] == want, (g, tm)
+
+
+def test_default_order_rule():
+    # row-major only on grids of one round (<= 256 tiles) of tiles under 256
+    # rows, two tile-rows or more, a multiple of 4 tile-columns and at most
+    # twice as many tile-rows as tile-columns
+    t64, t32 = _tile_named("64x64x64s4"), _tile_named("32x64x64s4")
+    t256, t64x256 = _tile_named("256x256x32s4_w2x2"), _tile_named("64x256x32s5")
+    tsk = _tile_named("splitk_64x128")
+    RM, G = gr.ORDER_ROW_MAJOR, gr.ORDER_DEFAULT
+    cases = [(t64, 1024, 1024, RM), (t64, 1024, 512, RM), (t64, 1088, 512, G), (t64, 4096, 4096, G),
+             (t64, 960, 960, G), (t64, 64, 8192, G), (t64, 128, 8192, RM), (t64, 2560, 640, G),
+             (t32, 256, 256, RM), (t32, 512, 512, RM), (t256, 1024, 1024, G), (t256, 4096, 4096, G),
+             (t64x256, 2048, 2048, G), (t64x256, 1024, 4096, RM), (t64x256, 4096, 1024, G), (tsk, 64, 1024, G),
+             (t64, 0, 0, G)]
+    for t, M, N, want in cases:
+        assert gr.default_order(t, M, N)[0] == want, (gr.tile_name(t), M, N)
+    lib = gr.load()
+    o, g = ctypes.c_int32(7), ctypes.c_int32(7)
+    assert lib.gemm_relu_default_order(gr.tile_count(), 64, 64, ctypes.byref(o), ctypes.byref(g)) == gr.EUNSUPPORTED
+    assert lib.gemm_relu_default_order(-1, 64, 64, ctypes.byref(o), ctypes.byref(g)) == gr.EUNSUPPORTED
+    assert lib.gemm_relu_default_order(0, -1, 64, ctypes.byref(o), ctypes.byref(g)) == gr.EINVAL
+    assert lib.gemm_relu_default_order(0, 64, 64, None, ctypes.byref(g)) == gr.EINVAL
+    assert lib.gemm_relu_default_order(0, 64, 64, ctypes.byref(o), None) == gr.EINVAL
+    assert (o.value, g.value) == (7, 7)
 
 
 def test_timing_rotation_covers_the_last_level_cache():

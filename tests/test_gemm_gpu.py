@@ -105,10 +105,12 @@ def test_integer_inputs_bit_exact(M, N, K):
 # Each tile walks K from a step set by its position; with a K tail (K not a
 # multiple of the step) the partial step lands anywhere in the walk. Integer
 # inputs keep every fp32 sum exact, so any walk order must give the oracle's
-# bits: the 256 x 256 tile past one round (where it skews), the 64 x 256 and
-# 64 x 64 tiles, operands as stored and transposed.
+# bits: the 256 x 256 tile past one round (where it skews), the 64 x 256
+# tiles with four and five slots and the 64 x 64 tile, operands as stored and
+# transposed.
 SKEW_CASES = [(0, 4160, 4160, 1000, False, False), (0, 4160, 4160, 1000, True, True), (0, 4160, 4160, 1000, False, True),
               (10, 1088, 1024, 1000, False, False), (10, 1088, 1024, 1000, True, False),
+              (13, 1088, 1024, 1000, False, False), (13, 1088, 1024, 1000, False, True),
               (11, 1088, 1088, 1000, False, False), (9, 2112, 2048, 1000, False, False)]
 
 

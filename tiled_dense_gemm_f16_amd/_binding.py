@@ -53,8 +53,8 @@ _lib = None
 
 EXPORTED = ("gemm_relu_f16", "gemm_relu_f16_noalloc", "gemm_relu_f16_ex", "gemm_relu_f16_op", "gemm_bias_gelu_f16",
             "gemm_bias_gelu_f16_ex", "gemm_bias_gelu_f16_op", "gemm_relu_strerror", "gemm_relu_tile_count",
-            "gemm_relu_tile_name", "gemm_relu_tile_info", "gemm_relu_select_tile", "gemm_relu_select_tile_op",
-            "softmax_rows_f16", "flash_attn_fwd_f16")
+            "gemm_relu_tile_name", "gemm_relu_tile_info", "gemm_relu_default_order", "gemm_relu_select_tile",
+            "gemm_relu_select_tile_op", "softmax_rows_f16", "flash_attn_fwd_f16")
 
 
 def load():
@@ -96,6 +96,8 @@ def load():
         lib.gemm_relu_tile_name.restype = ctypes.c_char_p
         lib.gemm_relu_tile_info.argtypes = [i32, ctypes.POINTER(TileDesc)]
         lib.gemm_relu_tile_info.restype = i32
+        lib.gemm_relu_default_order.argtypes = [i32, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        lib.gemm_relu_default_order.restype = i32
         lib.gemm_relu_select_tile.argtypes = [i64, i64, i64, p, p, p]
         lib.gemm_relu_select_tile.restype = i32
         _lib = lib
@@ -177,6 +179,14 @@ def tile_info(tile: int) -> dict:
     d = TileDesc()
     _check(load().gemm_relu_tile_info(int(tile), ctypes.byref(d)))
     return d.as_dict()
+
+
+def default_order(tile: int, M: int, N: int) -> tuple[int, int]:
+    """(block_order, group_m) of a launch of `tile` over an M x N output whose
+    opts leave both at their defaults."""
+    order, group = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().gemm_relu_default_order(int(tile), int(M), int(N), ctypes.byref(order), ctypes.byref(group)))
+    return int(order.value), int(group.value)
 
 
 def select_tile(M: int, N: int, K: int, A: int = 0, B: int = 0, C: int = 0, *, trans_a: bool = False,

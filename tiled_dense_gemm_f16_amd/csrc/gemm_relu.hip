@@ -42,6 +42,12 @@ using P256W8 = gemm_relu::pipelined::Cfg<256, 256, 4, 2>; // 8 waves x 64x128: t
 using P256S5 = gemm_relu::pipelined::Cfg<256, 256, 2, 2, 5>; // five-slot ring: 4 steps in flight
 using P128 = gemm_relu::pipelined::Cfg<128, 256, 2, 2>;      // 4 waves x 64x128
 using P64 = gemm_relu::pipelined::Cfg<64, 256, 1, 2>;        // 2 waves x 64x128
+// The same with a five-slot ring (4 steps in flight, 100 KiB: one workgroup
+// per CU). On grids of at most one workgroup per CU it is 5-12 % faster
+// (2048^3 31.7 -> 30.0 us, 4096 x 1024 x 4096 57.4 -> 52.2, TN 256 x 8192 x
+// 8192 107.8 -> 94.3); on larger grids two four-slot workgroups share a CU
+// and the deeper ring loses (2560^3 with this tile: 48.6 -> 68.1 us).
+using P64S5 = gemm_relu::pipelined::Cfg<64, 256, 1, 2, 5>;
 using Q64 = gemm_relu::small::Cfg<64, 64, 2, 2, 2, 4>;     // 4 waves x 32x32, 64-deep steps, 4 slots
 using Q32 = gemm_relu::small::Cfg<32, 64, 1, 2, 2, 4>;     // 2 waves x 32x32, 64-deep steps, 4 slots
 using S256 = gemm_relu::staged::Tile<256, 256, 64, 2, 2>;  // generic instance of the same tile
@@ -200,8 +206,11 @@ const TileEntry kTiles[] = {
      launch_staged<S64, false>},
     {"32x64x64s4_w1x2_mfma32x32x16_lds-small", small_desc<Q32>(4), launch_small<Q32, S64>,
      launch_staged<S64, false>},
+    {"64x256x32s5_w1x2_mfma32x32x16_lds-dma", pipelined_desc<P64S5>(4), launch_pipelined<P64S5>,
+     launch_staged<S64, false>},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+constexpr int kP64Tile = 10, kP64S5Tile = 13;  // 64 x 256 with four and with five slots
 
 // The group a launch without opts uses: the tile's default, cut to a power of
 // two that leaves at least two groups when the grid has four tile-rows or
@@ -290,9 +299,10 @@ bool splitk_ok(int64_t M, int64_t K) { return M * K * 2 < ((int64_t)1 << 31); }
 // (M <= 32 with operands as stored, M <= 64 otherwise) always take a split-K
 // tile, and the 16x64 tile is only for latency-bound outputs of at most 64 K
 // elements. Over the offline sweeps the default launch (this model, the
-// small-tile model below and the group rule) is 1.4 % slower than the
-// measured fastest on average in NN (8 % at worst, 46 shapes) and 1.3-1.7 %
-// in the transposed layouts (5 % at worst, 12 shapes each). The rules it
+// small-tile model below, the group and block-order rules) is 1.4 % slower
+// than the measured fastest on average in NN (10 % at worst, on outputs 64
+// columns wide; 46 shapes) and 0.7-1.6 % in the transposed layouts (5 % at
+// worst, 12 shapes each). The rules it
 // replaced, which looked at M and the 256x256 tile count alone, were up to
 // 6x slower on shapes they were not written for.
 struct AutoTile {
@@ -368,6 +378,22 @@ Prediction predict(const AutoTile& at, int layout, int64_t M, int64_t N, int64_t
     return {(compute > memory ? compute : memory) + combine, compute};
 }
 
+// The block order of a launch whose opts leave it to the library. On a grid
+// of one round (every tile resident at once) of tiles of fewer than 256 rows,
+// with two tile-rows or more, a multiple of 4 tile-columns and at least half
+// as many tile-columns as tile-rows, plain row-major order ran 3-5 % faster
+// than the grouped one in two tile sweeps at 256^3, 512^3, 768^3 and 1024^3,
+// and 1-2 % on the wide skinny shapes (deep-K squares such as 1024 x 1024 x
+// 4096 land within +-5 % either way from run to run); the grouped order wins
+// on taller grids, on grids of several rounds and with the 256 x 256 tiles.
+int default_order(const gemm_relu_tile_desc& d, int64_t tiles_m, int64_t tiles_n)
+{
+    const bool one_round = tiles_m * tiles_n <= (int64_t)kComputeUnits;
+    return (!d.split_k && d.bm < 256 && one_round && tiles_m >= 2 && tiles_n % 4 == 0 && tiles_m <= 2 * tiles_n)
+               ? GEMM_RELU_ORDER_ROW_MAJOR
+               : GEMM_RELU_ORDER_DEFAULT;
+}
+
 // Predicted time of a small tile (operands as stored).
 double predict_small(const SmallTile& st, int64_t M, int64_t N, int64_t K)
 {
@@ -416,6 +442,8 @@ int choose_tile(int64_t M, int64_t N, int64_t K, bool ta, bool tb)
             }
         }
     }
+    // 64 x 256 on a grid of one round: the five-slot ring
+    if (best == kP64Tile && ((M + 63) / 64) * ((N + 255) / 256) <= (int64_t)kComputeUnits) best = kP64S5Tile;
     return best;
 }
 
@@ -645,6 +673,8 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B,
         a.group_m = default_group(te.desc.default_group_m, a.tiles_m);
     }
     a.order = opts ? opts->block_order : GEMM_RELU_ORDER_DEFAULT;
+    if (a.order == GEMM_RELU_ORDER_DEFAULT && !(opts && opts->group_m > 0))
+        a.order = default_order(te.desc, a.tiles_m, a.tiles_n);
     a.trans_a = ta ? 1 : 0;
     a.trans_b = tb ? 1 : 0;
     a.act = act;
@@ -723,6 +753,17 @@ int gemm_relu_tile_info(int tile, gemm_relu_tile_desc* desc)
     if (!desc) return GEMM_RELU_EINVAL;
     if (tile < 0 || tile >= kNumTiles) return GEMM_RELU_EUNSUPPORTED;
     *desc = kTiles[tile].desc;
+    return GEMM_RELU_OK;
+}
+
+int gemm_relu_default_order(int tile, int64_t M, int64_t N, int32_t* block_order, int32_t* group_m)
+{
+    if (!block_order || !group_m || M < 0 || N < 0) return GEMM_RELU_EINVAL;
+    if (tile < 0 || tile >= kNumTiles) return GEMM_RELU_EUNSUPPORTED;
+    const gemm_relu_tile_desc& d = kTiles[tile].desc;
+    const int64_t tiles_m = (M + d.bm - 1) / d.bm, tiles_n = (N + d.bn - 1) / d.bn;
+    *group_m = default_group(d.default_group_m, (int)(tiles_m < INT32_MAX ? tiles_m : INT32_MAX));
+    *block_order = default_order(d, tiles_m, tiles_n);
     return GEMM_RELU_OK;
 }
 

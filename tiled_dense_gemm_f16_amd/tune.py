@@ -100,7 +100,7 @@ def candidates(M: int, N: int, K: int, lds_limit: int = LDS_PER_WORKGROUP) -> li
             out.append(base)
             continue
         # the library's own group (clamped to the tile-rows) is always a candidate
-        for g in sorted({g for g in GROUP_SIZES if g <= tm} | {default_group(d["default_group_m"], tm)}):
+        for g in sorted({g for g in GROUP_SIZES if g <= tm} | {gr.default_order(t, M, N)[1]}):
             out.append(dict(base, group_m=g))
         out.append(dict(base, block_order=gr.ORDER_ROW_MAJOR))
     return out
@@ -240,27 +240,18 @@ def tune(M: int, N: int, K: int, *, epilogue: str = "relu", seed: int = 0, graph
             "default": _default_of(M, N, K, results, trans_a, trans_b)}
 
 
-def default_group(group: int, tiles_m: int) -> int:
-    """The group size a launch without opts uses (gemm_relu.hip's rule): the
-    tile's default cut to a power of two that leaves at least two groups when
-    there are four tile-rows or more."""
-    g = 1
-    while 2 * g <= group and 2 * g <= tiles_m:
-        g *= 2
-    if g == tiles_m and tiles_m >= 4:
-        g //= 2
-    return g
-
-
 def _default_of(M, N, K, results, trans_a=False, trans_b=False):
     """The result of the launch the library makes without opts, if it was timed."""
     auto = gr.select_tile(M, N, K, trans_a=trans_a, trans_b=trans_b)
     if auto < 0:
         return None
-    info = gr.tile_info(auto)
-    g = default_group(info["default_group_m"], -(-M // info["bm"]))
+    order, g = gr.default_order(auto, M, N)
     for r in results:
-        if r["tile"] == auto and r["block_order"] == gr.ORDER_DEFAULT and r["group_m"] in (0, g):
+        if r["tile"] != auto:
+            continue
+        if r["block_order"] == order == gr.ORDER_ROW_MAJOR:
+            return r
+        if r["block_order"] == order == gr.ORDER_DEFAULT and r["group_m"] in (0, g):
             return r
     return None
 
