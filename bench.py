@@ -660,6 +660,10 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=workloads.SQUARE_4096.name, choices=sorted(workloads.BY_NAME))
     ap.add_argument("--tile", type=int, default=None, help="pin a tile id (default: library's choice)")
+    ap.add_argument("--input-dist", choices=("normal", "uniform", "intsmall", "ones"), default=None,
+                    help="ablation: draw the workload's inputs from another distribution (intsmall: integers "
+                         "in [-2, 2]; ones: every element 1), to show how operand bit activity sets the "
+                         "clock the chip holds; the line is then not the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--all", action="store_true", help="also time every workload (lines on stderr)")
@@ -736,6 +740,8 @@ def main(argv=None) -> int:
         return 0
 
     w = workloads.BY_NAME[args.workload]
+    if args.input_dist:
+        w = workloads.with_dist(w, args.input_dist)
     r = time_gpu(w, args.steps, args.warmup, args.tile, args.graph, args.epilogue, args.layout,
                  args.rotate_mib << 20, args.steady_ms)
     print(f"[bench] {w.name}: {r['ms_per_step'] * 1e3:.2f} us/step (graph batch {r['graph_batch']}), "
@@ -806,7 +812,11 @@ def main(argv=None) -> int:
     cpu = None
     if not args.no_cpu_baseline and args.epilogue == "relu" and args.layout == "nn":
         cpu = cpu_baseline(w, r, args.cpu_seconds)
-    print(json.dumps(result_line(w, r, args.steps, args.warmup, cpu)), flush=True)
+    line = result_line(w, r, args.steps, args.warmup, cpu)
+    if args.input_dist:
+        line["note"] = (f"ablation: inputs drawn from {args.input_dist!r} instead of the workload's own; the "
+                        "headline is the workload's own inputs")
+    print(json.dumps(line), flush=True)
     return 0
 
 

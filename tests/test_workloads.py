@@ -43,3 +43,16 @@ def test_shard_draws_the_same_a_as_the_full_problem():
     a_shard, b_shard = workloads.workload_inputs(workloads.n_shard(base, 4))
     assert torch.equal(a_full, a_shard)
     assert b_shard.shape == (32, 16)
+
+
+def test_input_distribution_ablation():
+    w = workloads.with_dist(workloads.SQUARE_4096, "ones")
+    assert (w.M, w.N, w.K, w.seed) == (4096, 4096, 4096, 0) and w.dist == "ones"
+    assert w.name.endswith("_inputs-ones") and w.name not in workloads.BY_NAME
+    assert workloads.with_dist(workloads.SQUARE_4096, "normal") is workloads.SQUARE_4096
+    a, b = workloads.make_inputs(8, 4, 16, "ones")
+    assert a.shape == (8, 16) and b.shape == (16, 4)
+    assert torch.all(a == 1) and torch.all(b == 1) and a.dtype == torch.float16
+    small = workloads.with_dist(workloads.SKINNY, "intsmall")
+    a, b = workloads.workload_inputs(workloads.Workload("t", 8, 8, 8, small.dist, small.scale))
+    assert set(torch.unique(torch.cat([a.flatten(), b.flatten()])).tolist()) <= {-2.0, -1.0, 0.0, 1.0, 2.0}

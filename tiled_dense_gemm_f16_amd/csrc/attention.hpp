@@ -148,10 +148,12 @@ __global__ void __launch_bounds__(256) softmax_rows_any(SoftmaxArgs a)
 // value tiles with a running maximum and sum, and the score matrix never goes
 // to memory).
 //
-//  * A workgroup owns BM = 128 query rows of one (batch, head): 4 waves of 32
-//    rows. Two workgroups share a CU (two waves per SIMD) and run out of step
-//    with each other, so one's softmax arithmetic overlaps the other's
-//    matrix ops; the small workgroup also evens out causal work.
+//  * A workgroup owns BM = 32 NW query rows of one (batch, head): NW waves of
+//    32 rows, two waves per SIMD. With NW = 4 two workgroups share a CU and
+//    run out of step with each other, so one's softmax arithmetic overlaps
+//    the other's matrix ops, and the small workgroup evens out causal work;
+//    with NW = 8 (D = 128 without the mask) one workgroup fills the CU and
+//    each K and V tile is loaded into LDS once for 256 query rows.
 //  * Key and value tiles of BN = 64 rows go global -> LDS with direct 1 KiB
 //    buffer loads into two LDS stages (one array per stage and operand), the
 //    next tile in flight while the current one is used; rows past the

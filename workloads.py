@@ -28,7 +28,7 @@ class Workload:
     M: int
     N: int
     K: int
-    dist: str          # "normal" or "uniform"
+    dist: str          # "normal" or "uniform" (also "intsmall", "ones")
     scale: float       # standard deviation (normal) or half-width (uniform)
     seed: int = 0
 
@@ -65,6 +65,15 @@ def n_shard(w: Workload, ways: int) -> Workload:
     return Workload(name, w.M, n, w.K, w.dist, w.scale, w.seed)
 
 
+def with_dist(w: Workload, dist: str) -> Workload:
+    """The same shape and seed with inputs drawn from `dist` (an ablation of
+    the input values: the time of a product depends on its operands' bit
+    activity through the power the chip draws). The name records the change."""
+    if dist == w.dist:
+        return w
+    return Workload(f"{w.name}_inputs-{dist}", w.M, w.N, w.K, dist, 1.0, w.seed)
+
+
 # One GPU's share of the headline square problem and of the skinny one under
 # 2-, 4- and 8-way column splits.
 SHARDS = tuple(n_shard(w, ways) for w in (SQUARE_4096, SKINNY) for ways in (2, 4, 8))
@@ -83,6 +92,9 @@ def _draw(gen: torch.Generator, shape, dist: str, scale: float) -> torch.Tensor:
         # integers in {-2,...,2}: every partial sum of K <= 4096 such products
         # stays below 2**24 and is therefore exact in fp32 in any order
         x = torch.randint(-2, 3, shape, generator=gen).to(torch.float32)
+    elif dist == "ones":
+        # every element equal to `scale`: operands whose bits never change
+        x = torch.full(shape, float(scale), dtype=torch.float32)
     else:
         raise ValueError(f"unknown distribution {dist!r}")
     return x.to(torch.float16)
