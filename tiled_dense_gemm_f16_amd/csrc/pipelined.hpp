@@ -139,7 +139,7 @@ __device__ __forceinline__ int c_swz(int r) { return r & 31; }
 
 // Which memory items follow the matrix op at each position of a region of
 // 2 * NMMA ops (positions 0..NMMA-1 use fragments y, the rest x). Positions
-// up to PRE hold the barrier and the descriptors. After them:
+// up to PRE hold the barrier. After them:
 //  * the NSLOT read slots of x, one per position, all before block x starts;
 //  * the NSLOT read slots of y, one per position from the start of block x
 //    (after the last op that reads y);
@@ -266,42 +266,77 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         }
     }
 
-    // Buffer descriptors of step kt. Steps past the end of K get empty
+    // Buffer descriptors of the steps. Step kt reads the K columns [k0, k0 +
+    // BK), k0 = ((kt + kskew) % nk) * BK; steps past the end of K get empty
     // descriptors: every lane is out of range and the stage fills with zeros.
+    // A cursor walks the steps with a few scalar additions (recomputing a
+    // step's descriptors from kt took a modulo and 64-bit products, some 60
+    // scalar instructions in a row that held up the matrix ops behind them).
     struct Rsrc {
         __amdgpu_buffer_rsrc_t a, b;
+        int kleft;  // K columns from the step's first to the end of K (0 past the end)
     };
-    auto descriptors = [&](int kt) -> Rsrc {
-        const bool live = kt < nk;
-        const int k0 = live ? ((kt + kskew) % nk) * T::BK : 0;
-        int64_t arem = TA ? ((int64_t)K - k0) * M * 2 : ((int64_t)(M - m0) * K - k0) * 2;
-        int64_t brem = TB ? ((int64_t)(N - n0) * K - k0) * 2 : ((int64_t)K - k0) * N * 2;
-        arem = live ? arem : 0;
-        brem = live ? brem : 0;
-        const uint16_t* abase = TA ? p.A + (int64_t)k0 * M : p.A + (int64_t)m0 * K + k0;
-        const uint16_t* bbase = TB ? p.B + (int64_t)n0 * K + k0 : p.B + (int64_t)k0 * N;
-        return {make_rsrc(abase, (uint64_t)arem), make_rsrc(bbase, (uint64_t)brem)};
+    struct Cursor {
+        int kt, s;            // the step, and its place in the walk: k0 = s * BK
+        uint64_t aoff, boff;  // byte offsets of column k0 from column 0
     };
-    // Load number i (A loads first, then B loads) of step kt into stage S.
+    const char* const abase0 = reinterpret_cast<const char*>(TA ? p.A : p.A + (int64_t)m0 * K);
+    const char* const bbase0 = reinterpret_cast<const char*>(TB ? p.B + (int64_t)n0 * K : p.B);
+    const uint64_t arem0 = TA ? (uint64_t)K * M * 2 : (uint64_t)(M - m0) * K * 2;
+    const uint64_t brem0 = TB ? (uint64_t)(N - n0) * K * 2 : (uint64_t)K * N * 2;
+    // bytes per step (below 2^31: 32 M and 32 N halves are below 2^30)
+    const uint32_t astep = TA ? (uint32_t)(T::BK * 2) * (uint32_t)M : (uint32_t)(T::BK * 2);
+    const uint32_t bstep = TB ? (uint32_t)(T::BK * 2) : (uint32_t)(T::BK * 2) * (uint32_t)N;
+    auto cursor_at = [&](int kt) -> Cursor {
+        const int s = nk > 0 ? (kt + kskew) % nk : 0;
+        return {kt, s, (uint64_t)s * astep, (uint64_t)s * bstep};
+    };
+    auto advance = [&](Cursor& c) {
+        c.kt += 1;
+        const bool wrap = c.s + 1 == nk;
+        c.s = wrap ? 0 : c.s + 1;
+        c.aoff = wrap ? 0 : c.aoff + astep;
+        c.boff = wrap ? 0 : c.boff + bstep;
+    };
+    // the descriptor's record count: the bytes left, at most kMaxRecords
+    // (2^31), in 32-bit scalar operations: the compiler would otherwise fold
+    // the test into a 64-bit comparison, which goes through vector registers
+    auto records = [](uint64_t bytes, bool live) -> int {
+        uint32_t hi = (uint32_t)(bytes >> 32);
+        const uint32_t lo = (uint32_t)bytes;
+        asm("" : "+s"(hi));
+        const uint32_t n = (hi | (lo >> 31)) != 0 ? (uint32_t)kMaxRecords : lo;
+        return live ? (int)n : 0;
+    };
+    auto desc_a = [&](const Cursor& c) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase0 + c.aoff), (short)0,
+                                                 records(arem0 - c.aoff, c.kt < nk), kRsrcWord3);
+    };
+    auto desc_b = [&](const Cursor& c) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(bbase0 + c.boff), (short)0,
+                                                 records(brem0 - c.boff, c.kt < nk), kRsrcWord3);
+    };
+    auto descriptors = [&](const Cursor& c) -> Rsrc {
+        return {desc_a(c), desc_b(c), c.kt < nk ? K - c.s * T::BK : 0};
+    };
+    // Load number i (A loads first, then B loads) of the step of r into stage S.
     // (The descriptor is copied into a local first: handing the builtin a
     // member of a reference keeps the host side from emitting the kernel.)
-    auto load_one = [&]<int S>(int i, const Rsrc& r, int kt) {
+    auto load_one = [&]<int S>(int i, const Rsrc& r) {
         uint16_t* sa = stage_a.template operator()<S>();
         uint16_t* sb = stage_b.template operator()<S>();
         if (i < T::A_LOADS_W) {
             const __amdgpu_buffer_rsrc_t ra = r.a;
             uint32_t off = a_off[i];
             // a k-contiguous tile masks the K tail per lane
-            if constexpr (!KALIGNED && !TA)
-                off = (kt < nk && ((kt + kskew) % nk) * T::BK + a_kc[i] * 8 < K) ? off : kOOB;
+            if constexpr (!KALIGNED && !TA) off = (a_kc[i] * 8 < r.kleft) ? off : kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (GR_LDS void*)(sa + (wave * T::A_LOADS_W + i) * 512), 16, (int)off, 0, 0, 0);
         } else {
             const __amdgpu_buffer_rsrc_t rb = r.b;
             const int j = i - T::A_LOADS_W;
             uint32_t off = b_off[j];
-            if constexpr (!KALIGNED && TB)
-                off = (kt < nk && ((kt + kskew) % nk) * T::BK + b_kc[j] * 8 < K) ? off : kOOB;
+            if constexpr (!KALIGNED && TB) off = (b_kc[j] * 8 < r.kleft) ? off : kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rb, (GR_LDS void*)(sb + (wave * T::B_LOADS_W + j) * 512), 16, (int)off, 0, 0, 0);
         }
@@ -413,6 +448,8 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     constexpr int R = T::STAGES, AHEAD = T::STAGES - 1;  // loads run AHEAD steps ahead
     const int nkr = (nk + R - 1) / R * R;
     Frag x, y;
+    Cursor cur = cursor_at(0);  // the next step to load
+    Rsrc r, rn;                 // its descriptors, and the following step's
 
     // The code of region kt (S = kt % R): 2 * NMMA matrix ops, those of step
     // kt, second half (fragments y), then those of step kt+1, first half
@@ -422,10 +459,14 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     //    have landed (later steps may still be in flight) and its fragment
     //    reads are done, and after it every wave's have. The first kPre ops of y do not depend on it and are
     //    issued first, so the matrix cores have work while the waves meet.
-    //  * at position kPre: the descriptors of step kt+AHEAD;
     //  * then the read slots of step kt+1's first half (into x, needed by
     //    block x), from the start of block x the read slots of its second
-    //    half (into y), and the loads of step kt+AHEAD spread over the region.
+    //    half (into y), and the loads of step kt+AHEAD spread over the region;
+    //  * from position kAdv on, one item per position: the cursor moves on
+    //    and the descriptors of step kt+AHEAD+1 are made for the next region
+    //    (a short run of scalar instructions per position, which issue while
+    //    the matrix ops run); they replace the current ones after the last
+    //    load.
     // A wave issues instructions in order, so whatever sits between two
     // matrix ops must issue within one op's 32 cycles or the matrix core
     // idles; the four waves' 32 one-kilobyte direct-to-LDS loads of a step,
@@ -436,19 +477,27 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     using Plan = RegionPlan<T::NMMA, T::NSLOT, T::LPT, kPre>;
     static_assert(kPre >= 0 && Plan::fits(), "the region has too few matrix ops for its reads and loads");
     constexpr Plan plan;
-    auto region = [&]<int S>(int kt) {
+    constexpr int kNext = 2 * T::NMMA - 1;
+    constexpr int kAdv = kPre + 1 + T::NSLOT;
+    static_assert(kAdv + 3 < kNext, "the region has room for the cursor");
+    auto region = [&]<int S>() {
         constexpr int S1 = (S + 1) % R, SL = (S + AHEAD) % R;
-        Rsrc r;
 #pragma unroll
         for (int q = 0; q < 2 * T::NMMA; ++q) {
             // step kt+1 has landed (steps up to kt+AHEAD-1 may still be in flight)
             if (q == kPre) sync.template operator()<(AHEAD - 2) * T::LPT>();
             if (q < T::NMMA) mma_one(y, q);
             else mma_one(x, q - T::NMMA);
-            if (q == kPre) r = descriptors(kt + AHEAD);
-            if (plan.load[q] >= 0) load_one.template operator()<SL>(plan.load[q], r, kt + AHEAD);
+            if (plan.load[q] >= 0) load_one.template operator()<SL>(plan.load[q], r);
             if (plan.readx[q] >= 0) read_slot.template operator()<S1>(0, plan.readx[q], x);
             if (plan.ready[q] >= 0) read_slot.template operator()<S1>(1, plan.ready[q], y);
+            if (q == kAdv) advance(cur);
+            if (q == kAdv + 1) rn.a = desc_a(cur);
+            if (q == kAdv + 3) {
+                rn.b = desc_b(cur);
+                rn.kleft = cur.kt < nk ? K - cur.s * T::BK : 0;
+            }
+            if (q == kNext) r = rn;
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -459,12 +508,14 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         [&]<int... I>(std::integer_sequence<int, I...>) {
             (
                 [&] {
-                    const Rsrc r0 = descriptors(I);
+                    const Rsrc r0 = descriptors(cur);
 #pragma unroll
-                    for (int i = 0; i < T::LPT; ++i) load_one.template operator()<I>(i, r0, I);
+                    for (int i = 0; i < T::LPT; ++i) load_one.template operator()<I>(i, r0);
+                    advance(cur);
                 }(),
                 ...);
         }(std::make_integer_sequence<int, AHEAD>{});
+        r = descriptors(cur);
         sync.template operator()<(AHEAD - 1) * T::LPT>();
         GR_STAMP(1);
 #pragma unroll
@@ -481,7 +532,7 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     // pass multiplies the first half of step nkr, a zero tile.
     for (int kt = 0; kt < nkr; kt += R) {
         [&]<int... S>(std::integer_sequence<int, S...>) {
-            (region.template operator()<S>(kt + S), ...);
+            (region.template operator()<S>(), ...);
         }(std::make_integer_sequence<int, R>{});
     }
     // the zero-filling loads past the end must land, and every wave must be

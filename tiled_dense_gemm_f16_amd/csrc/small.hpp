@@ -162,26 +162,62 @@ __global__ void __launch_bounds__(T::NT, T::NW >= 4 ? 2 : 3) small_kernel(Args p
         }
     }
 
+    // Descriptors of the steps. Step kt reads the K columns [k0, k0 + BK),
+    // k0 = ((kt + kskew) % nk) * BK; steps past the end of K get empty
+    // descriptors (every lane out of range: zeros). A cursor walks the steps
+    // with a few scalar additions, and the next step's descriptors are made
+    // a piece at a time between the matrix ops (built from kt at once, they
+    // were a run of some 60 scalar instructions in front of the barrier).
     struct Rsrc {
         __amdgpu_buffer_rsrc_t a, b;
+        int kleft;  // K columns from the step's first to the end of K (0 past the end)
     };
-    // Descriptors of step kt; steps past the end of K get empty ones (zeros).
-    auto descriptors = [&](int kt) -> Rsrc {
-        const bool live = kt < nk;
-        const int k0 = live ? ((kt + kskew) % nk) * T::BK : 0;
-        const int64_t arem = live ? ((int64_t)(M - m0) * K - k0) * 2 : 0;
-        const int64_t brem = live ? ((int64_t)K - k0) * N * 2 : 0;
-        const int kk = live ? k0 : 0;
-        return {make_rsrc(p.A + (int64_t)m0 * K + kk, (uint64_t)arem), make_rsrc(p.B + (int64_t)kk * N, (uint64_t)brem)};
+    struct Cursor {
+        int kt, s;            // the step, and its place in the walk: k0 = s * BK
+        uint64_t aoff, boff;  // byte offsets of column k0 from column 0
     };
-    // this wave's load i of step kt into ring slot S
-    auto load_one = [&]<int S>(int i, const Rsrc& r, int kt) {
+    const char* const abase0 = reinterpret_cast<const char*>(p.A + (int64_t)m0 * K);
+    const char* const bbase0 = reinterpret_cast<const char*>(p.B);
+    const uint64_t arem0 = (uint64_t)(M - m0) * K * 2, brem0 = (uint64_t)K * N * 2;
+    const uint32_t astep = T::BK * 2, bstep = (uint32_t)(T::BK * 2) * (uint32_t)N;  // N <= 2^24: at most 2^31
+    auto cursor_at = [&](int kt) -> Cursor {
+        const int s = nk > 0 ? (kt + kskew) % nk : 0;
+        return {kt, s, (uint64_t)s * astep, (uint64_t)s * bstep};
+    };
+    auto advance = [&](Cursor& c) {
+        c.kt += 1;
+        const bool wrap = c.s + 1 == nk;
+        c.s = wrap ? 0 : c.s + 1;
+        c.aoff = wrap ? 0 : c.aoff + astep;
+        c.boff = wrap ? 0 : c.boff + bstep;
+    };
+    // record count: the bytes left, at most 2^31, in 32-bit scalar operations
+    // (the compiler would otherwise fold the test into a 64-bit comparison,
+    // which goes through vector registers)
+    auto records = [](uint64_t bytes, bool live) -> int {
+        uint32_t hi = (uint32_t)(bytes >> 32);
+        const uint32_t lo = (uint32_t)bytes;
+        asm("" : "+s"(hi));
+        const uint32_t n = (hi | (lo >> 31)) != 0 ? (uint32_t)kMaxRecords : lo;
+        return live ? (int)n : 0;
+    };
+    auto desc_a = [&](const Cursor& c) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase0 + c.aoff), (short)0,
+                                                 records(arem0 - c.aoff, c.kt < nk), kRsrcWord3);
+    };
+    auto desc_b = [&](const Cursor& c) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(bbase0 + c.boff), (short)0,
+                                                 records(brem0 - c.boff, c.kt < nk), kRsrcWord3);
+    };
+    auto kleft = [&](const Cursor& c) { return c.kt < nk ? K - c.s * T::BK : 0; };
+    auto descriptors = [&](const Cursor& c) -> Rsrc { return {desc_a(c), desc_b(c), kleft(c)}; };
+    // this wave's load i of the step of r into ring slot S
+    auto load_one = [&]<int S>(int i, const Rsrc& r) {
         uint16_t* dst = slot.template operator()<S>() + ldst[i];
         if (is_a[i]) {
             const __amdgpu_buffer_rsrc_t ra = r.a;
             uint32_t off = goff[i];
-            if constexpr (!KALIGNED)
-                off = (kt < nk && ((kt + kskew) % nk) * T::BK + kcol[i] < K) ? off : kOOB;
+            if constexpr (!KALIGNED) off = (kcol[i] < r.kleft) ? off : kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (GR_LDS void*)dst, 16, (int)off, 0, 0, 0);
         } else {
             const __amdgpu_buffer_rsrc_t rb = r.b;
@@ -282,11 +318,14 @@ __global__ void __launch_bounds__(T::NT, T::NW >= 4 ? 2 : 3) small_kernel(Args p
     // multiple of R steps; the extra steps multiply zero tiles.
     const int nkr = (nk + R - 1) / R * R;
     constexpr int NMEM = T::LPW + T::NREAD;
-    auto region = [&]<int S>(int j, Frag& x, Frag& y) {
+    // after which matrix ops the cursor moves on and the next descriptors are made
+    constexpr int kAdvU = T::NMMA > 1 ? 1 : 0, kDescAU = T::NMMA > 2 ? 2 : T::NMMA - 1,
+                  kDescBU = T::NMMA > 3 ? 3 : T::NMMA - 1;
+    Cursor cur = cursor_at(0);  // the next step to load
+    Rsrc r, rn;                 // its descriptors, and the following step's
+    auto region = [&]<int S>(Frag& x, Frag& y) {
         constexpr int S1 = (S + 1) % R;
-        // the descriptors do not depend on the other waves: built before the wait
-        const Rsrc rs = descriptors(j + R);
-        __builtin_amdgcn_sched_barrier(0);
+        const Rsrc rs = r;  // step j + R
         sync.template operator()<(R - 2) * T::LPW>();
         int m = 0;
 #pragma unroll
@@ -296,11 +335,18 @@ __global__ void __launch_bounds__(T::NT, T::NW >= 4 ? 2 : 3) small_kernel(Args p
             const int m_end = (NMEM * (u + 1)) / T::NMMA;
 #pragma unroll
             for (; m < m_end; ++m) {
-                if (m < T::LPW) load_one.template operator()<S>(m, rs, j + R);
+                if (m < T::LPW) load_one.template operator()<S>(m, rs);
                 else read_one.template operator()<S1>(m - T::LPW, y);
+            }
+            if (u == kAdvU) advance(cur);
+            if (u == kDescAU) rn.a = desc_a(cur);
+            if (u == kDescBU) {
+                rn.b = desc_b(cur);
+                rn.kleft = kleft(cur);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        r = rn;
     };
 
     Frag x, y;
@@ -309,12 +355,14 @@ __global__ void __launch_bounds__(T::NT, T::NW >= 4 ? 2 : 3) small_kernel(Args p
         [&]<int... I>(std::integer_sequence<int, I...>) {
             (
                 [&] {
-                    const Rsrc r0 = descriptors(I);
+                    const Rsrc r0 = descriptors(cur);
 #pragma unroll
-                    for (int i = 0; i < T::LPW; ++i) load_one.template operator()<I>(i, r0, I);
+                    for (int i = 0; i < T::LPW; ++i) load_one.template operator()<I>(i, r0);
+                    advance(cur);
                 }(),
                 ...);
         }(std::make_integer_sequence<int, R>{});
+        r = descriptors(cur);
         sync.template operator()<(R - 1) * T::LPW>();
         GR_STAMP(1);
 #pragma unroll
@@ -323,8 +371,7 @@ __global__ void __launch_bounds__(T::NT, T::NW >= 4 ? 2 : 3) small_kernel(Args p
     // R regions per pass, fragments alternating between x and y
     for (int j = 0; j < nkr; j += R) {
         [&]<int... S>(std::integer_sequence<int, S...>) {
-            ((S % 2 == 0 ? region.template operator()<S>(j + S, x, y) : region.template operator()<S>(j + S, y, x)),
-             ...);
+            ((S % 2 == 0 ? region.template operator()<S>(x, y) : region.template operator()<S>(y, x)), ...);
         }(std::make_integer_sequence<int, R>{});
     }
     // the zero-filling loads past the end must land before the waves exit
