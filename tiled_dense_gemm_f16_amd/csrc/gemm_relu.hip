@@ -299,10 +299,11 @@ bool splitk_ok(int64_t M, int64_t K) { return M * K * 2 < ((int64_t)1 << 31); }
 // (M <= 32 with operands as stored, M <= 64 otherwise) always take a split-K
 // tile, and the 16x64 tile is only for latency-bound outputs of at most 64 K
 // elements. Over the offline sweeps the default launch (this model, the
-// small-tile model below, the group and block-order rules) is 1.4 % slower
-// than the measured fastest on average in NN (10 % at worst, on outputs 64
-// columns wide; 46 shapes) and 0.7-1.6 % in the transposed layouts (5 % at
-// worst, 12 shapes each). The rules it
+// small-tile model below, the group and block-order rules) is 1.5 % slower
+// than the measured fastest on average in NN (10 % at worst; 46 shapes) and
+// 2.2-3.4 % in the transposed layouts (12 shapes each; 19 % at worst, TT
+// 4096 x 64 x 4096, where the split-K tile is chosen over the 64 x 256 one).
+// The rules it
 // replaced, which looked at M and the 256x256 tile count alone, were up to
 // 6x slower on shapes they were not written for.
 struct AutoTile {
@@ -312,9 +313,9 @@ struct AutoTile {
 constexpr AutoTile kAutoTiles[] = {
     {0, {6.96, 5.78, 6.63, 6.10}},   // 256x256 pipelined
     {9, {5.24, 3.90, 4.96, 4.04}},   // 128x256 pipelined
-    {10, {3.21, 2.21, 2.79, 2.25}},  // 64x256 pipelined
+    {10, {3.21, 2.21, 3.49, 2.25}},  // 64x256 pipelined (TN: refit after the step-descriptor change)
     {6, {2.13, 1.15, 0.570, 0.517}}, // split-K 64x128
-    {5, {1.59, 0.772, 0.390, 0.344}},// split-K 32x128
+    {5, {1.48, 0.772, 0.390, 0.344}},// split-K 32x128
     {4, {1.12, 0.472, 0.408, 0.324}},// split-K 16x128
     {2, {0.895, 1.24, 0.429, 0.756}},// 64x64 staged
     // 128x128 staged: with B stored N x K (NT) it needs no transpose and beat
@@ -331,9 +332,13 @@ constexpr AutoTile kAutoTiles[] = {
 // of A or B that are not whole 128-byte lines take more L2 requests (1000 x
 // 1016 x 1000: 13.6 us against 9.1 at 1024^3). The three constants were
 // chosen on a sweep of 46 shapes (every tile and block order, inputs from
-// HBM) for the choices they lead to against the other tiles' predictions
-// (the kernels have since become faster with their skewed K walks, which
-// left the choices as they were apart from 768^3, below).
+// HBM) for the choices they lead to against the other tiles' predictions.
+// After the skewed K walks and the step-descriptor cursor made the small and
+// pipelined kernels faster, a coordinate search over the constants on a new
+// sweep of every layout (82 shapes) lowered the fixed part (2.25 -> 1.80 us),
+// the NN rate of the 32 x 128 split-K tile (1.59 -> 1.48) and the TN rate of
+// the 64 x 256 tile (2.79 -> 3.49): 4096 x 512 x 4096, 1024 x 64 x 8192 and
+// TN 4096 x 64 x 4096 now take the tiles that were 10-14 % faster there.
 struct SmallTile {
     int id;
     bool one_round;  // only for grids of at most one workgroup per CU
@@ -343,7 +348,7 @@ struct SmallTile {
 // round: with a partial second round (768^3: 288 workgroups) the units that
 // run two take twice as long (8.8 us against 7.2 for 64 x 64).
 constexpr SmallTile kSmallTiles[] = {{11, false}, {12, true}};
-constexpr double kSmallFixedUs = 2.25;
+constexpr double kSmallFixedUs = 1.80;
 // The rate model below predicts times that are, over the sweep, about
 // 1.455 x + 4.0 us short of the measured ones (4096^3: 77 -> 116 us, 2048^3:
 // 20.9 -> 34.4 us, 1024^3 split-K: 5.3 -> 11.9 us); a small tile's time is
