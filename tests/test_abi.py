@@ -396,12 +396,12 @@ def test_product_path_never_imports_the_oracle():
 
 
 def test_noalloc_refuses_oversized_scratch_before_any_hip_call():
-    # 32 rows over 65 tiles of 32 x 128: 2 splits, 2.03 MiB of partial sums,
+    # 32 rows over 33 tiles of 32 x 128: 4 splits, 2.03 MiB of partial sums,
     # more than the fixed array holds; refused before the device is touched
     F = 1 << 32  # never dereferenced
-    assert gr.tile_name(gr.select_tile(32, 8320, 8192)).startswith("splitk_32x128")
-    assert 2 * 32 * 8320 * 4 > gr.NOALLOC_MAX_PARTIAL_BYTES
-    assert gr.gemm_relu_f16_noalloc(32, 8320, 8192, F, 2 * F, 3 * F, 0) == gr.ETOOBIG
+    assert gr.tile_name(gr.select_tile(32, 4160, 8192)).startswith("splitk_32x128")
+    assert 4 * 32 * 4160 * 4 > gr.NOALLOC_MAX_PARTIAL_BYTES
+    assert gr.gemm_relu_f16_noalloc(32, 4160, 8192, F, 2 * F, 3 * F, 0) == gr.ETOOBIG
     assert "scratch" in gr.strerror(gr.ETOOBIG)
     # the same argument checks as gemm_relu_f16
     assert gr.gemm_relu_f16_noalloc(-1, 8, 8, F, 2 * F, 3 * F, 0) == gr.EINVAL
