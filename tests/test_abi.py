@@ -74,13 +74,14 @@ def test_tile_selection_is_host_only():
     # clear: few rows -> split-K tiles; otherwise the largest tile that still
     # fills the 256 compute units
     name = lambda *s: gr.tile_name(gr.select_tile(*s))  # noqa: E731
-    assert gr.select_tile(4096, 4096, 4096) == 0
+    # 256x256 with A stored M x K loaded two steps at a time (whole lines)
+    assert name(4096, 4096, 4096) == "256x256x32s4_w2x2_mfma32x32x16_lds-dma-a2"
     assert name(16, 8192, 8192).startswith("splitk_16x")
     assert name(1, 8192, 8192).startswith("splitk_16x")
     assert name(4096, 64, 4096).startswith("32x64x64s4_w1x2")  # narrow: 128 tiles of 32x64
     assert name(32, 8192, 8192).startswith("splitk_16x")     # few rows: split-K only
     assert name(64, 8192, 8192).startswith("32x64x64s4_w1x2")
-    assert gr.select_tile(3072, 3072, 3072) == 0  # 144 tiles of 256x256
+    assert name(3072, 3072, 3072).startswith("256x256x32s4_w2x2")  # 144 tiles of 256x256
     assert name(2560, 2560, 2560).startswith("128x256")  # 200 tiles
     assert name(2048, 2048, 2048).startswith("64x256")  # 256 tiles
     assert name(1024, 1024, 1024).startswith("64x64x64s4_w2x2_mfma32x32x16_lds-small")  # 256 tiles of 64x64
@@ -98,7 +99,8 @@ def test_tile_selection_is_host_only():
     for ta in (False, True):
         for tb in (False, True):
             assert tname(16, 8192, 8192, trans_a=ta, trans_b=tb).startswith("splitk_16x")  # few rows
-            assert gr.select_tile(4096, 4096, 4096, trans_a=ta, trans_b=tb) == 0
+            # the paired-A tile where A is stored M x K, the plain one where it is K x M
+            assert gr.select_tile(4096, 4096, 4096, trans_a=ta, trans_b=tb) == (0 if ta else 14)
     # the split-K kernel's 32-bit A offsets: M*K*2 must stay below 2^31
     assert "splitk" not in name(65536, 256, 16384)
     # K or N not a multiple of 8 -> the generic element-wise path

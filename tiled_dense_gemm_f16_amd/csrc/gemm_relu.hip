@@ -48,6 +48,9 @@ using P64 = gemm_relu::pipelined::Cfg<64, 256, 1, 2>;        // 2 waves x 64x128
 // 8192 107.8 -> 94.3); on larger grids two four-slot workgroups share a CU
 // and the deeper ring loses (2560^3 with this tile: 48.6 -> 68.1 us).
 using P64S5 = gemm_relu::pipelined::Cfg<64, 256, 1, 2, 5>;
+// 256 x 256 with A (stored M x K) loaded two steps at a time: whole 128-byte
+// lines per row, 256 L2 requests per step and CU instead of 384
+using P256AP = gemm_relu::pipelined::Cfg<256, 256, 2, 2, 4, true>;
 using Q64 = gemm_relu::small::Cfg<64, 64, 2, 2, 2, 4>;     // 4 waves x 32x32, 64-deep steps, 4 slots
 using Q32 = gemm_relu::small::Cfg<32, 64, 1, 2, 2, 4>;     // 2 waves x 32x32, 64-deep steps, 4 slots
 using S256 = gemm_relu::staged::Tile<256, 256, 64, 2, 2>;  // generic instance of the same tile
@@ -208,9 +211,12 @@ const TileEntry kTiles[] = {
      launch_staged<S64, false>},
     {"64x256x32s5_w1x2_mfma32x32x16_lds-dma", pipelined_desc<P64S5>(4), launch_pipelined<P64S5>,
      launch_staged<S64, false>},
+    {"256x256x32s4_w2x2_mfma32x32x16_lds-dma-a2", pipelined_desc<P256AP>(4), launch_pipelined<P256AP>,
+     launch_staged<S256, false>},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kP64Tile = 10, kP64S5Tile = 13;  // 64 x 256 with four and with five slots
+constexpr int kP256Tile = 0, kP256PairTile = 14;  // 256 x 256, and with A loaded two steps at a time
 
 // The group a launch without opts uses: the tile's default, cut to a power of
 // two that leaves at least two groups when the grid has four tile-rows or
@@ -449,6 +455,8 @@ int choose_tile(int64_t M, int64_t N, int64_t K, bool ta, bool tb)
     }
     // 64 x 256 on a grid of one round: the five-slot ring
     if (best == kP64Tile && ((M + 63) / 64) * ((N + 255) / 256) <= (int64_t)kComputeUnits) best = kP64S5Tile;
+    // 256 x 256 with A stored M x K: A loaded two steps at a time
+    if (best == kP256Tile && !ta) best = kP256PairTile;
     return best;
 }
 

@@ -66,9 +66,13 @@ namespace pipelined {
 // tiles one launch places one per compute unit (256 CUs)
 constexpr int kSkewTilesOneRound = 256;
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_ = 4>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_ = 4, bool APAIR_ = false>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = STAGES_;
+    // A stored M x K is loaded two steps at a time (128 bytes of each row:
+    // whole cache lines) into the A parts of two ring slots, rows 0-127 in
+    // the even slot and 128-255 in the odd one; steps 2p and 2p+1 share them.
+    static constexpr bool APAIR = APAIR_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int NW = WAVES_M * WAVES_N, NT = kWave * NW;
     static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;  // wave sub-tile
@@ -98,6 +102,9 @@ struct Cfg {
     static_assert(C_ROWS_FIT >= 32 && BM <= STAGES * C_ROWS_PER_STAGE, "the C tile must fit in the ring");
     static_assert(C_ROWS_PER_STAGE % C_ROWS_PER_PASS == 0, "a store pass stays in one slot");
     static_assert(BN == 256, "the epilogue maps 32 lanes x 16 B onto one row of C");
+    static constexpr int AP_LOADS_W = APAIR ? BM * 64 * 2 / 1024 / NW : 0;  // 1 KiB loads per wave per pair
+    static_assert(!APAIR || (BM == 256 && WAVES_M == 2 && NW == 4 && STAGES == 4),
+                  "paired A steps: 256 rows, two waves along M (128 rows each), a four-slot ring");
 };
 
 // A: row r of a stage holds 32 halves = four 16-byte chunks; logical chunk c
@@ -111,6 +118,13 @@ struct Cfg {
 // cycles as conflicts, as did bits 1-2, so gfx950 does not serve a 16-byte
 // read in groups of 16 consecutive lanes.
 __device__ __forceinline__ int a_swz(int r) { return (r >> 2) & 3; }
+
+// A with paired steps: row r holds 64 halves = eight 16-byte chunks (two
+// steps); logical chunk c sits at physical chunk c ^ ap_swz(r). Two rows fill
+// a 256-byte bank window, and (r / 2) % 8 gives the rows of each parity in
+// any 16 consecutive ones eight different chunks, so a fragment read of 16
+// rows at one logical chunk touches every bank once.
+__device__ __forceinline__ int ap_swz(int r) { return (r >> 1) & 7; }
 
 // B: row kr of a stage holds BN halves; logical chunk c sits at physical chunk
 // c ^ b_swz(kr). A transposing read touches four consecutive rows (kr % 4 =
@@ -173,7 +187,18 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     // (Two slots in one array would make the reads of either wait for the
     // loads into both.) Arrays past the ring's last slot are never referenced
     // and take no LDS.
-    constexpr int SLOT = T::A_HALVES + T::B_HALVES;
+    // Paired A (AP): the A pairs live in two arrays of their own and the B
+    // steps in four, so that every fragment read and every load names its
+    // array at compile time (a pointer chosen between two arrays at run time
+    // makes the compiler wait for every load in flight before each read).
+    constexpr bool AP = T::APAIR && !TA;
+    constexpr int SLOT = AP ? 8 : T::A_HALVES + T::B_HALVES;
+    __shared__ __attribute__((aligned(1024))) uint16_t pa0[AP ? T::BM * 64 : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t pa1[AP ? T::BM * 64 : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t sb0[AP ? T::B_HALVES : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t sb1[AP ? T::B_HALVES : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t sb2[AP ? T::B_HALVES : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t sb3[AP ? T::B_HALVES : 8];
     __shared__ __attribute__((aligned(1024))) uint16_t st0[SLOT];
     __shared__ __attribute__((aligned(1024))) uint16_t st1[SLOT];
     __shared__ __attribute__((aligned(1024))) uint16_t st2[SLOT];
@@ -193,7 +218,21 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         else if constexpr (S == 6) return st6;
         else return st7;
     };
-    auto stage_b = [&]<int S>() -> uint16_t* { return stage_a.template operator()<S>() + T::A_HALVES; };
+    auto stage_b = [&]<int S>() -> uint16_t* {
+        if constexpr (AP) {
+            static_assert(S >= 0 && S < 4, "ring slot");
+            if constexpr (S == 0) return sb0;
+            else if constexpr (S == 1) return sb1;
+            else if constexpr (S == 2) return sb2;
+            else return sb3;
+        } else {
+            return stage_a.template operator()<S>() + T::A_HALVES;
+        }
+    };
+    auto pair_a = [&]<int PS>() -> uint16_t* {
+        if constexpr (PS == 0) return pa0;
+        else return pa1;
+    };
 
     static_assert(!TA || (T::BM >= 64 && 512 % T::BM == 0), "a transposed A tile row is 64 to 512 halves");
     GR_STAMP_DECL;
@@ -223,6 +262,9 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         else
             kskew = (tm + tn) % nk;
     }
+    // paired A steps: a pair starts on an even step of the walk and never
+    // wraps inside it
+    if constexpr (AP) kskew = nk % 2 == 0 ? (kskew & ~1) : 0;
 
     // ---- per-lane global offsets of this wave's direct loads (bytes, relative
     // to the step's descriptor base: A + m0*K + k0 and B + k0*N) ----
@@ -245,6 +287,22 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
             a_kc[i] = 0;
             // rows past K are cut off by the descriptor's byte count
             a_off[i] = (m0 + c * 8 < M) ? (uint32_t)(kr * M + m0 + c * 8) * 2u : kOOB;
+        }
+    }
+    // paired A (AP): load v of a wave covers rows 64 wave + 8 v .. + 7, 128
+    // bytes each (16 bytes per lane), of the pair's two steps. The lane's
+    // chunk depends on v only through v % 2 (the swizzle repeats every 16
+    // rows), so two offsets serve all loads; rows past M lie beyond the
+    // descriptor's byte count and read as zeros.
+    uint32_t ap_off[2];
+    int ap_kc[2];  // logical k-chunk (0..7) of the lane within the pair
+    if constexpr (AP) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int row = wave * (T::BM / T::NW) + 8 * e + lane / 8;
+            const int c = (lane % 8) ^ ap_swz(row);
+            ap_kc[e] = c;
+            ap_off[e] = (uint32_t)(row * K + c * 8) * 2u;
         }
     }
     uint32_t b_off[T::B_LOADS_W];
@@ -323,9 +381,10 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     // (The descriptor is copied into a local first: handing the builtin a
     // member of a reference keeps the host side from emitting the kernel.)
     auto load_one = [&]<int S>(int i, const Rsrc& r) {
-        uint16_t* sa = stage_a.template operator()<S>();
         uint16_t* sb = stage_b.template operator()<S>();
         if (i < T::A_LOADS_W) {
+            uint16_t* sa = nullptr;
+            if constexpr (!AP) sa = stage_a.template operator()<S>();
             const __amdgpu_buffer_rsrc_t ra = r.a;
             uint32_t off = a_off[i];
             // a k-contiguous tile masks the K tail per lane
@@ -342,7 +401,30 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         }
     };
 
+    // Paired A: load v of the pair whose first step is that of r into pair
+    // array PS (rows of 64 halves).
+    auto load_pair = [&]<int PS>(int v, const Rsrc& r) {
+        const __amdgpu_buffer_rsrc_t ra = r.a;
+        uint32_t off = ap_off[v % 2] + (uint32_t)(32 * (v / 2)) * (uint32_t)K;  // 16 (v / 2) rows further
+        if constexpr (!KALIGNED) off = (ap_kc[v % 2] * 8 < r.kleft) ? off : kOOB;
+        const int row0 = wave * (T::BM / T::NW) + 8 * v;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (GR_LDS void*)(pair_a.template operator()<PS>() + row0 * 64), 16, (int)off, 0, 0, 0);
+    };
+    // B load j of the step of r into stage S
+    auto load_b = [&]<int S>(int j, const Rsrc& r) {
+        load_one.template operator()<S>(T::A_LOADS_W + j, r);
+    };
+
     // ---- per-lane LDS byte offsets of the fragment reads ----
+    // Paired A, step SP (0, 1) of the pair, half h: row wm*TM + 32i + lane%32
+    // of the pair array, logical chunk 4 SP + 2h + lane/32. The chunk of the
+    // second step differs from the first's in bit 2 only, so its byte offset
+    // is the first's with bit 6 flipped.
+    uint32_t ap_rd[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        ap_rd[h] = (wm * T::TM + lane % 32) * 128 + (((2 * h + lane / 32) ^ ap_swz(lane % 32)) * 16);
     // A block i, half h of a step: row wm*TM + 32i + lane%32, chunk 2h + lane/32.
     const int ar = wm * T::TM + lane % 32;
     uint32_t a_rd[2];
@@ -394,7 +476,8 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     // 1..FN are the B blocks (two transposing reads each), the rest the other
     // A blocks -- the first matrix operation needs only slots 0 and 1.
     auto read_slot = [&]<int S>(int half, int s, Frag& f) {
-        const char* sa = reinterpret_cast<const char*>(stage_a.template operator()<S>());
+        const char* sa = nullptr;
+        if constexpr (!AP) sa = reinterpret_cast<const char*>(stage_a.template operator()<S>());
         const char* sb = reinterpret_cast<const char*>(stage_b.template operator()<S>());
         auto tr_read = [](const char* base, int row_bytes) -> f16x8 {
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GR_LDS i16x4*)(base));
@@ -403,7 +486,11 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         };
         if (s == 0 || s > T::FN) {
             const int i = (s == 0) ? 0 : s - T::FN;
-            if constexpr (!TA) f.a[i] = *reinterpret_cast<const f16x8*>(sa + a_rd[half] + i * 32 * 64);
+            if constexpr (AP) {
+                constexpr int PS = S / 2, SP = S % 2;
+                const char* pa = reinterpret_cast<const char*>(pair_a.template operator()<PS>());
+                f.a[i] = *reinterpret_cast<const f16x8*>(pa + (ap_rd[half] ^ (64u * SP)) + i * 32 * 128);
+            } else if constexpr (!TA) f.a[i] = *reinterpret_cast<const f16x8*>(sa + a_rd[half] + i * 32 * 64);
             else f.a[i] = tr_read(sa + at_rd[i] + half * 16 * (T::BM * 2), T::BM * 2);
         } else {
             const int j = s - 1;
@@ -477,6 +564,23 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     using Plan = RegionPlan<T::NMMA, T::NSLOT, T::LPT, kPre>;
     static_assert(kPre >= 0 && Plan::fits(), "the region has too few matrix ops for its reads and loads");
     constexpr Plan plan;
+    // Paired A: even regions load B only; odd regions also load the A pair
+    // of steps kt+3 and kt+4 (loads 0 .. AP_LOADS_W-1 of the region)
+    using PlanE = RegionPlan<T::NMMA, T::NSLOT, T::B_LOADS_W, kPre>;
+    using PlanO = RegionPlan<T::NMMA, T::NSLOT, T::B_LOADS_W + T::AP_LOADS_W, kPre>;
+    static_assert(!AP || PlanO::fits(), "the region has too few matrix ops for its reads and loads");
+    constexpr PlanE plan_e;
+    constexpr PlanO plan_o;
+    // Loads allowed in flight at the barrier of region kt (S = kt % R): those
+    // issued after the last one step kt+1 needs. Plain: the previous region's.
+    // Paired A: step kt+1's B was loaded in region kt-2, its A pair in region
+    // kt-2 (kt+1 even) or earlier, so again the previous region's loads,
+    // which number B_LOADS_W after an even region and B_LOADS_W + AP_LOADS_W
+    // after an odd one.
+    auto wait_count = [](int s) constexpr -> int {
+        if constexpr (AP) return s % 2 == 1 ? T::B_LOADS_W : T::B_LOADS_W + T::AP_LOADS_W;
+        else return (AHEAD - 2) * T::LPT;
+    };
     constexpr int kNext = 2 * T::NMMA - 1;
     constexpr int kAdv = kPre + 1 + T::NSLOT;
     static_assert(kAdv + 3 < kNext, "the region has room for the cursor");
@@ -485,10 +589,18 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
 #pragma unroll
         for (int q = 0; q < 2 * T::NMMA; ++q) {
             // step kt+1 has landed (steps up to kt+AHEAD-1 may still be in flight)
-            if (q == kPre) sync.template operator()<(AHEAD - 2) * T::LPT>();
+            if (q == kPre) sync.template operator()<wait_count(S)>();
             if (q < T::NMMA) mma_one(y, q);
             else mma_one(x, q - T::NMMA);
-            if (plan.load[q] >= 0) load_one.template operator()<SL>(plan.load[q], r);
+            if constexpr (!AP) {
+                if (plan.load[q] >= 0) load_one.template operator()<SL>(plan.load[q], r);
+            } else if constexpr (S % 2 == 0) {
+                if (plan_e.load[q] >= 0) load_b.template operator()<SL>(plan_e.load[q], r);
+            } else {
+                const int v = plan_o.load[q];
+                if (v >= 0 && v < T::AP_LOADS_W) load_pair.template operator()<SL / 2>(v, r);
+                else if (v >= 0) load_b.template operator()<SL>(v - T::AP_LOADS_W, r);
+            }
             if (plan.readx[q] >= 0) read_slot.template operator()<S1>(0, plan.readx[q], x);
             if (plan.ready[q] >= 0) read_slot.template operator()<S1>(1, plan.ready[q], y);
             if (q == kAdv) advance(cur);
@@ -509,14 +621,26 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
             (
                 [&] {
                     const Rsrc r0 = descriptors(cur);
+                    if constexpr (!AP) {
 #pragma unroll
-                    for (int i = 0; i < T::LPT; ++i) load_one.template operator()<I>(i, r0);
+                        for (int i = 0; i < T::LPT; ++i) load_one.template operator()<I>(i, r0);
+                    } else {
+                        // steps 0 and 2 bring their A pairs, then every step its B
+                        if constexpr (I % 2 == 0) {
+#pragma unroll
+                            for (int v = 0; v < T::AP_LOADS_W; ++v) load_pair.template operator()<I / 2>(v, r0);
+                        }
+#pragma unroll
+                        for (int j = 0; j < T::B_LOADS_W; ++j) load_b.template operator()<I>(j, r0);
+                    }
                     advance(cur);
                 }(),
                 ...);
         }(std::make_integer_sequence<int, AHEAD>{});
         r = descriptors(cur);
-        sync.template operator()<(AHEAD - 1) * T::LPT>();
+        // step 0 has landed: in flight may stay what came after its B (plain:
+        // steps 1 and 2; paired: B(1), the pair of steps 2-3 and B(2))
+        sync.template operator()<AP ? 2 * T::B_LOADS_W + T::AP_LOADS_W : (AHEAD - 1) * T::LPT>();
         GR_STAMP(1);
 #pragma unroll
         for (int s = 0; s < T::NSLOT; ++s) read_slot.template operator()<0>(0, s, x);
@@ -544,12 +668,28 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     // row stores ----
     // Lane holds, for result rows d = 8q + 4*(lane/32) + r (r = 0..3), the
     // column 16*(j%4) + 64*(q/2) + 8*(q%2) + 4*(lane/32) + r of unit j/4.
+    // C rows per block of the staging area: a ring slot's worth, or with
+    // paired A 32 rows (16 KiB): blocks 0-1 in the first pair array, 2-3 in
+    // the second, 4-7 in the B arrays
+    constexpr int CRS = AP ? 32 : T::C_ROWS_PER_STAGE;
     auto c_stage = [&](int s) -> char* {
-        char* r = reinterpret_cast<char*>(st0);
-        [&]<int... I>(std::integer_sequence<int, I...>) {
-            ((s == I ? (void)(r = reinterpret_cast<char*>(stage_a.template operator()<I>())) : (void)0), ...);
-        }(std::make_integer_sequence<int, T::STAGES>{});
-        return r;
+        if constexpr (AP) {
+            char* r = reinterpret_cast<char*>(sb3);
+            r = s == 6 ? reinterpret_cast<char*>(sb2) : r;
+            r = s == 5 ? reinterpret_cast<char*>(sb1) : r;
+            r = s == 4 ? reinterpret_cast<char*>(sb0) : r;
+            r = s == 3 ? reinterpret_cast<char*>(pa1) + CRS * T::BN * 2 : r;
+            r = s == 2 ? reinterpret_cast<char*>(pa1) : r;
+            r = s == 1 ? reinterpret_cast<char*>(pa0) + CRS * T::BN * 2 : r;
+            r = s == 0 ? reinterpret_cast<char*>(pa0) : r;
+            return r;
+        } else {
+            char* r = reinterpret_cast<char*>(st0);
+            [&]<int... I>(std::integer_sequence<int, I...>) {
+                ((s == I ? (void)(r = reinterpret_cast<char*>(stage_a.template operator()<I>())) : (void)0), ...);
+            }(std::make_integer_sequence<int, T::STAGES>{});
+            return r;
+        }
     };
     // Stores of C: 16 bytes per lane, kLanesPerRow lanes per row of the tile.
     constexpr int kRowsPerPass = T::C_ROWS_PER_PASS;  // BN / 8 lanes x 16 B per row
@@ -560,8 +700,8 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     auto pass_row = [&](int it) -> int { return it * kRowsPerPass + (int)threadIdx.x / kLanesPerRow; };
     auto pass_read = [&](int it) -> u32x4 {
         const int rl = pass_row(it);
-        const char* cs = c_stage((it * kRowsPerPass) / T::C_ROWS_PER_STAGE);
-        return *reinterpret_cast<const u32x4*>(cs + (rl % T::C_ROWS_PER_STAGE) * (T::BN * 2) + ((c ^ c_swz(rl)) * 16));
+        const char* cs = c_stage((it * kRowsPerPass) / CRS);
+        return *reinterpret_cast<const u32x4*>(cs + (rl % CRS) * (T::BN * 2) + ((c ^ c_swz(rl)) * 16));
     };
     with_epilogue(p, [&]<int ACT>() {
         // the bias of this lane's columns, loaded once for all its rows
@@ -578,8 +718,8 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
         for (int i = 0; i < T::FM; ++i) {
             const int rl = wm * T::TM + 32 * i + lane % 32;  // row in the tile
             // the 32 rows of block i lie in one stage array
-            char* cs = c_stage(__builtin_amdgcn_readfirstlane((wm * T::TM + 32 * i) / T::C_ROWS_PER_STAGE));
-            char* crow = cs + (rl % T::C_ROWS_PER_STAGE) * (T::BN * 2);
+            char* cs = c_stage(__builtin_amdgcn_readfirstlane((wm * T::TM + 32 * i) / CRS));
+            char* crow = cs + (rl % CRS) * (T::BN * 2);
 #pragma unroll
             for (int j = 0; j < T::FN; ++j) {
 #pragma unroll
