@@ -51,6 +51,8 @@ using P64S5 = gemm_relu::pipelined::Cfg<64, 256, 1, 2, 5>;
 // 256 x 256 with A (stored M x K) loaded two steps at a time: whole 128-byte
 // lines per row, 256 L2 requests per step and CU instead of 384
 using P256AP = gemm_relu::pipelined::Cfg<256, 256, 2, 2, 4, true>;
+using P128AP = gemm_relu::pipelined::Cfg<128, 256, 2, 2, 4, true>;  // the same for 128 x 256
+using P64AP = gemm_relu::pipelined::Cfg<64, 256, 1, 2, 4, true>;    // and 64 x 256
 using Q64 = gemm_relu::small::Cfg<64, 64, 2, 2, 2, 4>;     // 4 waves x 32x32, 64-deep steps, 4 slots
 using Q32 = gemm_relu::small::Cfg<32, 64, 1, 2, 2, 4>;     // 2 waves x 32x32, 64-deep steps, 4 slots
 using S256 = gemm_relu::staged::Tile<256, 256, 64, 2, 2>;  // generic instance of the same tile
@@ -213,10 +215,17 @@ const TileEntry kTiles[] = {
      launch_staged<S64, false>},
     {"256x256x32s4_w2x2_mfma32x32x16_lds-dma-a2", pipelined_desc<P256AP>(4), launch_pipelined<P256AP>,
      launch_staged<S256, false>},
+    {"128x256x32s4_w2x2_mfma32x32x16_lds-dma-a2", pipelined_desc<P128AP>(4), launch_pipelined<P128AP>,
+     launch_staged<S128, false>},
+    {"64x256x32s4_w1x2_mfma32x32x16_lds-dma-a2", pipelined_desc<P64AP>(4), launch_pipelined<P64AP>,
+     launch_staged<S64, false>},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kP64Tile = 10, kP64S5Tile = 13;  // 64 x 256 with four and with five slots
-constexpr int kP256Tile = 0, kP256PairTile = 14;  // 256 x 256, and with A loaded two steps at a time
+// the same tiles with A (stored M x K) loaded two steps at a time
+constexpr int kP256Tile = 0, kP256PairTile = 14;
+constexpr int kP128Tile = 9, kP128PairTile = 15;
+constexpr int kP64PairTile = 16;
 
 // The group a launch without opts uses: the tile's default, cut to a power of
 // two that leaves at least two groups when the grid has four tile-rows or
@@ -453,10 +462,18 @@ int choose_tile(int64_t M, int64_t N, int64_t K, bool ta, bool tb)
             }
         }
     }
-    // 64 x 256 on a grid of one round: the five-slot ring
-    if (best == kP64Tile && ((M + 63) / 64) * ((N + 255) / 256) <= (int64_t)kComputeUnits) best = kP64S5Tile;
-    // 256 x 256 with A stored M x K: A loaded two steps at a time
-    if (best == kP256Tile && !ta) best = kP256PairTile;
+    // The pipelined tiles with A stored M x K load it two steps at a time
+    // (whole cache lines: 3-14 % faster at 256 x 256, 7-8 % at 128 x 256;
+    // at 64 x 256, 9-13 % in NT and on a par with the five-slot ring in NN).
+    // With A stored K x M, 64 x 256 on a grid of one round takes the
+    // five-slot ring.
+    if (!ta) {
+        if (best == kP256Tile) best = kP256PairTile;
+        else if (best == kP128Tile) best = kP128PairTile;
+        else if (best == kP64Tile) best = kP64PairTile;
+    } else if (best == kP64Tile && ((M + 63) / 64) * ((N + 255) / 256) <= (int64_t)kComputeUnits) {
+        best = kP64S5Tile;
+    }
     return best;
 }
 

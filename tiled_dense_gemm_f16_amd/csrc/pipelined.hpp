@@ -70,8 +70,8 @@ template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_ = 4, bool AP
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = STAGES_;
     // A stored M x K is loaded two steps at a time (128 bytes of each row:
-    // whole cache lines) into the A parts of two ring slots, rows 0-127 in
-    // the even slot and 128-255 in the odd one; steps 2p and 2p+1 share them.
+    // whole cache lines) into one of two pair arrays; steps 2p and 2p+1
+    // share it.
     static constexpr bool APAIR = APAIR_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int NW = WAVES_M * WAVES_N, NT = kWave * NW;
@@ -103,8 +103,8 @@ struct Cfg {
     static_assert(C_ROWS_PER_STAGE % C_ROWS_PER_PASS == 0, "a store pass stays in one slot");
     static_assert(BN == 256, "the epilogue maps 32 lanes x 16 B onto one row of C");
     static constexpr int AP_LOADS_W = APAIR ? BM * 64 * 2 / 1024 / NW : 0;  // 1 KiB loads per wave per pair
-    static_assert(!APAIR || (BM == 256 && WAVES_M == 2 && NW == 4 && STAGES == 4),
-                  "paired A steps: 256 rows, two waves along M (128 rows each), a four-slot ring");
+    static_assert(!APAIR || (STAGES == 4 && (BM / NW) % 16 == 0 && BM <= 256),
+                  "paired A steps: a four-slot ring, 16 rows or a multiple per wave");
 };
 
 // A: row r of a stage holds 32 halves = four 16-byte chunks; logical chunk c
@@ -669,19 +669,21 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     // Lane holds, for result rows d = 8q + 4*(lane/32) + r (r = 0..3), the
     // column 16*(j%4) + 64*(q/2) + 8*(q%2) + 4*(lane/32) + r of unit j/4.
     // C rows per block of the staging area: a ring slot's worth, or with
-    // paired A 32 rows (16 KiB): blocks 0-1 in the first pair array, 2-3 in
-    // the second, 4-7 in the B arrays
+    // paired A 32 rows (16 KiB): blocks 0-3 in the B arrays, 4-5 in the
+    // first pair array and 6-7 in the second (those two only for 256 rows)
     constexpr int CRS = AP ? 32 : T::C_ROWS_PER_STAGE;
+    static_assert(!AP || T::B_HALVES * 2 == CRS * T::BN * 2, "a B array holds 32 rows of C");
+    static_assert(!AP || T::BM <= 128 || T::BM * 64 * 2 == 2 * CRS * T::BN * 2, "a pair array holds 64 rows of C");
     auto c_stage = [&](int s) -> char* {
         if constexpr (AP) {
-            char* r = reinterpret_cast<char*>(sb3);
-            r = s == 6 ? reinterpret_cast<char*>(sb2) : r;
-            r = s == 5 ? reinterpret_cast<char*>(sb1) : r;
-            r = s == 4 ? reinterpret_cast<char*>(sb0) : r;
-            r = s == 3 ? reinterpret_cast<char*>(pa1) + CRS * T::BN * 2 : r;
-            r = s == 2 ? reinterpret_cast<char*>(pa1) : r;
-            r = s == 1 ? reinterpret_cast<char*>(pa0) + CRS * T::BN * 2 : r;
-            r = s == 0 ? reinterpret_cast<char*>(pa0) : r;
+            char* r = reinterpret_cast<char*>(pa1) + CRS * T::BN * 2;
+            r = s == 6 ? reinterpret_cast<char*>(pa1) : r;
+            r = s == 5 ? reinterpret_cast<char*>(pa0) + CRS * T::BN * 2 : r;
+            r = s == 4 ? reinterpret_cast<char*>(pa0) : r;
+            r = s == 3 ? reinterpret_cast<char*>(sb3) : r;
+            r = s == 2 ? reinterpret_cast<char*>(sb2) : r;
+            r = s == 1 ? reinterpret_cast<char*>(sb1) : r;
+            r = s == 0 ? reinterpret_cast<char*>(sb0) : r;
             return r;
         } else {
             char* r = reinterpret_cast<char*>(st0);
