@@ -697,7 +697,12 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     constexpr int kRowsPerPass = T::C_ROWS_PER_PASS;  // BN / 8 lanes x 16 B per row
     constexpr int kLanesPerRow = T::BN / 8;
     constexpr int kPasses = T::BM / kRowsPerPass;
-    const int c = threadIdx.x % kLanesPerRow;
+    // recomputed here from an opaque copy of the lane index: a value shared
+    // with the prologue would stay live through the loop (a spilled VGPR in
+    // the 256-row tiles)
+    int tid_c = threadIdx.x;
+    asm volatile("" : "+v"(tid_c));
+    const int c = tid_c % kLanesPerRow;
     // pass `it`: this lane's row of the tile and its 16 bytes from the LDS copy
     auto pass_row = [&](int it) -> int { return it * kRowsPerPass + (int)threadIdx.x / kLanesPerRow; };
     auto pass_read = [&](int it) -> u32x4 {
