@@ -96,6 +96,9 @@ def test_tile_selection_is_host_only():
     tname = lambda *s, **kw: gr.tile_name(gr.select_tile(*s, **kw))  # noqa: E731
     assert tname(1024, 1024, 1024, trans_a=True).startswith("64x256")
     assert tname(512, 4096, 8192, trans_a=True).startswith("64x256")
+    # B stored N x K: the 64 x 256 tile that loads A two steps at a time
+    # beats the 128 x 128 staged one (no transpose of B) at 2048^3
+    assert tname(2048, 2048, 2048, trans_b=True) == "64x256x32s4_w1x2_mfma32x32x16_lds-dma-a2"
     for ta in (False, True):
         for tb in (False, True):
             assert tname(16, 8192, 8192, trans_a=ta, trans_b=tb).startswith("splitk_16x")  # few rows

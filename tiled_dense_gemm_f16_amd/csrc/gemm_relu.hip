@@ -314,10 +314,11 @@ bool splitk_ok(int64_t M, int64_t K) { return M * K * 2 < ((int64_t)1 << 31); }
 // (M <= 32 with operands as stored, M <= 64 otherwise) always take a split-K
 // tile, and the 16x64 tile is only for latency-bound outputs of at most 64 K
 // elements. Over the offline sweeps the default launch (this model, the
-// small-tile model below, the group and block-order rules) is 1.5 % slower
-// than the measured fastest on average in NN (10 % at worst; 46 shapes) and
-// 2.2-3.4 % in the transposed layouts (12 shapes each; 19 % at worst, TT
-// 4096 x 64 x 4096, where the split-K tile is chosen over the 64 x 256 one).
+// small-tile model below, the group and block-order rules) is 2.3 % slower
+// than the measured fastest on average in NN (12 % at worst, a group size;
+// 46 shapes) and 1.4-2.9 % in the transposed layouts (12 shapes each; 18 %
+// at worst, TT 4096 x 64 x 4096, where the split-K tile is chosen over the
+// 64 x 256 one).
 // The rules it
 // replaced, which looked at M and the 256x256 tile count alone, were up to
 // 6x slower on shapes they were not written for.
@@ -328,15 +329,19 @@ struct AutoTile {
 constexpr AutoTile kAutoTiles[] = {
     {0, {6.96, 5.78, 6.63, 6.10}},   // 256x256 pipelined
     {9, {5.24, 3.90, 4.96, 4.04}},   // 128x256 pipelined
-    {10, {3.21, 2.21, 3.49, 2.25}},  // 64x256 pipelined (TN: refit after the step-descriptor change)
+    // 64x256 pipelined (TN: refit after the step-descriptor change; NT: refit
+    // when it came to load A two steps at a time)
+    {10, {3.21, 2.43, 3.49, 2.25}},
     {6, {2.13, 1.15, 0.570, 0.517}}, // split-K 64x128
     {5, {1.48, 0.772, 0.390, 0.344}},// split-K 32x128
     {4, {1.12, 0.472, 0.408, 0.324}},// split-K 16x128
     {2, {0.895, 1.24, 0.429, 0.756}},// 64x64 staged
     // 128x128 staged: with B stored N x K (NT) it needs no transpose and beat
     // the pipelined tiles at 2048^3 and 4096 x 1024 x 4096 (39.1 against
-    // 40.7 us, 71.1 against 76.8); its other rates keep it out of the NN, TN
-    // and TT choices, where it was 1.15-3x off the best.
+    // 40.7 us, 71.1 against 76.8) until the 64 x 256 tile came to load A two
+    // steps at a time (34.4-37.9 against 39.7 us, 66.3 against 72.2); its
+    // other rates keep it out of the NN, TN and TT choices, where it was
+    // 1.15-3x off the best.
     {1, {1.0, 2.35, 0.9, 1.4}},
     {3, {0.273, 0.706, 0.118, 0.262}},// 16x64 staged
 };
