@@ -107,11 +107,17 @@ def test_integer_inputs_bit_exact(M, N, K):
 # inputs keep every fp32 sum exact, so any walk order must give the oracle's
 # bits: the 256 x 256 tile past one round (where it skews), the 64 x 256
 # tiles with four and five slots and the 64 x 64 tile, operands as stored and
-# transposed.
+# transposed; and the tiles that load A two steps at a time, whose walk starts
+# on an even step (the K tail inside the last pair) and does not skew when the
+# step count is odd (K = 984: 31 steps).
 SKEW_CASES = [(0, 4160, 4160, 1000, False, False), (0, 4160, 4160, 1000, True, True), (0, 4160, 4160, 1000, False, True),
               (10, 1088, 1024, 1000, False, False), (10, 1088, 1024, 1000, True, False),
               (13, 1088, 1024, 1000, False, False), (13, 1088, 1024, 1000, False, True),
-              (11, 1088, 1088, 1000, False, False), (9, 2112, 2048, 1000, False, False)]
+              (11, 1088, 1088, 1000, False, False), (9, 2112, 2048, 1000, False, False),
+              (14, 4160, 4160, 1000, False, False), (14, 4160, 4160, 1000, False, True),
+              (14, 4160, 4160, 984, False, False), (15, 2112, 2048, 1000, False, False),
+              (15, 2112, 2048, 984, False, True), (16, 1088, 1024, 1000, False, False),
+              (16, 1088, 1024, 1000, False, True)]
 
 
 @pytest.mark.parametrize("tile,M,N,K,ta,tb", SKEW_CASES)
@@ -137,6 +143,26 @@ def test_skewed_k_walk_with_k_tail_bit_exact(tile, M, N, K, ta, tb):
         ii, jj = rng.integers(0, M, 4096), rng.integers(0, N, 4096)
         want = oracle.gemm_relu_f16_points(A, B, ii, jj)
         assert np.array_equal(got[ii, jj], want), f"{np.sum(got[ii, jj] != want)} point mismatches"
+
+
+def _tile_named(name):
+    return next(t for t in range(gr.tile_count()) if gr.tile_name(t) == name)
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 2048, 1024), (1280, 2304, 1000), (4096, 4096, 4096)])
+def test_paired_a_tile_same_bits_as_plain_on_one_round(M, N, K):
+    # Loading A two steps at a time changes where the operands wait in LDS,
+    # not the order of the sums: on a grid of one round (where the 256 x 256
+    # K walk does not skew) both tiles give the same bits on N(0,1) inputs
+    plain = _tile_named("256x256x32s4_w2x2_mfma32x32x16_lds-dma")
+    paired = _tile_named("256x256x32s4_w2x2_mfma32x32x16_lds-dma-a2")
+    say(f"[paired] M={M} N={N} K={K} tiles {plain} {paired}")
+    a, b = workloads.make_inputs(M, N, K, dist="normal", seed=M + N + K)
+    a, b = a.cuda(), b.cuda()
+    c0 = gr.gemm_relu(a, b, tile=plain)
+    c1 = gr.gemm_relu(a, b, tile=paired)
+    torch.cuda.synchronize()
+    assert torch.equal(c0.view(torch.int16), c1.view(torch.int16))
 
 
 EDGE = [1, 7, 8, 9, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 257]
