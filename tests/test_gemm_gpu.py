@@ -392,13 +392,17 @@ def test_guard_bands(M, N, K, off):
 # invariance and hygiene
 # ---------------------------------------------------------------------------
 
-def test_block_order_does_not_change_results():
-    w = workloads.RAGGED
+@pytest.mark.parametrize("w", [workloads.RAGGED, workloads.SKINNY,
+                               workloads.Workload("gemm_relu_f16_32x8192x2048_normal0.02", 32, 8192, 2048, "normal", 0.02)],
+                         ids=lambda w: w.name)
+def test_block_order_does_not_change_results(w):
+    # (the split-K tiles accept either order and keep one mapping of
+    # workgroups to tiles and splits)
     a, b = workloads.workload_inputs(w)
     ref = run(a, b)
     for order, gm in ((gr.ORDER_ROW_MAJOR, 0), (gr.ORDER_DEFAULT, 1), (gr.ORDER_DEFAULT, 2),
                       (gr.ORDER_DEFAULT, 8), (gr.ORDER_DEFAULT, 64)):
-        say(f"[order] order={order} group_m={gm}")
+        say(f"[order] {w.name} order={order} group_m={gm}")
         assert np.array_equal(run(a, b, block_order=order, group_m=gm), ref)
 
 
