@@ -259,8 +259,9 @@ constexpr double kSplitCuBytesPerUs = 58.07e3;   // one CU streaming B
 constexpr double kSplitHbmBytesPerUs = 6.18e6;   // all CUs streaming B
 constexpr double kSplitDepthUsPer1024 = 1.89;    // per 1024 rows of a workgroup's K range
 constexpr int64_t kSplitMaxWorkgroups = 256;     // one per CU
+constexpr int64_t kMaxSplitPartialBytes = (int64_t)1 << 31;  // one split's M x N fp32 partials
 
-void choose_splits(int64_t K, int64_t tiles, int& splits, int& kc)
+void choose_splits(int64_t M, int64_t N, int64_t K, int64_t tiles, int& splits, int& kc)
 {
     const int64_t max_s = (K + kSplitKStep - 1) / kSplitKStep;  // at least one step per workgroup
     const double bytes = (double)tiles * kSplitKTN * (double)K * 2.0;  // B, once per row tile
@@ -268,6 +269,9 @@ void choose_splits(int64_t K, int64_t tiles, int& splits, int& kc)
     splits = 1;
     kc = (int)((K + kSplitKStep - 1) / kSplitKStep * kSplitKStep);
     if (kc < kSplitKStep) kc = kSplitKStep;
+    // the combine reads one split's M x N fp32 partials through a buffer
+    // descriptor, whose range ends below 2^31 bytes
+    if (M * N * 4 >= kMaxSplitPartialBytes) return;
     for (int64_t s = 1; s <= max_s; s *= 2) {
         int64_t c = (K + s - 1) / s;
         c = (c + kSplitKStep - 1) / kSplitKStep * kSplitKStep;
@@ -394,7 +398,7 @@ Prediction predict(const AutoTile& at, int layout, int64_t M, int64_t N, int64_t
     const gemm_relu_tile_desc& d = kTiles[at.id].desc;
     const int64_t tiles = ((M + d.bm - 1) / d.bm) * ((N + d.bn - 1) / d.bn);
     int splits = 1, kc = (int)K;
-    if (d.split_k) choose_splits(K, tiles, splits, kc);
+    if (d.split_k) choose_splits(M, N, K, tiles, splits, kc);
     const double rounds = (double)((tiles * splits + (int64_t)kComputeUnits - 1) / (int64_t)kComputeUnits);
     const double compute = rounds * 2.0 * d.bm * d.bn * (double)kc / (at.tflops_per_cu[layout] * 1e6);
     const double bw = kHbmBytesPerUs * (d.family == GEMM_RELU_FAMILY_STAGED ? kStagedHbmShare : 1.0);
@@ -722,7 +726,7 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int op_a, const void* B,
     const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
     if (tiles > INT32_MAX) return GEMM_RELU_EUNSUPPORTED;
     if (splitk) {
-        choose_splits(K, tiles, a.splits, a.kc);
+        choose_splits(M, N, K, tiles, a.splits, a.kc);
         if (tiles * a.splits > INT32_MAX) return GEMM_RELU_EUNSUPPORTED;
     }
     const size_t partial_bytes = (size_t)a.splits * (size_t)M * (size_t)N * 4;

@@ -52,6 +52,10 @@
 namespace gemm_relu {
 namespace splitk {
 
+// cache-policy operand of the buffer load builtin: the sc1 scope bit (device
+// scope), as in the compiler's relaxed device-scope atomic accesses
+constexpr int kCachePolicySc1 = 16;
+
 template <int MB_, int NW_ = 4, int D_ = 2>
 struct Cfg {
     static constexpr int MB = MB_;          // 16-row blocks
@@ -301,19 +305,23 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
     //    workgroup-scope fences keep the count after the wait, and the
     //    last workgroup's loads after the barrier that publishes the count
     //    (and they depend on it through the branch on last_flag).
-    // partials travel as 8-byte device-scope atomics (pairs of fp32)
-    auto pack = [](float lo, float hi) -> uint64_t {
-        return (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
-    };
+    // Partials are stored 16 bytes at a time with the device-scope cache
+    // policy (sc1): the instruction the compiler emits for a relaxed
+    // device-scope atomic store, which it does not offer wider than 8 bytes.
+    // Each dword is stored with device scope; nothing reads a partial before
+    // the count below, so the 16 bytes need not land as one. A store of more
+    // than 8 bytes reads its data registers after issue: an instruction that
+    // writes them must wait one cycle, which the compiler ensures for its own
+    // stores but not around inline asm, hence the s_nop in each.
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int rl = cm + j * RP, m = m0 + rl;
         if (rl < T::BM && m < M && n < N) {
-            uint64_t* dst = reinterpret_cast<uint64_t*>(p.partial + ((int64_t)ks * M + m) * N + n);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                __hip_atomic_store(dst + e, pack(v[j][2 * e], v[j][2 * e + 1]), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+            float* dst = p.partial + ((int64_t)ks * M + m) * N + n;
+            const u32x4 lo = __builtin_bit_cast(u32x4, f32x4{v[j][0], v[j][1], v[j][2], v[j][3]});
+            const u32x4 hi = __builtin_bit_cast(u32x4, f32x4{v[j][4], v[j][5], v[j][6], v[j][7]});
+            asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(dst), "v"(lo) : "memory");
+            asm volatile("global_store_dwordx4 %0, %1, off offset:16 sc1\n\ts_nop 1" ::"v"(dst), "v"(hi) : "memory");
         }
     }
     asm volatile("" ::: "memory");  // the stores above stay above the wait
@@ -330,38 +338,46 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
         GR_STAMP_FLUSH(p);
         return;
     }
-    // Up to kBatch splits' partials are loaded before any is added, so their
-    // latencies overlap; the additions keep split order.
     constexpr int kBatch = 8;
     float sum[NJ][8];
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int e = 0; e < 8; ++e) sum[j][e] = 0.f;
+    // The partials are read 16 bytes at a time with the device-scope cache
+    // policy (sc1, what a relaxed device-scope atomic load compiles to),
+    // through one buffer descriptor per split: the host splits K only when
+    // one split's M x N fp32 partials stay below 2^31 bytes. Up to kBatch
+    // splits are loaded before any is added (their latencies overlap); the
+    // additions keep split order.
     for (int q0 = 0; q0 < p.splits; q0 += kBatch) {
-        uint64_t buf[kBatch][NJ][4];
+        u32x4 buf[kBatch][NJ][2];
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
+            const int q = q0 + b;
+            const __amdgpu_buffer_rsrc_t rq =
+                make_rsrc(p.partial + (int64_t)(q < p.splits ? q : 0) * M * N, (uint64_t)M * N * 4);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int rl = cm + j * RP, m = m0 + rl;
-                const bool ok = q0 + b < p.splits && rl < T::BM && m < M && n < N;
-                uint64_t* src = reinterpret_cast<uint64_t*>(p.partial + ((int64_t)(q0 + b) * M + m) * N + n);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    buf[b][j][e] = ok ? __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+                const bool ok = q < p.splits && rl < T::BM && m < M && n < N;
+                const uint32_t off = ok ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 4u : kOOB;
+                buf[b][j][0] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)off, 0, kCachePolicySc1);
+                buf[b][j][1] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(off + 16u), 0, kCachePolicySc1);
             }
         }
+        // (each element is copied out before the cast: this compiler's
+        // __builtin_bit_cast of a vector element reads element 0 whatever
+        // the index)
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
+        for (int b = 0; b < kBatch; ++b)
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sum[j][2 * e] += __builtin_bit_cast(float, (uint32_t)buf[b][j][e]);
-                    sum[j][2 * e + 1] += __builtin_bit_cast(float, (uint32_t)(buf[b][j][e] >> 32));
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t w = buf[b][j][e / 4][e % 4];
+                    sum[j][e] += __builtin_bit_cast(float, w);
                 }
-        }
     }
     store_c(sum);
     if (t == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
