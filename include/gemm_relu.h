@@ -30,7 +30,8 @@
  *
  * Workspace: for few rows (M <= 64) the K dimension is split across
  * workgroups, whose fp32 partial sums meet in a library-owned workspace
- * (partials plus one counter per output tile). The library allocates it with
+ * (partials plus one counter per output tile; K is not split when one
+ * split's M x N fp32 partials would reach 2 GiB). The library allocates it with
  * hipMalloc on the first such call for a (device, stream) pair, clears its
  * counters with an asynchronous memset on that stream, keeps it until the
  * process ends, and grows it (to at least twice its size) when a later call
