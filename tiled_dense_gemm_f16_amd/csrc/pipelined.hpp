@@ -178,6 +178,25 @@ struct RegionPlan {
     static constexpr bool fits() { return PRE + 1 + NSLOT <= NMMA && NSLOT <= NMMA && LPT <= kPositions - PRE - 1; }
 };
 
+// COUNT loads spread evenly over the positions [FIRST, END) of a region of
+// 2 NMMA matrix ops: count[q] of them at position q, numbered from first[q]
+// (several to a position when there are more loads than positions).
+template <int NMMA, int FIRST, int END, int COUNT>
+struct LoadSpread {
+    static_assert(0 <= FIRST && FIRST < END && END <= 2 * NMMA, "positions inside the region");
+    int first[2 * NMMA];
+    int count[2 * NMMA];
+    constexpr LoadSpread() : first{}, count{}
+    {
+        for (int q = 0; q < 2 * NMMA; ++q) first[q] = count[q] = 0;
+        for (int v = 0; v < COUNT; ++v) {
+            const int q = FIRST + (v * (END - FIRST)) / COUNT;
+            if (count[q] == 0) first[q] = v;
+            ++count[q];
+        }
+    }
+};
+
 template <class T, bool KALIGNED, bool TA = false, bool TB = false>
 __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
 {
@@ -564,26 +583,34 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     using Plan = RegionPlan<T::NMMA, T::NSLOT, T::LPT, kPre>;
     static_assert(kPre >= 0 && Plan::fits(), "the region has too few matrix ops for its reads and loads");
     constexpr Plan plan;
-    // Paired A: even regions load B only; odd regions also load the A pair
-    // of steps kt+3 and kt+4 (loads 0 .. AP_LOADS_W-1 of the region)
-    using PlanE = RegionPlan<T::NMMA, T::NSLOT, T::B_LOADS_W, kPre>;
-    using PlanO = RegionPlan<T::NMMA, T::NSLOT, T::B_LOADS_W + T::AP_LOADS_W, kPre>;
-    static_assert(!AP || PlanO::fits(), "the region has too few matrix ops for its reads and loads");
-    constexpr PlanE plan_e;
-    constexpr PlanO plan_o;
-    // Loads allowed in flight at the barrier of region kt (S = kt % R): those
-    // issued after the last one step kt+1 needs. Plain: the previous region's.
-    // Paired A: step kt+1's B was loaded in region kt-2, its A pair in region
-    // kt-2 (kt+1 even) or earlier, so again the previous region's loads,
-    // which number B_LOADS_W after an even region and B_LOADS_W + AP_LOADS_W
-    // after an odd one.
-    auto wait_count = [](int s) constexpr -> int {
-        if constexpr (AP) return s % 2 == 1 ? T::B_LOADS_W : T::B_LOADS_W + T::AP_LOADS_W;
-        else return (AHEAD - 2) * T::LPT;
-    };
     constexpr int kNext = 2 * T::NMMA - 1;
     constexpr int kAdv = kPre + 1 + T::NSLOT;
     static_assert(kAdv + 3 < kNext, "the region has room for the cursor");
+    // Paired A: even regions load B of steps kt+3 and kt+4, odd regions the
+    // A pair of steps kt+3 and kt+4, so that both carry about as many loads.
+    // Step kt+4's B uses the descriptors the cursor makes in this region:
+    // those loads come after them (positions kLate on, several to a
+    // position where the region is short), into the stage of step kt, which
+    // no wave reads in region kt.
+    constexpr int kLate = kAdv + 4;
+    using PlanE = LoadSpread<T::NMMA, kPre + 1, kLate, T::B_LOADS_W>;
+    using PlanL = LoadSpread<T::NMMA, kLate, 2 * T::NMMA, T::B_LOADS_W>;
+    using PlanO = RegionPlan<T::NMMA, T::NSLOT, T::AP_LOADS_W, kPre>;
+    static_assert(!AP || PlanO::fits(), "the region has too few matrix ops for its reads and loads");
+    constexpr PlanE plan_e;
+    constexpr PlanL plan_l;
+    constexpr PlanO plan_o;
+    // Loads allowed in flight at the barrier of region kt (S = kt % R): those
+    // issued after the last one step kt+1 needs. Plain: the previous region's.
+    // Paired A, kt even: step kt+1's B came from region kt-3 (the second B
+    // of an even region) and its A pair is in; in flight may stay region
+    // kt-2's second B (step kt+2) and region kt-1's pair: B_LOADS_W +
+    // AP_LOADS_W. kt odd: step kt+1's pair came from region kt-2 and its B
+    // from region kt-3; in flight may stay region kt-1's two B steps.
+    auto wait_count = [](int s) constexpr -> int {
+        if constexpr (AP) return s % 2 == 1 ? 2 * T::B_LOADS_W : T::B_LOADS_W + T::AP_LOADS_W;
+        else return (AHEAD - 2) * T::LPT;
+    };
     auto region = [&]<int S>() {
         constexpr int S1 = (S + 1) % R, SL = (S + AHEAD) % R;
 #pragma unroll
@@ -595,11 +622,12 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
             if constexpr (!AP) {
                 if (plan.load[q] >= 0) load_one.template operator()<SL>(plan.load[q], r);
             } else if constexpr (S % 2 == 0) {
-                if (plan_e.load[q] >= 0) load_b.template operator()<SL>(plan_e.load[q], r);
+                for (int j = plan_e.first[q]; j < plan_e.first[q] + plan_e.count[q]; ++j)
+                    load_b.template operator()<SL>(j, r);
+                for (int j = plan_l.first[q]; j < plan_l.first[q] + plan_l.count[q]; ++j)
+                    load_b.template operator()<S>(j, rn);
             } else {
-                const int v = plan_o.load[q];
-                if (v >= 0 && v < T::AP_LOADS_W) load_pair.template operator()<SL / 2>(v, r);
-                else if (v >= 0) load_b.template operator()<SL>(v - T::AP_LOADS_W, r);
+                if (plan_o.load[q] >= 0) load_pair.template operator()<SL / 2>(plan_o.load[q], r);
             }
             if (plan.readx[q] >= 0) read_slot.template operator()<S1>(0, plan.readx[q], x);
             if (plan.ready[q] >= 0) read_slot.template operator()<S1>(1, plan.ready[q], y);
