@@ -318,11 +318,11 @@ bool splitk_ok(int64_t M, int64_t K) { return M * K * 2 < ((int64_t)1 << 31); }
 // (M <= 32 with operands as stored, M <= 64 otherwise) always take a split-K
 // tile, and the 16x64 tile is only for latency-bound outputs of at most 64 K
 // elements. Over the offline sweeps the default launch (this model, the
-// small-tile model below, the group and block-order rules) is 2.3 % slower
-// than the measured fastest on average in NN (12 % at worst, a group size;
-// 46 shapes) and 1.4-2.9 % in the transposed layouts (12 shapes each; 18 %
-// at worst, TT 4096 x 64 x 4096, where the split-K tile is chosen over the
-// 64 x 256 one).
+// small-tile model below, the group and block-order rules) is 2.3-2.7 %
+// slower than the measured fastest on average in NN over two sweeps (12-17 %
+// at worst; 46 shapes) and 1.2-3.0 % in the transposed layouts (12 shapes
+// each; 11-18 % at worst, TT 4096 x 64 x 4096, where the split-K tile is
+// chosen over the 64 x 256 one).
 // The rules it
 // replaced, which looked at M and the 256x256 tile count alone, were up to
 // 6x slower on shapes they were not written for.
