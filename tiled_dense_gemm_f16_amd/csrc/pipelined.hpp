@@ -602,11 +602,11 @@ __global__ void __launch_bounds__(T::NT, 1) pipelined_kernel(Args p)
     constexpr PlanO plan_o;
     // Loads allowed in flight at the barrier of region kt (S = kt % R): those
     // issued after the last one step kt+1 needs. Plain: the previous region's.
-    // Paired A, kt even: step kt+1's B came from region kt-3 (the second B
-    // of an even region) and its A pair is in; in flight may stay region
-    // kt-2's second B (step kt+2) and region kt-1's pair: B_LOADS_W +
-    // AP_LOADS_W. kt odd: step kt+1's pair came from region kt-2 and its B
-    // from region kt-3; in flight may stay region kt-1's two B steps.
+    // Paired A, kt even: step kt+1's B came first in region kt-2 and its A
+    // pair from region kt-3; in flight may stay region kt-2's second B (step
+    // kt+2) and region kt-1's pair: B_LOADS_W + AP_LOADS_W. kt odd: step
+    // kt+1's B came second in region kt-3 and its pair from region kt-2; in
+    // flight may stay region kt-1's two B steps: 2 B_LOADS_W.
     auto wait_count = [](int s) constexpr -> int {
         if constexpr (AP) return s % 2 == 1 ? 2 * T::B_LOADS_W : T::B_LOADS_W + T::AP_LOADS_W;
         else return (AHEAD - 2) * T::LPT;
