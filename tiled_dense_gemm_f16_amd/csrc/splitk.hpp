@@ -286,12 +286,14 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
     // ---- split across workgroups: partials, then the last workgroup combines ----
     // The eight XCDs each have their own L2, and a device-wide fence would
     // write back or invalidate a whole L2 per workgroup. Instead every access
-    // to the shared data (partials, counter) is a device-scope atomic, which
-    // the hardware performs at the level the XCDs share: the partials are
-    // stored that way, this wave waits until its stores are acknowledged
+    // to the shared data (partials, counter) carries the device-scope cache
+    // policy (sc1, as the compiler's device-scope atomics do), which the
+    // hardware performs at the level the XCDs share: the partials are stored
+    // that way, this wave waits until its stores are acknowledged
     // (vmcnt(0)), the workgroup meets, and only then one lane counts the
-    // workgroup in. The last workgroup reads the partials with device-scope
-    // atomic loads, all issued after it saw the final count.
+    // workgroup in (a device-scope atomic). The last workgroup reads the
+    // partials with device-scope loads, all issued after it saw the final
+    // count.
     // Why this order holds without release/acquire at device scope:
     //  * hardware: a device-scope store is acknowledged (and vmcnt drops) only
     //    once it is visible at the level the XCDs share, and device-scope
@@ -299,7 +301,7 @@ __global__ void __launch_bounds__(T::NT, 1) splitk_kernel(Args p)
     //    workgroup's count lands, all of its partials are already visible
     //    there, and the last workgroup's loads, issued after its count
     //    returned, read them from there;
-    //  * compiler: the relaxed stores may not sink below the empty asm with
+    //  * compiler: the asm stores may not sink below the empty asm with
     //    a memory clobber that sits before the vmcnt(0) wait, and the wait
     //    and the volatile asm keep their order; the barrier's
     //    workgroup-scope fences keep the count after the wait, and the
